@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the gated-attention decode / verify step.
+
+This module is shared by the tests, the benchmark and the smoke check; it holds
+none of the step's arithmetic.  Values are drawn with numpy's PCG64 and cast to
+bf16 / float8 e4m3 with torch's CPU casts (library routines), so the oracle and
+the HIP library receive identical bytes.
+
+The five named workloads are the decode and verify shapes of the page
+"012-attention-local-splits.py" (Config: Hq 16 and Hkv 2 per GPU under TP8,
+head_dim 64, page_size 1 as served or 64 in tests, window 2048 with RoPE theta
+500000 on sliding layers, sm_scale 1/8, cache scales 1 unless set), with the
+batch, context and distribution recipe of each case listed below.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    q_len: int
+    seq_lo: int            # cached tokens per request, drawn uniformly in [seq_lo, seq_hi]
+    seq_hi: int
+    window: int            # 0 = full causal attention
+    rope_theta: float      # 0 = no RoPE
+    page_size: int = 1
+    kv_scale: float = 1.0
+    qkv_std: float = 1.0
+    table: str = "perm"    # "identity": page j of request b is page b*max + j; "perm": shuffled
+    num_q_heads: int = 16
+    num_kv_heads: int = 2
+    head_dim: int = 64
+    sm_scale: float = 0.125
+    spare_pages: int = 0   # pool pages no request references
+    seed: int = 0
+
+    @property
+    def width(self) -> int:
+        return (2 * self.num_q_heads + 2 * self.num_kv_heads) * self.head_dim
+
+
+# The five workloads, each with its fixed seed (1000 + index).
+WORKLOADS = {
+    # batch 1, one token, 512 cached, full attention, identity page table
+    "tiny_decode": Workload("tiny_decode", 1, 1, 512, 512, 0, 0.0, table="identity", seed=1001),
+    # batch 32, one token, 4k-16k cached, window 2048, RoPE 5e5, shuffled rows
+    "swa_decode": Workload("swa_decode", 32, 1, 4096, 16384, 2048, 500000.0, seed=1002),
+    # batch 64, one token, 32768 cached, full attention
+    "full_decode_32k": Workload("full_decode_32k", 64, 1, 32768, 32768, 0, 0.0, seed=1003),
+    # batch 32, 8-token verify block, 8k-32k cached, window 2048, RoPE 5e5
+    "swa_verify": Workload("swa_verify", 32, 8, 8192, 32768, 2048, 500000.0, seed=1004),
+    # batch 8, 8-token block, 64k-128k cached, page 64, cache scales 0.5, qkv ~ N(0, 2)
+    "paged_scaled_long": Workload("paged_scaled_long", 8, 8, 65536, 131072, 0, 0.0,
+                                  page_size=64, kv_scale=0.5, qkv_std=math.sqrt(2.0),
+                                  seed=1005),
+}
+ORDER = ["tiny_decode", "swa_decode", "full_decode_32k", "swa_verify", "paged_scaled_long"]
+
+
+@dataclass
+class Inputs:
+    w: Workload
+    qkv: np.ndarray            # uint16 bf16 bits [B, L, width]
+    positions: np.ndarray      # int64 [B*L]
+    cache_loc: np.ndarray      # int64 [B*L]
+    cache_seqlens: np.ndarray  # int32 [B]  = seq_lens + L
+    cu_seqlens_q: np.ndarray   # int32 [B+1] = 0, L, 2L, ...
+    page_table: np.ndarray     # int32 [B, max_pages], -1 unused
+    seq_lens: np.ndarray       # int32 [B]
+    k_cache: np.ndarray        # uint8 e4m3 codes [num_pages*P, Hkv, D]
+    v_cache: np.ndarray
+    k_scale: float
+    v_scale: float
+    max_pages: int
+    num_pages: int
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def tokens(self) -> int:
+        return self.w.batch * self.w.q_len
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns via torch's cast (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """float32 -> float8_e4m3fn codes via torch's cast."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy()
+
+
+def _normal_e4m3(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint8)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        out[s:e] = to_e4m3_codes(rng.standard_normal(e - s, dtype=np.float32))
+    return out.reshape(shape)
+
+
+def make_inputs(w: Workload, seed: int | None = None, seq_lens: np.ndarray | None = None,
+                max_pages: int | None = None) -> Inputs:
+    """Build one step's inputs.
+
+    Recipe: seq_lens ~ U{seq_lo..seq_hi} (or given); cache_seqlens = seq_lens + L;
+    each request owns ceil(cache_seqlens/P) pages taken consecutively from the
+    identity or a random permutation of the pool; the page_table row tail is -1;
+    the new token i of request b sits at position p = seq_lens[b] + i and flat
+    cache row page_table[b, p // P] * P + p % P; the pool holds e4m3(N(0,1));
+    qkv = bf16(N(0, qkv_std^2)); the cache scales equal kv_scale.
+    """
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    B, L, P = w.batch, w.q_len, w.page_size
+    if seq_lens is None:
+        seq_lens = rng.integers(w.seq_lo, w.seq_hi, size=B, endpoint=True)
+    seq_lens = np.ascontiguousarray(seq_lens, np.int32)
+    assert seq_lens.shape == (B,)
+    cache_seqlens = (seq_lens + L).astype(np.int32)
+    n_pages = (cache_seqlens.astype(np.int64) + P - 1) // P
+    if max_pages is None:
+        max_pages = int(-(-(max(w.seq_hi, int(seq_lens.max(initial=0))) + L) // P)) + 1
+    assert n_pages.max(initial=0) <= max_pages
+    num_pages = int(n_pages.sum()) + w.spare_pages
+    if w.table == "identity":
+        order = np.arange(num_pages, dtype=np.int64)
+    else:
+        order = rng.permutation(num_pages).astype(np.int64)
+    page_table = np.full((B, max_pages), -1, np.int32)
+    off = 0
+    for b in range(B):
+        page_table[b, : n_pages[b]] = order[off: off + n_pages[b]]
+        off += int(n_pages[b])
+    positions = (seq_lens[:, None].astype(np.int64) + np.arange(L, dtype=np.int64)[None, :])
+    rows = page_table[np.arange(B)[:, None], positions // P].astype(np.int64) * P + positions % P
+    rows_total = num_pages * P
+    k_cache = _normal_e4m3(rng, (rows_total, w.num_kv_heads, w.head_dim))
+    v_cache = _normal_e4m3(rng, (rows_total, w.num_kv_heads, w.head_dim))
+    qkv = to_bf16_bits(rng.standard_normal((B, L, w.width), dtype=np.float32) * np.float32(w.qkv_std))
+    cu = (np.arange(B + 1, dtype=np.int32) * L).astype(np.int32)
+    return Inputs(w=w, qkv=qkv, positions=positions.reshape(-1).copy(),
+                  cache_loc=rows.reshape(-1).copy(), cache_seqlens=cache_seqlens,
+                  cu_seqlens_q=cu, page_table=page_table, seq_lens=seq_lens,
+                  k_cache=k_cache, v_cache=v_cache, k_scale=float(w.kv_scale),
+                  v_scale=float(w.kv_scale), max_pages=int(max_pages), num_pages=num_pages)
+
+
+def small(name: str = "small", batch: int = 3, q_len: int = 1, seq_lo: int = 40, seq_hi: int = 300,
+          window: int = 0, rope_theta: float = 0.0, page_size: int = 1, kv_scale: float = 1.0,
+          qkv_std: float = 1.0, table: str = "perm", sm_scale: float = 0.125,
+          num_q_heads: int = 16, num_kv_heads: int = 2, spare_pages: int = 3,
+          seed: int = 7) -> Workload:
+    """A workload small enough for the oracle to finish in well under a second."""
+    return Workload(name, batch, q_len, seq_lo, seq_hi, window, rope_theta, page_size=page_size,
+                    kv_scale=kv_scale, qkv_std=qkv_std, table=table, sm_scale=sm_scale,
+                    num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                    spare_pages=spare_pages, seed=seed)
+
+
+def with_seed(w: Workload, seed: int) -> Workload:
+    return replace(w, seed=seed)
+
