@@ -1,0 +1,62 @@
+"""Build the gfx950 C-ABI library libmi355x_gated_attn.so in-tree with hipcc.
+
+    python -m attention_decode_qk_amd.build [--force]
+
+Every HIP source is compiled for gfx950 only, with packed-fp32 instructions
+disabled (-Xclang -target-feature -Xclang -packed-fp32-ops), then linked into
+one shared library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+OUT_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libmi355x_gated_attn.so")
+SOURCES = ["prologue.hip", "attention.hip", "combine.hip", "api.cpp"]
+HEADERS = [os.path.join(CSRC, "kernels.h"),
+           os.path.join(os.path.dirname(HERE), "include", "mi355x_gated_attn.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-Wno-unused-result"]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    return obj
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile every source and link the library; returns its path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    if not force and os.path.exists(LIB):
+        newest = max(os.path.getmtime(os.path.join(CSRC, s)) for s in SOURCES)
+        newest = max([newest] + [os.path.getmtime(h) for h in HEADERS])
+        if os.path.getmtime(LIB) >= newest:
+            return LIB
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build(force="--force" in sys.argv or True, verbose=True)

@@ -1,0 +1,295 @@
+// api.cpp -- the C ABI declared in include/mi355x_gated_attn.h: validation,
+// the split-KV plan, workspace layout, the three launches of a step and the
+// optional per-kernel timing hook.
+//
+// The plan replaces the page's FA3 scheduler metadata and its H200 split
+// heuristic max(1, min(16, cdiv(132, B*Hkv))) ("012-attention-local-splits.py",
+// kernel_fn): on gfx950 a work unit covers both KV heads of a request (every
+// 128-byte cache row is used whole), so the split count is chosen from the
+// batch and the key bound against 256 compute units.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/mi355x_gated_attn.h"
+#include "kernels.h"
+
+using namespace mi355x_ga;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MI355X_GA_OK;
+}
+
+constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs x 32 CUs
+constexpr int kTargetUnitsPerCu = 2;
+constexpr int kMaxSplits = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+struct mi355x_gated_attn_ctx {
+  mi355x_gated_attn_config cfg;
+  int device;
+  float inv_freq[kHeadDim / 2];
+  bool planned = false;
+  int32_t splits = 0;
+  size_t q_bytes = 0, po_off = 0, pml_off = 0, ws_bytes = 0;
+  bool timing = false;
+  std::vector<hipEvent_t> events;  // 4 per timed step, reused
+  size_t events_used = 0;
+};
+
+extern "C" {
+
+const char* mi355x_gated_attn_last_error(void) { return g_last_error.c_str(); }
+
+int mi355x_gated_attn_supports(const mi355x_gated_attn_config* c) {
+  if (!c) return fail(MI355X_GA_INVALID_ARGUMENT, "config is NULL");
+  if (c->batch < 0) return fail(MI355X_GA_INVALID_ARGUMENT, "batch %d < 0", c->batch);
+  if (c->q_len < 1) return fail(MI355X_GA_INVALID_ARGUMENT, "q_len %d < 1", c->q_len);
+  if (c->num_q_heads < 1 || c->num_kv_heads < 1 || c->head_dim < 1)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "head counts and head_dim must be positive");
+  if (c->page_size < 1) return fail(MI355X_GA_INVALID_ARGUMENT, "page_size %d < 1", c->page_size);
+  if (c->window < 0) return fail(MI355X_GA_INVALID_ARGUMENT, "window %d < 0", c->window);
+  if (c->max_pages < 1) return fail(MI355X_GA_INVALID_ARGUMENT, "max_pages %d < 1", c->max_pages);
+  if (c->num_pages < 1) return fail(MI355X_GA_INVALID_ARGUMENT, "num_pages < 1");
+  if (!(c->rope_theta >= 0.0f) || std::isinf(c->rope_theta))
+    return fail(MI355X_GA_INVALID_ARGUMENT, "rope_theta must be 0 or a finite positive value");
+  if (!(c->sm_scale > 0.0f) || std::isinf(c->sm_scale))
+    return fail(MI355X_GA_INVALID_ARGUMENT, "sm_scale must be finite and positive");
+  if (!(c->kv_scale > 0.0f) || std::isinf(c->kv_scale))
+    return fail(MI355X_GA_INVALID_ARGUMENT, "kv_scale must be finite and positive");
+  if (c->num_q_heads % c->num_kv_heads)
+    return fail(MI355X_GA_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                c->num_q_heads, c->num_kv_heads);
+  if (c->head_dim != kHeadDim)
+    return fail(MI355X_GA_UNSUPPORTED, "head_dim %d: this build serves %d", c->head_dim, kHeadDim);
+  if (c->num_q_heads != kQHeads || c->num_kv_heads != kKvHeads)
+    return fail(MI355X_GA_UNSUPPORTED, "heads %d/%d: this build serves %d query / %d KV heads",
+                c->num_q_heads, c->num_kv_heads, kQHeads, kKvHeads);
+  if (c->q_len > kMaxQLen)
+    return fail(MI355X_GA_UNSUPPORTED, "q_len %d: this build serves 1..%d", c->q_len, kMaxQLen);
+  if ((int64_t)c->max_pages * c->page_size > (int64_t)1 << 30)
+    return fail(MI355X_GA_UNSUPPORTED, "max_pages * page_size exceeds 2^30 keys per request");
+  return ok();
+}
+
+int mi355x_gated_attn_prepare(const mi355x_gated_attn_config* cfg, int device,
+                              mi355x_gated_attn_ctx** out_ctx) {
+  if (!out_ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "out_ctx is NULL");
+  *out_ctx = nullptr;
+  int rc = mi355x_gated_attn_supports(cfg);
+  if (rc) return rc;
+  if (device < 0) return fail(MI355X_GA_INVALID_ARGUMENT, "device %d < 0", device);
+  auto* ctx = new (std::nothrow) mi355x_gated_attn_ctx();
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "out of host memory");
+  ctx->cfg = *cfg;
+  ctx->device = device;
+  // inv_freq[i] = 1 / theta^(2i/D): the exponent is exact in fp32, the power is
+  // rounded once to fp32, then the fp32 reciprocal (the page's fp32 recipe).
+  for (int i = 0; i < kHeadDim / 2; ++i) {
+    ctx->inv_freq[i] = 0.0f;
+    if (cfg->rope_theta != 0.0f) {
+      const float ex = (float)(2 * i) / (float)kHeadDim;
+      const float pw = (float)std::pow((double)cfg->rope_theta, (double)ex);
+      ctx->inv_freq[i] = 1.0f / pw;
+    }
+  }
+  *out_ctx = ctx;
+  return ok();
+}
+
+int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int32_t num_splits,
+                           size_t* workspace_bytes, int32_t* num_splits_out) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  if (max_context < 0) return fail(MI355X_GA_INVALID_ARGUMENT, "max_context %d < 0", max_context);
+  if (num_splits < 0 || num_splits > kMaxSplits)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "num_splits %d outside 0..%d", num_splits, kMaxSplits);
+  const auto& c = ctx->cfg;
+  int64_t keys = max_context;  // union of a request's visible keys
+  if (c.window > 0) keys = std::min<int64_t>(keys, (int64_t)c.window + c.q_len - 1);
+  int32_t s = num_splits;
+  if (s == 0) {
+    const int64_t min_keys_per_split = (int64_t)kAttnWaves * kKeyBlock;  // a block per wave
+    const int64_t by_len = std::max<int64_t>(1, (keys + min_keys_per_split - 1) / min_keys_per_split);
+    const int64_t target = (int64_t)kComputeUnits * kTargetUnitsPerCu;
+    const int64_t by_batch = c.batch > 0 ? (target + c.batch - 1) / c.batch : 1;
+    s = (int32_t)std::max<int64_t>(1, std::min<int64_t>({by_len, by_batch, (int64_t)kMaxSplits}));
+  }
+  const size_t T = (size_t)c.batch * c.q_len;
+  const size_t rows = T * kQHeads;  // (token, q head) rows
+  ctx->q_bytes = T * kQHeads * kHeadDim;
+  ctx->po_off = align_up(ctx->q_bytes, 256);
+  ctx->pml_off = align_up(ctx->po_off + (size_t)s * rows * kHeadDim * sizeof(float), 256);
+  ctx->ws_bytes = align_up(ctx->pml_off + (size_t)s * rows * 2 * sizeof(float), 256);
+  if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
+  ctx->splits = s;
+  ctx->planned = true;
+  if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
+  if (num_splits_out) *num_splits_out = s;
+  return ok();
+}
+
+int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
+                           const int64_t* cache_loc, const int32_t* cache_seqlens,
+                           const int32_t* page_table, const int32_t* seq_lens, void* k_cache,
+                           void* v_cache, const float* k_scale, const float* v_scale, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  (void)seq_lens;  // the page's attention call takes cache_seqlens only
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
+  const auto& c = ctx->cfg;
+  if (c.batch == 0) return ok();
+  const bool scaled = c.kv_scale != 1.0f;
+  const bool rope = c.rope_theta != 0.0f;
+  if (!qkv || !cache_loc || !cache_seqlens || !page_table || !k_cache || !v_cache || !out ||
+      !workspace)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "a required pointer is NULL");
+  if (rope && !positions) return fail(MI355X_GA_INVALID_ARGUMENT, "positions is NULL with RoPE on");
+  if (scaled && (!k_scale || !v_scale))
+    return fail(MI355X_GA_INVALID_ARGUMENT, "k_scale/v_scale are NULL on the scaled path");
+  if (workspace_bytes < ctx->ws_bytes)
+    return fail(MI355X_GA_WORKSPACE_TOO_SMALL, "workspace %zu bytes < planned %zu", workspace_bytes,
+                ctx->ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(qkv) % 8 || reinterpret_cast<uintptr_t>(k_cache) % 16 ||
+      reinterpret_cast<uintptr_t>(v_cache) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "qkv/cache/out pointers are misaligned");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "current device %d is not the ctx device %d", cur,
+                ctx->device);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const int T = c.batch * c.q_len;
+
+  PrologueParams pp{};
+  pp.qkv = reinterpret_cast<const uint16_t*>(qkv);
+  pp.positions = positions;
+  pp.cache_loc = cache_loc;
+  pp.k_cache = reinterpret_cast<uint8_t*>(k_cache);
+  pp.v_cache = reinterpret_cast<uint8_t*>(v_cache);
+  pp.k_scale = k_scale;
+  pp.v_scale = v_scale;
+  pp.q_out = ws;
+  pp.num_rows = c.num_pages * (int64_t)c.page_size;
+  pp.tokens = T;
+  pp.rope = rope ? 1 : 0;
+  pp.scaled = scaled ? 1 : 0;
+  std::memcpy(pp.inv_freq, ctx->inv_freq, sizeof pp.inv_freq);
+
+  AttnParams ap{};
+  ap.q = ws;
+  ap.k_cache = pp.k_cache;
+  ap.v_cache = pp.v_cache;
+  ap.page_table = page_table;
+  ap.cache_seqlens = cache_seqlens;
+  ap.k_scale = k_scale;
+  ap.part_o = reinterpret_cast<float*>(ws + ctx->po_off);
+  ap.part_ml = reinterpret_cast<float*>(ws + ctx->pml_off);
+  ap.num_pages = c.num_pages;
+  ap.batch = c.batch;
+  ap.splits = ctx->splits;
+  ap.max_pages = c.max_pages;
+  ap.page_size = c.page_size;
+  ap.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;
+  ap.window = c.window;
+  ap.scaled = pp.scaled;
+  ap.sm_scale_log2 = c.sm_scale * 1.4426950408889634f;
+
+  CombineParams cp{};
+  cp.part_o = ap.part_o;
+  cp.part_ml = ap.part_ml;
+  cp.qkv = pp.qkv;
+  cp.v_scale = v_scale;
+  cp.out = reinterpret_cast<uint16_t*>(out);
+  cp.tokens = T;
+  cp.q_len = c.q_len;
+  cp.splits = ctx->splits;
+  cp.scaled = pp.scaled;
+
+  hipEvent_t* ev = nullptr;
+  if (ctx->timing) {
+    if (ctx->events_used + 4 > ctx->events.size()) {
+      for (int k = 0; k < 4; ++k) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "hipEventCreate failed");
+        ctx->events.push_back(e);
+      }
+    }
+    ev = &ctx->events[ctx->events_used];
+    ctx->events_used += 4;
+  }
+  hipError_t e = hipSuccess;
+  if (ev) e = hipEventRecord(ev[0], st);
+  if (e == hipSuccess) e = launch_prologue(pp, st);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
+  if (e == hipSuccess) e = launch_attention(ap, c.q_len, st);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
+  if (e == hipSuccess) e = launch_combine(cp, st);
+  if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
+  if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx) {
+  if (!ctx) return;
+  for (hipEvent_t e : ctx->events) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+int mi355x_gated_attn_timing(mi355x_gated_attn_ctx* ctx, int enable) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  ctx->timing = enable != 0;
+  if (ctx->timing) ctx->events_used = 0;
+  return ok();
+}
+
+int mi355x_gated_attn_timing_read(mi355x_gated_attn_ctx* ctx, double* kernel_ms, int64_t* steps) {
+  if (!ctx || !kernel_ms) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx or kernel_ms is NULL");
+  double acc[3] = {0, 0, 0};
+  const size_t n = ctx->events_used / 4;
+  if (n) {
+    if (hipEventSynchronize(ctx->events[ctx->events_used - 1]) != hipSuccess)
+      return fail(MI355X_GA_HIP_ERROR, "hipEventSynchronize failed");
+  }
+  for (size_t i = 0; i < n; ++i) {
+    for (int k = 0; k < 3; ++k) {
+      float ms = 0.0f;
+      if (hipEventElapsedTime(&ms, ctx->events[4 * i + k], ctx->events[4 * i + k + 1]) != hipSuccess)
+        return fail(MI355X_GA_HIP_ERROR, "hipEventElapsedTime failed");
+      acc[k] += ms;
+    }
+  }
+  for (int k = 0; k < 3; ++k) kernel_ms[k] = acc[k];
+  if (steps) *steps = (int64_t)n;
+  ctx->events_used = 0;
+  return ok();
+}
+
+}  // extern "C"

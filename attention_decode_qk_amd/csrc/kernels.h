@@ -1,0 +1,78 @@
+// kernels.h -- internal interface between the C-ABI host code and the three
+// gfx950 kernels of the gated-attention step.  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355x_ga {
+
+// Shapes this build serves: one GPU's head share of the page's model
+// (16 query heads, 2 KV heads, head_dim 64; 8 query heads per KV head).
+constexpr int kHeadDim = 64;
+constexpr int kQHeads = 16;
+constexpr int kKvHeads = 2;
+constexpr int kGroup = kQHeads / kKvHeads;           // 8
+constexpr int kRowBytes = kKvHeads * kHeadDim;       // 128 B: one cache row, both KV heads
+constexpr int kMaxQLen = 8;
+constexpr int kWidth = (2 * kQHeads + 2 * kKvHeads) * kHeadDim;  // 2304 projection columns
+constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
+
+// Split attention work unit: a workgroup of kAttnWaves waves walks one
+// request's key chunk in blocks of kKeyBlock keys (one block per wave at a time).
+constexpr int kAttnWaves = 4;
+constexpr int kKeyBlock = 32;
+
+struct PrologueParams {
+  const uint16_t* qkv;       // bf16 [T, kWidth]
+  const int64_t* positions;  // [T]
+  const int64_t* cache_loc;  // [T]
+  uint8_t* k_cache;          // e4m3 [rows, kKvHeads, kHeadDim]
+  uint8_t* v_cache;
+  const float* k_scale;      // device scalars, read iff scaled
+  const float* v_scale;
+  uint8_t* q_out;            // e4m3 [T, kQHeads, kHeadDim]
+  int64_t num_rows;          // pool rows (bounds for cache_loc)
+  int32_t tokens;            // T = B * L
+  int32_t rope;              // 1 iff rope_theta != 0
+  int32_t scaled;            // 1 iff kv_scale != 1
+  float inv_freq[kHeadDim / 2];
+};
+
+struct AttnParams {
+  const uint8_t* q;              // e4m3 [T, kQHeads, kHeadDim]
+  const uint8_t* k_cache;        // e4m3 [rows, kKvHeads, kHeadDim]
+  const uint8_t* v_cache;
+  const int32_t* page_table;     // [B, max_pages]
+  const int32_t* cache_seqlens;  // [B]
+  const float* k_scale;          // read iff scaled
+  float* part_o;                 // fp32 [B, S, L*kQHeads, kHeadDim]
+  float* part_ml;                // fp32 [B, S, L*kQHeads, 2]: running max (log2 units), sum
+  int64_t num_pages;
+  int32_t batch;
+  int32_t splits;                // S
+  int32_t max_pages;
+  int32_t page_size;
+  int32_t page_shift;            // log2(page_size) if a power of two, else -1
+  int32_t window;
+  int32_t scaled;
+  float sm_scale_log2;           // sm_scale * log2(e)
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_ml;
+  const uint16_t* qkv;       // gate logits live in the projection row
+  const float* v_scale;      // read iff scaled
+  uint16_t* out;             // bf16 [T, kQHeads * kHeadDim]
+  int32_t tokens;
+  int32_t q_len;
+  int32_t splits;
+  int32_t scaled;
+};
+
+hipError_t launch_prologue(const PrologueParams& p, hipStream_t stream);
+hipError_t launch_attention(const AttnParams& p, int q_len, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+}  // namespace mi355x_ga

@@ -1,0 +1,165 @@
+/*
+ * mi355x_gated_attn.h -- C ABI of the MI355X (gfx950) gated-attention step.
+ *
+ * One decoder layer's attention step for a decode (q_len 1) or speculative
+ * verify (q_len up to 8) batch, at one GPU's head share, as defined on the
+ * page "012-attention-local-splits.py" (SGLang's Muse Spark Open gated
+ * attention, FP8 e4m3 KV cache).  In the page's order (module docstring):
+ *
+ *   1. per-head unweighted RMSNorm (eps 1e-5) of the q and k heads of the
+ *      fused bf16 projection row, with interleaved RoPE on sliding-window
+ *      layers (`_prepare_qkv`, `_cos_sin`);
+ *   2. k and v stored as float8 e4m3 at each new token's flat cache row,
+ *      divided by the cache scales when they are not 1 (`set_kv_buffer`);
+ *      q cast to e4m3 (`prepare_paged_mha_query`);
+ *   3. paged, causal, sliding-window grouped-query attention over the e4m3
+ *      cache (the `flash_attn_with_kvcache` call in `kernel_fn`);
+ *   4. per-head RMSNorm of the bf16 attention output times sigmoid(gate)
+ *      (`rms_norm_gate`).
+ *
+ * Conventions.  Every buffer is caller-owned device memory unless stated;
+ * the library never allocates, frees or retains a caller buffer.  Every
+ * entry point returns an int status (MI355X_GA_*); nothing throws across the
+ * ABI and mi355x_gated_attn_last_error() gives the calling thread's last
+ * message.  Validation is host-side and reads scalars only: device-resident
+ * values (lengths, rows, positions) are never read on the host, so a step can
+ * be captured in a HIP graph.  Out-of-range device values are clamped where a
+ * memory access depends on them (no fault), but their results are undefined.
+ */
+#ifndef MI355X_GATED_ATTN_H
+#define MI355X_GATED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  MI355X_GA_OK = 0,
+  MI355X_GA_UNSUPPORTED = 1,          /* a shape this build does not serve      */
+  MI355X_GA_INVALID_ARGUMENT = 2,     /* bad scalar, null pointer, unplanned ctx */
+  MI355X_GA_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes below the plan's size  */
+  MI355X_GA_HIP_ERROR = 4             /* a HIP runtime call or launch failed    */
+};
+
+/*
+ * Step configuration: the page's Config (batch, q_len, num_q_heads,
+ * num_kv_heads, head_dim, page_size, window, rope_theta, sm_scale, kv_scale)
+ * plus the two bounds the library needs to keep every access in range.
+ */
+typedef struct mi355x_gated_attn_config {
+  int32_t batch;        /* B >= 0 requests; B == 0 makes every step a no-op     */
+  int32_t q_len;        /* L new tokens per request, 1..8 (causal in the block) */
+  int32_t num_q_heads;  /* Hq; this build serves 16 (one GPU's share under TP8) */
+  int32_t num_kv_heads; /* Hkv; this build serves 2; q head h reads h/(Hq/Hkv)  */
+  int32_t head_dim;     /* D; 64                                                */
+  int32_t page_size;    /* P >= 1 cache rows per page                           */
+  int32_t window;       /* W >= 0: a query at p sees keys p-W+1..p; 0 = all     */
+  int32_t max_pages;    /* >= 1, row stride of page_table                       */
+  int64_t num_pages;    /* >= 1, pages in the cache pool (rows = num_pages * P) */
+  float rope_theta;     /* 0 = no RoPE; > 0 = interleaved RoPE base             */
+  float sm_scale;       /* the softmax scale applied to q.k (the page folds its */
+                        /* query factor in: sm_scale * qk_scale_factor)        */
+  float kv_scale;       /* != 1 selects the scaled store (divide by k_scale /   */
+                        /* v_scale) and the descaled read; == 1 ignores them    */
+} mi355x_gated_attn_config;
+
+/* Opaque per-configuration context (host memory only). */
+typedef struct mi355x_gated_attn_ctx mi355x_gated_attn_ctx;
+
+/*
+ * Whether this build serves cfg: returns MI355X_GA_OK, MI355X_GA_UNSUPPORTED
+ * (head_dim != 64, Hq != 16, Hkv != 2, q_len outside 1..8) or
+ * MI355X_GA_INVALID_ARGUMENT (negative or zero sizes, window < 0,
+ * rope_theta < 0, non-finite or non-positive scales).  Pure host code.
+ */
+int mi355x_gated_attn_supports(const mi355x_gated_attn_config* cfg);
+
+/*
+ * Validate cfg and create a context bound to HIP device `device`.
+ * Host-only: computes the RoPE inverse frequencies, 1 / theta^(2i/D) with the
+ * power and the reciprocal each rounded to fp32 (the page's `_cos_sin`
+ * recipe), and touches no device memory.  *out_ctx receives the context;
+ * release it with mi355x_gated_attn_destroy.
+ */
+int mi355x_gated_attn_prepare(const mi355x_gated_attn_config* cfg, int device,
+                              mi355x_gated_attn_ctx** out_ctx);
+
+/*
+ * Plan the split-KV schedule for every step (and layer) that uses this ctx,
+ * outside any graph capture; it replaces the page's per-step FA3 scheduler
+ * metadata and its split-count heuristic.  max_context bounds
+ * cache_seqlens[b] (keys per request including the new tokens) and only steers
+ * the split count; num_splits > 0 forces the count (1..256), 0 chooses it.
+ * Outputs (either may be NULL): *workspace_bytes = the workspace a step needs,
+ * *num_splits_out = the chosen split count.  Host-only.
+ */
+int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int32_t num_splits,
+                           size_t* workspace_bytes, int32_t* num_splits_out);
+
+/*
+ * One layer-step, asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream); the calling thread's current device must be the ctx's device.
+ * No host synchronisation, allocation or device-value read: capturable.
+ *
+ *   qkv            bf16 [B, L, (2Hq + 2Hkv) * D], rows contiguous: q heads |
+ *                  k heads | v heads | gate logits (Hq*D)
+ *   positions      int64 [B*L]  RoPE position of each new token (read iff
+ *                  rope_theta != 0; must be < 2^21 as on the page)
+ *   cache_loc      int64 [B*L]  flat cache row of each new token; rows outside
+ *                  [0, num_pages*P) are not written
+ *   cache_seqlens  int32 [B]    keys per request including the L new tokens;
+ *                  query i of request b sits at p = cache_seqlens[b] - L + i
+ *   page_table     int32 [B, max_pages]  physical page of each logical page,
+ *                  -1 where unused (never read beyond a request's keys)
+ *   seq_lens       int32 [B]    cached tokens per request; accepted for parity
+ *                  with the page's inputs and not read (the page's attention
+ *                  call takes cache_seqlens); may be NULL
+ *   k_cache, v_cache  float8 e4m3 (OCP) [num_pages, P, Hkv, D], written in
+ *                  place at the cache_loc rows only
+ *   k_scale, v_scale  device float32 scalars (read iff kv_scale != 1; may be
+ *                  NULL otherwise)
+ *   out            bf16 [B, L, Hq * D]
+ *   workspace      device memory of at least the planned size, 256-byte
+ *                  aligned.  Layout after a step: bytes [0, B*L*Hq*D) hold q
+ *                  as e4m3 [B*L, Hq, D]; the rest holds split partials.
+ * Calls that share a workspace, or write the same cache rows, must be ordered
+ * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
+ */
+int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
+                           const int64_t* cache_loc, const int32_t* cache_seqlens,
+                           const int32_t* page_table, const int32_t* seq_lens, void* k_cache,
+                           void* v_cache, const float* k_scale, const float* v_scale, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release a context (NULL is ignored).  Does not synchronise. */
+void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx);
+
+/* The calling thread's last error message ("" if none). */
+const char* mi355x_gated_attn_last_error(void);
+
+/*
+ * Measurement hook (not part of the page's interface): while enabled, each
+ * step records HIP events on its stream around each of its three kernels
+ * (prologue, split attention, combine + gated epilogue).  `enable` != 0
+ * starts a fresh accumulation, 0 stops recording.  Not for use under graph
+ * capture.
+ */
+int mi355x_gated_attn_timing(mi355x_gated_attn_ctx* ctx, int enable);
+
+/*
+ * Wait for the recorded events and return the summed per-kernel durations in
+ * milliseconds (kernel_ms[3]) and the number of timed steps; then clear the
+ * accumulation.
+ */
+int mi355x_gated_attn_timing_read(mi355x_gated_attn_ctx* ctx, double* kernel_ms,
+                                  int64_t* steps);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355X_GATED_ATTN_H */

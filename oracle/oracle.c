@@ -272,7 +272,9 @@ int orc_prologue(const orc_config* cfg, const uint16_t* qkv, const int64_t* posi
   for (int64_t t = 0; t < T; ++t) {
     const uint16_t* row = qkv + t * width;
     int64_t slot = cache_loc[t];
-    if (slot < 0 || slot >= rows) return ORC_BAD_ROW;
+    /* READING: a token whose cache row lies outside the pool (e.g. a padded
+     * request slot) stores nothing; its q is still produced. */
+    const int store = slot >= 0 && slot < rows;
     for (int h = 0; h < hq + hkv; ++h) { /* q heads then k heads */
       norm_row(row + (int64_t)h * d, d, y, NULL);
       if (cfg->rope_theta != 0.0f) rope_row(y, d, positions[t], inv_freq);
@@ -283,7 +285,7 @@ int orc_prologue(const orc_config* cfg, const uint16_t* qkv, const int64_t* posi
         for (int c = 0; c < d; ++c) {
           float key = y[c];
           if (scaled) key = bf16r(key / k_scale); /* fp32 quotient, then bf16 */
-          k_cache[(slot * hkv + g) * d + c] = orc_e4m3_encode(key);
+          if (store) k_cache[(slot * hkv + g) * d + c] = orc_e4m3_encode(key);
         }
       }
     }
@@ -292,7 +294,7 @@ int orc_prologue(const orc_config* cfg, const uint16_t* qkv, const int64_t* posi
       for (int c = 0; c < d; ++c) {
         float val = orc_bf16_to_float(vin[c]);
         if (scaled) val = bf16r(val / v_scale);
-        v_cache[(slot * hkv + g) * d + c] = orc_e4m3_encode(val);
+        if (store) v_cache[(slot * hkv + g) * d + c] = orc_e4m3_encode(val);
       }
     }
   }

@@ -1,0 +1,186 @@
+"""Host-side tests of the C-ABI library (no GPU needed): it loads, exports every
+symbol the header declares, and validates configurations, plans and step
+arguments with the documented status codes before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import attention_decode_qk_amd as ga
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ga.LIB_PATH):
+        from attention_decode_qk_amd import build
+        build.build(force=False)
+    return ga.lib()
+
+
+def _declared_symbols():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for f in os.listdir(inc):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(mi355x_gated_attn_\w+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol(L):
+    declared = _declared_symbols()
+    assert len(declared) >= 8
+    for name in sorted(declared):
+        assert hasattr(L, name), name
+    assert declared == set(ga.EXPORTED)
+
+
+def cfg(**kw):
+    base = dict(batch=32, q_len=1, page_size=1, window=2048, max_pages=16386, num_pages=400000,
+                rope_theta=500000.0)
+    base.update(kw)
+    return ga.make_config(**base)
+
+
+def test_supports_accepts_the_served_shapes(L):
+    for q_len in range(1, 9):
+        assert ga.mi355x_gated_attn_supports(cfg(q_len=q_len)) == ga.MI355X_GA_OK
+    assert ga.mi355x_gated_attn_supports(cfg(batch=0)) == ga.MI355X_GA_OK
+    assert ga.mi355x_gated_attn_supports(cfg(page_size=64, window=0, rope_theta=0.0,
+                                             kv_scale=0.5)) == ga.MI355X_GA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=128), ga.MI355X_GA_UNSUPPORTED),
+    (dict(num_q_heads=15), ga.MI355X_GA_UNSUPPORTED),
+    (dict(num_q_heads=8, num_kv_heads=1), ga.MI355X_GA_UNSUPPORTED),
+    (dict(q_len=9), ga.MI355X_GA_UNSUPPORTED),
+    (dict(q_len=0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(batch=-1), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(page_size=0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(window=-1), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(max_pages=0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(num_pages=0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(rope_theta=-1.0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(rope_theta=float("inf")), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(sm_scale=0.0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(sm_scale=float("nan")), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(kv_scale=-0.5), ga.MI355X_GA_INVALID_ARGUMENT),
+])
+def test_supports_rejects(L, kw, status):
+    assert ga.mi355x_gated_attn_supports(cfg(**kw)) == status
+    assert ga.mi355x_gated_attn_last_error() != ""
+    with pytest.raises(ga.GatedAttnError) as e:
+        ga.mi355x_gated_attn_prepare(cfg(**kw))
+    assert e.value.status == status
+
+
+def test_prepare_plan_workspace_layout(L):
+    c = cfg(batch=32, q_len=8)
+    ctx = ga.mi355x_gated_attn_prepare(c)
+    try:
+        ws, s = ga.mi355x_gated_attn_plan(ctx, 32776, 4)
+        assert s == 4
+        T = 32 * 8
+        q = T * 16 * 64
+        po = -(-q // 256) * 256
+        pml = -(-(po + s * T * 16 * 64 * 4) // 256) * 256
+        assert ws == -(-(pml + s * T * 16 * 2 * 4) // 256) * 256
+        ws0, s0 = ga.mi355x_gated_attn_plan(ctx, 32776, 0)
+        assert 1 <= s0 <= 256
+        with pytest.raises(ga.GatedAttnError):
+            ga.mi355x_gated_attn_plan(ctx, 100, 257)
+        with pytest.raises(ga.GatedAttnError):
+            ga.mi355x_gated_attn_plan(ctx, -1, 0)
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_auto_split_count_fills_the_chip(L):
+    """Automatic plans: about two work units per compute unit, at least one
+    32-key block per wave, never more than 256 splits."""
+    cases = [(1, 1, 0, 513), (32, 1, 2048, 16385), (64, 1, 0, 32769), (32, 8, 2048, 32776),
+             (8, 8, 0, 131080)]
+    for B, Lq, W, ctxlen in cases:
+        ctx = ga.mi355x_gated_attn_prepare(cfg(batch=B, q_len=Lq, window=W))
+        try:
+            _, s = ga.mi355x_gated_attn_plan(ctx, ctxlen, 0)
+            keys = min(ctxlen, W + Lq - 1) if W else ctxlen
+            assert s <= max(1, -(-keys // 128))
+            assert s <= 256
+            assert B * s <= 512 + B
+        finally:
+            ga.mi355x_gated_attn_destroy(ctx)
+
+
+def _raw_step(L, ctx, **over):
+    """Call the C step with fake (never dereferenced on the host) pointers."""
+    P = ctypes.c_void_p
+    args = dict(qkv=P(0x1000), positions=P(0x2000), cache_loc=P(0x3000), cache_seqlens=P(0x4000),
+                page_table=P(0x5000), seq_lens=P(0x6000), k_cache=P(0x10000), v_cache=P(0x20000),
+                k_scale=P(0x7000), v_scale=P(0x8000), out=P(0x9000), workspace=P(0x100000),
+                ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    return L.mi355x_gated_attn_step(ctx, args["qkv"], args["positions"], args["cache_loc"],
+                                    args["cache_seqlens"], args["page_table"], args["seq_lens"],
+                                    args["k_cache"], args["v_cache"], args["k_scale"],
+                                    args["v_scale"], args["out"], args["workspace"],
+                                    args["ws_bytes"], args["stream"])
+
+
+def test_step_argument_errors_are_reported_before_any_launch(L):
+    ctx = ga.mi355x_gated_attn_prepare(cfg(kv_scale=0.5))
+    try:
+        assert _raw_step(L, ctx) == ga.MI355X_GA_INVALID_ARGUMENT  # not planned yet
+        ws, _ = ga.mi355x_gated_attn_plan(ctx, 16385, 0)
+        for name in ("qkv", "cache_loc", "cache_seqlens", "page_table", "k_cache", "v_cache",
+                     "out", "workspace", "positions", "k_scale", "v_scale"):
+            assert _raw_step(L, ctx, **{name: None}) == ga.MI355X_GA_INVALID_ARGUMENT, name
+        assert _raw_step(L, ctx, ws_bytes=ws - 1) == ga.MI355X_GA_WORKSPACE_TOO_SMALL
+        assert _raw_step(L, ctx, workspace=ctypes.c_void_p(0x100010)) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+        assert "aligned" in ga.mi355x_gated_attn_last_error()
+        assert L.mi355x_gated_attn_step(None, *([None] * 12), 0, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_unscaled_rope_free_step_needs_no_scales_or_positions(L):
+    ctx = ga.mi355x_gated_attn_prepare(cfg(rope_theta=0.0, window=0))
+    try:
+        ws, _ = ga.mi355x_gated_attn_plan(ctx, 1000, 0)
+        rc = _raw_step(L, ctx, positions=None, k_scale=None, v_scale=None, ws_bytes=ws)
+        # past argument validation: only the device check remains (no GPU here)
+        assert rc in (ga.MI355X_GA_OK, ga.MI355X_GA_INVALID_ARGUMENT, ga.MI355X_GA_HIP_ERROR)
+        if rc == ga.MI355X_GA_INVALID_ARGUMENT:
+            assert "device" in ga.mi355x_gated_attn_last_error()
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_empty_batch_is_a_no_op(L):
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=0))
+    try:
+        ga.mi355x_gated_attn_plan(ctx, 100, 0)
+        assert L.mi355x_gated_attn_step(ctx, *([None] * 12), 0, None) == ga.MI355X_GA_OK
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_destroy_accepts_null(L):
+    ga.mi355x_gated_attn_destroy(None)
+
+
+def test_timing_hook_without_steps(L):
+    ctx = ga.mi355x_gated_attn_prepare(cfg())
+    try:
+        ga.mi355x_gated_attn_timing(ctx, True)
+        ms, n = ga.mi355x_gated_attn_timing_read(ctx)
+        assert n == 0 and ms == [0.0, 0.0, 0.0]
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
