@@ -1,0 +1,314 @@
+"""Benchmark of the gated-attention layer-step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload swa_decode]
+
+A "step" is one layer-step of the whole hot path (prologue, split attention,
+combine + gated epilogue) over one batch of synthetic inputs.  The default
+workload is the decode batch the headline metric is quoted on: B=32, L=1,
+16 query / 2 KV heads, head_dim 64, page_size 1, window 2048, RoPE theta
+5e5, cached lengths uniform in [4096, 16384], shuffled page table.
+
+Cold-cache discipline: the steps round-robin over enough per-layer KV pools
+(own caches, own page-table permutation, own projection rows) to exceed 1 GiB,
+four times the 256 MB Infinity Cache, as a model's layers would.  Each layer's
+step is captured once in a HIP graph (outside the timed region) and the timed
+region replays exactly K of them, bracketed by synchronisation and HIP events
+on the replay stream.  A second, eager pass with the library's per-kernel
+event hook measures each kernel's average duration (the GPU is pre-loaded with
+a spin kernel so the host enqueues ahead and the kernels run back to back).
+
+Prints one JSON line (see the design doc for every field).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_swa_decode_counters.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "attention_decode_qk_amd", "csrc", f)
+                  for f in ("attention.hip", "kernels.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def attended_keys(w, cache_seqlens) -> int:
+    """Keys a step must read: per request, the union of its queries' visible
+    ranges (query i at p = cache_seqlens - L + i sees max(0, p-W+1)..p)."""
+    total = 0
+    for cs in cache_seqlens.tolist():
+        last = cs - 1
+        first = cs - w.q_len
+        if w.window > 0:
+            first = first - w.window + 1
+        first = max(first, 0)
+        total += max(0, last - first + 1)
+    return total
+
+
+def algorithmic_bytes(w, x):
+    """Per step: KV bytes (the metric's numerator), and the attention kernel's
+    algorithmic bytes (KV rows + page-table entries of the attended keys + q)."""
+    keys = attended_keys(w, x.cache_seqlens)
+    kv = keys * w.num_kv_heads * w.head_dim * 2
+    pages = 0
+    for cs in x.cache_seqlens.tolist():
+        first = cs - w.q_len - (w.window - 1 if w.window > 0 else cs)
+        first = max(first, 0)
+        pages += (cs - 1) // w.page_size - first // w.page_size + 1
+    q = x.tokens * w.num_q_heads * w.head_dim
+    return kv, kv + 4 * pages + q
+
+
+def load_traffic():
+    """HBM traffic per attention launch from the committed counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", text, re.M)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(x, budget_s: float):
+    """The oracle as it stands, single-threaded on this host, on whole steps of
+    layer pool 0's inputs until the time budget is used (at least one step)."""
+    import numpy as np
+    import oracle
+    cfg = oracle.Config(batch=x.w.batch, q_len=x.w.q_len, num_q_heads=x.w.num_q_heads,
+                        num_kv_heads=x.w.num_kv_heads, head_dim=x.w.head_dim,
+                        page_size=x.w.page_size, window=x.w.window, max_pages=x.max_pages,
+                        num_pages=x.num_pages, rope_theta=x.w.rope_theta,
+                        sm_scale=x.w.sm_scale, kv_scale=x.w.kv_scale)
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.step(cfg, x.qkv, x.positions, x.cache_loc, x.cache_seqlens, x.page_table, kc, vc,
+                    x.k_scale, x.v_scale)
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    del np
+    return n, dt
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="swa_decode")
+    ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of layer pools (cold cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = plan)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the step is "
+                          "head-sharded with no exchange, so N GPUs run N independent copies; "
+                          "--gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_decode_qk_amd as ga
+    import synth
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty(n, dtype=torch.uint8, device=dev)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return
+
+    w = synth.WORKLOADS[args.workload]
+    x0 = synth.make_inputs(w)
+    kv_bytes, attn_bytes = algorithmic_bytes(w, x0)
+    pool_bytes = x0.k_cache.nbytes + x0.v_cache.nbytes + x0.page_table.nbytes
+    n_layers = max(1, int(np.ceil(args.cold_bytes * (1 << 30) / pool_bytes)))
+    print(f"[bench] {w.name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}; "
+          f"{n_layers} layer pools of {pool_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+
+    cfg = ga.make_config(w.batch, w.q_len, w.page_size, w.window, x0.max_pages, x0.num_pages,
+                         w.rope_theta, w.sm_scale, w.kv_scale)
+    step = ga.GatedAttnStep(cfg, int(w.seq_hi + w.q_len), args.splits)
+
+    # Layer pools: pool 0 is the tests' seeded input; the others are drawn on
+    # the device with the same recipe (own page-table permutation, caches,
+    # projection rows) and the same lengths.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    P = w.page_size
+    seq = torch.from_numpy(x0.seq_lens).to(dev)
+    cache_seqlens = torch.from_numpy(x0.cache_seqlens).to(dev)
+    positions = torch.from_numpy(x0.positions).to(dev)
+    n_pages = (x0.cache_seqlens.astype(np.int64) + P - 1) // P
+    k_scale = torch.tensor([x0.k_scale], dtype=torch.float32, device=dev)
+    v_scale = torch.tensor([x0.v_scale], dtype=torch.float32, device=dev)
+    pos_b = torch.from_numpy(x0.positions.reshape(w.batch, w.q_len)).to(dev)
+    layers = []
+    for li in range(n_layers):
+        if li == 0:
+            pt = torch.from_numpy(x0.page_table).to(dev)
+            kc = torch.from_numpy(x0.k_cache).to(dev)
+            vc = torch.from_numpy(x0.v_cache).to(dev)
+            qkv = torch.from_numpy(x0.qkv.view(np.int16)).to(dev)
+        else:
+            perm = torch.randperm(x0.num_pages, generator=gen, device=dev).to(torch.int32)
+            pt = torch.full((w.batch, x0.max_pages), -1, dtype=torch.int32, device=dev)
+            off = 0
+            for b in range(w.batch):
+                pt[b, : n_pages[b]] = perm[off: off + n_pages[b]]
+                off += int(n_pages[b])
+            rows = x0.num_pages * P
+            kc = torch.randn((rows, w.num_kv_heads, w.head_dim), generator=gen, device=dev) \
+                .to(torch.float8_e4m3fn).view(torch.uint8)
+            vc = torch.randn((rows, w.num_kv_heads, w.head_dim), generator=gen, device=dev) \
+                .to(torch.float8_e4m3fn).view(torch.uint8)
+            qkv = (torch.randn((w.batch, w.q_len, w.width), generator=gen, device=dev)
+                   * w.qkv_std).to(torch.bfloat16).view(torch.int16)
+        cl = (pt.gather(1, pos_b // P).to(torch.int64) * P + pos_b % P).reshape(-1).contiguous()
+        out = torch.empty((w.batch, w.q_len, w.num_q_heads * w.head_dim), dtype=torch.int16,
+                          device=dev)
+        layers.append(dict(qkv=qkv, cache_loc=cl, page_table=pt, k_cache=kc, v_cache=vc, out=out))
+    torch.cuda.synchronize()
+
+    def run(li, stream=None):
+        L_ = layers[li]
+        step(L_["qkv"], positions, L_["cache_loc"], cache_seqlens, L_["page_table"], seq,
+             L_["k_cache"], L_["v_cache"], k_scale, v_scale, L_["out"], stream)
+
+    # One HIP graph per layer-step, captured outside the timed region.
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(cap):
+        for li in range(n_layers):
+            run(li, cap)
+        torch.cuda.synchronize()
+        for li in range(n_layers):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                run(li, cap)
+            graphs.append(g)
+    torch.cuda.synchronize()
+
+    def timed(n_steps, rotate=True):
+        for k in range(args.warmup):
+            graphs[k % n_layers if rotate else 0].replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(n_steps):
+            graphs[k % n_layers if rotate else 0].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    t_wall0 = time.perf_counter()
+    ms_total = timed(args.steps, rotate=True)
+    wall_s = time.perf_counter() - t_wall0
+    ms_warm = timed(args.steps, rotate=False)
+    us_step = 1000.0 * ms_total / args.steps
+    us_warm = 1000.0 * ms_warm / args.steps
+
+    # Per-kernel durations: eager steps with the event hook, host enqueueing
+    # ahead of a spinning GPU so the three kernels run back to back.
+    n_k = min(args.steps, 200)
+    torch.cuda.synchronize()
+    ga.mi355x_gated_attn_timing(step.ctx, True)
+    torch.cuda._sleep(int(5e7))
+    for k in range(n_k):
+        run(k % n_layers)
+    kernel_ms, n_timed = ga.mi355x_gated_attn_timing_read(step.ctx)
+    ga.mi355x_gated_attn_timing(step.ctx, False)
+    torch.cuda.synchronize()
+    k_us = [1000.0 * v / max(1, n_timed) for v in kernel_ms]
+    attn_us = k_us[1]
+
+    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    traffic = load_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(kv_bytes / (us_step * 1e-6) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_total / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_len": w.q_len,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size, "window": w.window,
+                   "rope_theta": w.rope_theta, "sm_scale": w.sm_scale, "kv_scale": w.kv_scale,
+                   "seq_lens": [w.seq_lo, w.seq_hi], "splits": step.splits,
+                   "layer_pools": n_layers, "cold_cache_bytes": n_layers * pool_bytes},
+        "us_per_layer_step": round(us_step, 3),
+        "kv_bytes_per_step": kv_bytes,
+        "kv_gbs_pct_of_peak": round(100.0 * kv_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+        "kernel_us": {"prologue": round(k_us[0], 3), "attention": round(k_us[1], 3),
+                      "combine_epilogue": round(k_us[2], 3)},
+        "attention_kv_gbs": round(kv_bytes / (attn_us * 1e-6) / 1e9, 1),
+        "warm_single_pool": {"us_per_layer_step": round(us_warm, 3),
+                             "kv_gbs": round(kv_bytes / (us_warm * 1e-6) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes": attn_bytes,
+                     "kernel": "attn_split_kernel<1>", "kernel_source": kernel_source_hash()},
+        "timed_wall_s": round(wall_s, 3),
+    }
+    if not args.no_cpu_baseline:
+        n, dt = cpu_baseline(x0, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(n * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n} whole steps of layer pool 0 ({w.name}), single-threaded, {dt:.1f} s",
+        }
+    print(json.dumps(result), flush=True)
+    step.close()
+
+
+if __name__ == "__main__":
+    main()
