@@ -22,7 +22,7 @@ MI355X_GA_WORKSPACE_TOO_SMALL = 3
 MI355X_GA_HIP_ERROR = 4
 
 EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_gated_attn_plan",
-            "mi355x_gated_attn_step", "mi355x_gated_attn_destroy",
+            "mi355x_gated_attn_workspace_init", "mi355x_gated_attn_step", "mi355x_gated_attn_destroy",
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
             "mi355x_gated_attn_timing_read"]
 
@@ -61,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.mi355x_gated_attn_plan.argtypes = [P, ctypes.c_int32, ctypes.c_int32,
                                              ctypes.POINTER(ctypes.c_size_t),
                                              ctypes.POINTER(ctypes.c_int32)]
+        L.mi355x_gated_attn_workspace_init.argtypes = [P, P, ctypes.c_size_t, P]
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_destroy.argtypes = [P]
         L.mi355x_gated_attn_destroy.restype = None
@@ -147,6 +148,16 @@ def mi355x_gated_attn_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_t
         _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
 
 
+def mi355x_gated_attn_workspace_init(ctx, workspace, stream=None):
+    """Zero a new workspace's counters (once, before its first step)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(workspace.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_workspace_init(ctx, _ptr(workspace), _nbytes(workspace),
+                                                  ctypes.c_void_p(handle)))
+
+
 def mi355x_gated_attn_destroy(ctx):
     lib().mi355x_gated_attn_destroy(ctx)
 
@@ -156,11 +167,11 @@ def mi355x_gated_attn_timing(ctx, enable: bool):
 
 
 def mi355x_gated_attn_timing_read(ctx):
-    """Returns ([prologue_ms, attention_ms, combine_ms] summed, timed steps)."""
-    ms = (ctypes.c_double * 3)()
+    """Returns (summed kernel milliseconds, timed steps)."""
+    ms = ctypes.c_double()
     n = ctypes.c_int64()
-    _check(lib().mi355x_gated_attn_timing_read(ctx, ms, ctypes.byref(n)))
-    return list(ms), n.value
+    _check(lib().mi355x_gated_attn_timing_read(ctx, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 class GatedAttnStep:
@@ -174,6 +185,7 @@ class GatedAttnStep:
                                                                    num_splits)
         self.workspace = torch.empty(self.workspace_bytes, dtype=torch.uint8,
                                      device=f"cuda:{device}")
+        mi355x_gated_attn_workspace_init(self.ctx, self.workspace)
 
     def q_bytes(self):
         """The q e4m3 codes a step left in the workspace, [B*L, Hq, D]."""

@@ -1,6 +1,6 @@
 // api.cpp -- the C ABI declared in include/mi355x_gated_attn.h: validation,
-// the split-KV plan, workspace layout, the three launches of a step and the
-// optional per-kernel timing hook.
+// the split-KV plan, the workspace layout, the launch of a step and the
+// optional timing hook.
 //
 // The plan replaces the page's FA3 scheduler metadata and its H200 split
 // heuristic max(1, min(16, cdiv(132, B*Hkv))) ("012-attention-local-splits.py",
@@ -43,7 +43,9 @@ int ok() {
 }
 
 constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs x 32 CUs
-constexpr int kTargetUnitsPerCu = 2;
+// Work units resident per compute unit: the q_len 1-2 kernels fit two 4-wave
+// workgroups per CU (<= 256 registers per lane), longer blocks one.
+int units_per_cu(int q_len) { return q_len <= 2 ? 2 : 1; }
 constexpr int kMaxSplits = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -56,11 +58,33 @@ struct mi355x_gated_attn_ctx {
   float inv_freq[kHeadDim / 2];
   bool planned = false;
   int32_t splits = 0;
-  size_t q_bytes = 0, po_off = 0, pml_off = 0, ws_bytes = 0;
+  size_t q_bytes = 0, po_off = 0, pml_off = 0, cnt_off = 0, ws_bytes = 0;
   bool timing = false;
-  std::vector<hipEvent_t> events;  // 4 per timed step, reused
+  std::vector<hipEvent_t> events;  // 2 per timed step, reused
   size_t events_used = 0;
 };
+
+namespace {
+
+int check_workspace(const mi355x_gated_attn_ctx* ctx, const void* workspace, size_t bytes) {
+  if (!workspace) return fail(MI355X_GA_INVALID_ARGUMENT, "workspace is NULL");
+  if (bytes < ctx->ws_bytes)
+    return fail(MI355X_GA_WORKSPACE_TOO_SMALL, "workspace %zu bytes < planned %zu", bytes,
+                ctx->ws_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
+  return MI355X_GA_OK;
+}
+
+int check_device(const mi355x_gated_attn_ctx* ctx) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "current device %d is not the ctx device %d", cur,
+                ctx->device);
+  return MI355X_GA_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -94,6 +118,8 @@ int mi355x_gated_attn_supports(const mi355x_gated_attn_config* c) {
     return fail(MI355X_GA_UNSUPPORTED, "q_len %d: this build serves 1..%d", c->q_len, kMaxQLen);
   if ((int64_t)c->max_pages * c->page_size > (int64_t)1 << 30)
     return fail(MI355X_GA_UNSUPPORTED, "max_pages * page_size exceeds 2^30 keys per request");
+  if (c->num_pages * (int64_t)c->page_size >= (int64_t)1 << 31)
+    return fail(MI355X_GA_UNSUPPORTED, "num_pages * page_size exceeds 2^31 - 1 cache rows");
   return ok();
 }
 
@@ -135,7 +161,7 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (s == 0) {
     const int64_t min_keys_per_split = (int64_t)kAttnWaves * kKeyBlock;  // a block per wave
     const int64_t by_len = std::max<int64_t>(1, (keys + min_keys_per_split - 1) / min_keys_per_split);
-    const int64_t target = (int64_t)kComputeUnits * kTargetUnitsPerCu;
+    const int64_t target = (int64_t)kComputeUnits * units_per_cu(c.q_len);
     const int64_t by_batch = c.batch > 0 ? (target + c.batch - 1) / c.batch : 1;
     s = (int32_t)std::max<int64_t>(1, std::min<int64_t>({by_len, by_batch, (int64_t)kMaxSplits}));
   }
@@ -144,12 +170,28 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   ctx->q_bytes = T * kQHeads * kHeadDim;
   ctx->po_off = align_up(ctx->q_bytes, 256);
   ctx->pml_off = align_up(ctx->po_off + (size_t)s * rows * kHeadDim * sizeof(float), 256);
-  ctx->ws_bytes = align_up(ctx->pml_off + (size_t)s * rows * 2 * sizeof(float), 256);
+  ctx->cnt_off = align_up(ctx->pml_off + (size_t)s * rows * 2 * sizeof(float), 256);
+  ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)c.batch * sizeof(int32_t), 256);
   if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
   ctx->splits = s;
   ctx->planned = true;
   if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
   if (num_splits_out) *num_splits_out = s;
+  return ok();
+}
+
+int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "workspace_init before plan");
+  if (ctx->cfg.batch == 0) return ok();
+  int rc = check_workspace(ctx, workspace, workspace_bytes);
+  if (rc) return rc;
+  rc = check_device(ctx);
+  if (rc) return rc;
+  int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) + ctx->cnt_off);
+  hipError_t e = launch_zero_counters(counters, ctx->cfg.batch, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 
@@ -171,88 +213,61 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   if (rope && !positions) return fail(MI355X_GA_INVALID_ARGUMENT, "positions is NULL with RoPE on");
   if (scaled && (!k_scale || !v_scale))
     return fail(MI355X_GA_INVALID_ARGUMENT, "k_scale/v_scale are NULL on the scaled path");
-  if (workspace_bytes < ctx->ws_bytes)
-    return fail(MI355X_GA_WORKSPACE_TOO_SMALL, "workspace %zu bytes < planned %zu", workspace_bytes,
-                ctx->ws_bytes);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256)
-    return fail(MI355X_GA_INVALID_ARGUMENT, "workspace is not 256-byte aligned");
-  if (reinterpret_cast<uintptr_t>(qkv) % 8 || reinterpret_cast<uintptr_t>(k_cache) % 16 ||
-      reinterpret_cast<uintptr_t>(v_cache) % 16 || reinterpret_cast<uintptr_t>(out) % 4)
+  int rc = check_workspace(ctx, workspace, workspace_bytes);
+  if (rc) return rc;
+  if (reinterpret_cast<uintptr_t>(qkv) % 16 || reinterpret_cast<uintptr_t>(k_cache) % 16 ||
+      reinterpret_cast<uintptr_t>(v_cache) % 16 || reinterpret_cast<uintptr_t>(out) % 8)
     return fail(MI355X_GA_INVALID_ARGUMENT, "qkv/cache/out pointers are misaligned");
-  int cur = -1;
-  if (hipGetDevice(&cur) != hipSuccess || cur != ctx->device)
-    return fail(MI355X_GA_INVALID_ARGUMENT, "current device %d is not the ctx device %d", cur,
-                ctx->device);
+  rc = check_device(ctx);
+  if (rc) return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  const int T = c.batch * c.q_len;
 
-  PrologueParams pp{};
-  pp.qkv = reinterpret_cast<const uint16_t*>(qkv);
-  pp.positions = positions;
-  pp.cache_loc = cache_loc;
-  pp.k_cache = reinterpret_cast<uint8_t*>(k_cache);
-  pp.v_cache = reinterpret_cast<uint8_t*>(v_cache);
-  pp.k_scale = k_scale;
-  pp.v_scale = v_scale;
-  pp.q_out = ws;
-  pp.num_rows = c.num_pages * (int64_t)c.page_size;
-  pp.tokens = T;
-  pp.rope = rope ? 1 : 0;
-  pp.scaled = scaled ? 1 : 0;
-  std::memcpy(pp.inv_freq, ctx->inv_freq, sizeof pp.inv_freq);
-
-  AttnParams ap{};
-  ap.q = ws;
-  ap.k_cache = pp.k_cache;
-  ap.v_cache = pp.v_cache;
-  ap.page_table = page_table;
-  ap.cache_seqlens = cache_seqlens;
-  ap.k_scale = k_scale;
-  ap.part_o = reinterpret_cast<float*>(ws + ctx->po_off);
-  ap.part_ml = reinterpret_cast<float*>(ws + ctx->pml_off);
-  ap.num_pages = c.num_pages;
-  ap.batch = c.batch;
-  ap.splits = ctx->splits;
-  ap.max_pages = c.max_pages;
-  ap.page_size = c.page_size;
-  ap.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;
-  ap.window = c.window;
-  ap.scaled = pp.scaled;
-  ap.sm_scale_log2 = c.sm_scale * 1.4426950408889634f;
-
-  CombineParams cp{};
-  cp.part_o = ap.part_o;
-  cp.part_ml = ap.part_ml;
-  cp.qkv = pp.qkv;
-  cp.v_scale = v_scale;
-  cp.out = reinterpret_cast<uint16_t*>(out);
-  cp.tokens = T;
-  cp.q_len = c.q_len;
-  cp.splits = ctx->splits;
-  cp.scaled = pp.scaled;
+  StepParams sp{};
+  sp.qkv = reinterpret_cast<const uint16_t*>(qkv);
+  sp.positions = positions;
+  sp.cache_loc = cache_loc;
+  sp.cache_seqlens = cache_seqlens;
+  sp.page_table = page_table;
+  sp.k_cache = reinterpret_cast<uint8_t*>(k_cache);
+  sp.v_cache = reinterpret_cast<uint8_t*>(v_cache);
+  sp.k_scale = k_scale;
+  sp.v_scale = v_scale;
+  sp.out = reinterpret_cast<uint16_t*>(out);
+  sp.q_out = ws;
+  sp.part_o = reinterpret_cast<float*>(ws + ctx->po_off);
+  sp.part_ml = reinterpret_cast<float*>(ws + ctx->pml_off);
+  sp.counters = reinterpret_cast<int32_t*>(ws + ctx->cnt_off);
+  sp.num_pages = c.num_pages;
+  sp.num_rows = c.num_pages * (int64_t)c.page_size;
+  sp.batch = c.batch;
+  sp.splits = ctx->splits;
+  sp.max_pages = c.max_pages;
+  sp.page_size = c.page_size;
+  sp.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;
+  sp.window = c.window;
+  sp.scaled = scaled ? 1 : 0;
+  sp.rope = rope ? 1 : 0;
+  sp.sm_scale_log2 = c.sm_scale * 1.4426950408889634f;
+  std::memcpy(sp.inv_freq, ctx->inv_freq, sizeof sp.inv_freq);
 
   hipEvent_t* ev = nullptr;
   if (ctx->timing) {
-    if (ctx->events_used + 4 > ctx->events.size()) {
-      for (int k = 0; k < 4; ++k) {
+    if (ctx->events_used + 2 > ctx->events.size()) {
+      for (int k = 0; k < 2; ++k) {
         hipEvent_t e;
         if (hipEventCreate(&e) != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "hipEventCreate failed");
         ctx->events.push_back(e);
       }
     }
     ev = &ctx->events[ctx->events_used];
-    ctx->events_used += 4;
+    ctx->events_used += 2;
   }
   hipError_t e = hipSuccess;
   if (ev) e = hipEventRecord(ev[0], st);
-  if (e == hipSuccess) e = launch_prologue(pp, st);
+  if (e == hipSuccess) e = launch_step(sp, c.q_len, st);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
-  if (e == hipSuccess) e = launch_attention(ap, c.q_len, st);
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[2], st);
-  if (e == hipSuccess) e = launch_combine(cp, st);
-  if (e == hipSuccess && ev) e = hipEventRecord(ev[3], st);
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -272,21 +287,19 @@ int mi355x_gated_attn_timing(mi355x_gated_attn_ctx* ctx, int enable) {
 
 int mi355x_gated_attn_timing_read(mi355x_gated_attn_ctx* ctx, double* kernel_ms, int64_t* steps) {
   if (!ctx || !kernel_ms) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx or kernel_ms is NULL");
-  double acc[3] = {0, 0, 0};
-  const size_t n = ctx->events_used / 4;
+  double acc = 0.0;
+  const size_t n = ctx->events_used / 2;
   if (n) {
     if (hipEventSynchronize(ctx->events[ctx->events_used - 1]) != hipSuccess)
       return fail(MI355X_GA_HIP_ERROR, "hipEventSynchronize failed");
   }
   for (size_t i = 0; i < n; ++i) {
-    for (int k = 0; k < 3; ++k) {
-      float ms = 0.0f;
-      if (hipEventElapsedTime(&ms, ctx->events[4 * i + k], ctx->events[4 * i + k + 1]) != hipSuccess)
-        return fail(MI355X_GA_HIP_ERROR, "hipEventElapsedTime failed");
-      acc[k] += ms;
-    }
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, ctx->events[2 * i], ctx->events[2 * i + 1]) != hipSuccess)
+      return fail(MI355X_GA_HIP_ERROR, "hipEventElapsedTime failed");
+    acc += ms;
   }
-  for (int k = 0; k < 3; ++k) kernel_ms[k] = acc[k];
+  *kernel_ms = acc;
   if (steps) *steps = (int64_t)n;
   ctx->events_used = 0;
   return ok();

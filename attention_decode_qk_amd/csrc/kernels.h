@@ -1,5 +1,5 @@
-// kernels.h -- internal interface between the C-ABI host code and the three
-// gfx950 kernels of the gated-attention step.  Not installed, not part of the ABI.
+// kernels.h -- internal interface between the C-ABI host code and the gfx950
+// kernel of the gated-attention step.  Not installed, not part of the ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,61 +18,41 @@ constexpr int kMaxQLen = 8;
 constexpr int kWidth = (2 * kQHeads + 2 * kKvHeads) * kHeadDim;  // 2304 projection columns
 constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
 
-// Split attention work unit: a workgroup of kAttnWaves waves walks one
-// request's key chunk in blocks of kKeyBlock keys (one block per wave at a time).
+// Work unit = (request, split): a workgroup of kAttnWaves waves walks the
+// split's key chunk in blocks of kKeyBlock keys, one block per wave at a time.
 constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
 
-struct PrologueParams {
-  const uint16_t* qkv;       // bf16 [T, kWidth]
-  const int64_t* positions;  // [T]
-  const int64_t* cache_loc;  // [T]
-  uint8_t* k_cache;          // e4m3 [rows, kKvHeads, kHeadDim]
-  uint8_t* v_cache;
-  const float* k_scale;      // device scalars, read iff scaled
-  const float* v_scale;
-  uint8_t* q_out;            // e4m3 [T, kQHeads, kHeadDim]
-  int64_t num_rows;          // pool rows (bounds for cache_loc)
-  int32_t tokens;            // T = B * L
-  int32_t rope;              // 1 iff rope_theta != 0
-  int32_t scaled;            // 1 iff kv_scale != 1
-  float inv_freq[kHeadDim / 2];
-};
-
-struct AttnParams {
-  const uint8_t* q;              // e4m3 [T, kQHeads, kHeadDim]
-  const uint8_t* k_cache;        // e4m3 [rows, kKvHeads, kHeadDim]
-  const uint8_t* v_cache;
-  const int32_t* page_table;     // [B, max_pages]
+struct StepParams {
+  const uint16_t* qkv;           // bf16 [T, kWidth]
+  const int64_t* positions;      // [T] (read iff rope)
+  const int64_t* cache_loc;      // [T]
   const int32_t* cache_seqlens;  // [B]
-  const float* k_scale;          // read iff scaled
+  const int32_t* page_table;     // [B, max_pages]
+  uint8_t* k_cache;              // e4m3 [rows, kKvHeads, kHeadDim]
+  uint8_t* v_cache;
+  const float* k_scale;          // device scalars, read iff scaled
+  const float* v_scale;
+  uint16_t* out;                 // bf16 [T, kQHeads * kHeadDim]
+  uint8_t* q_out;                // e4m3 [T, kQHeads, kHeadDim] (workspace)
   float* part_o;                 // fp32 [B, S, L*kQHeads, kHeadDim]
   float* part_ml;                // fp32 [B, S, L*kQHeads, 2]: running max (log2 units), sum
+  int32_t* counters;             // [B] finished units per request, 0 between steps
   int64_t num_pages;
+  int64_t num_rows;              // num_pages * page_size (< 2^31)
   int32_t batch;
   int32_t splits;                // S
   int32_t max_pages;
   int32_t page_size;
   int32_t page_shift;            // log2(page_size) if a power of two, else -1
   int32_t window;
-  int32_t scaled;
+  int32_t scaled;                // 1 iff kv_scale != 1
+  int32_t rope;                  // 1 iff rope_theta != 0
   float sm_scale_log2;           // sm_scale * log2(e)
+  float inv_freq[kHeadDim / 2];
 };
 
-struct CombineParams {
-  const float* part_o;
-  const float* part_ml;
-  const uint16_t* qkv;       // gate logits live in the projection row
-  const float* v_scale;      // read iff scaled
-  uint16_t* out;             // bf16 [T, kQHeads * kHeadDim]
-  int32_t tokens;
-  int32_t q_len;
-  int32_t splits;
-  int32_t scaled;
-};
-
-hipError_t launch_prologue(const PrologueParams& p, hipStream_t stream);
-hipError_t launch_attention(const AttnParams& p, int q_len, hipStream_t stream);
-hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_step(const StepParams& p, int q_len, hipStream_t stream);
+hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t stream);
 
 }  // namespace mi355x_ga

@@ -2,8 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload swa_decode]
 
-A "step" is one layer-step of the whole hot path (prologue, split attention,
-combine + gated epilogue) over one batch of synthetic inputs.  The default
+A "step" is one layer-step of the whole hot path (norm, RoPE, e4m3 store,
+split attention, combine + gated epilogue: one fused kernel) over one batch of
+synthetic inputs.  The default
 workload is the decode batch the headline metric is quoted on: B=32, L=1,
 16 query / 2 KV heads, head_dim 64, page_size 1, window 2048, RoPE theta
 5e5, cached lengths uniform in [4096, 16384], shuffled page table.
@@ -13,9 +14,9 @@ Cold-cache discipline: the steps round-robin over enough per-layer KV pools
 four times the 256 MB Infinity Cache, as a model's layers would.  Each layer's
 step is captured once in a HIP graph (outside the timed region) and the timed
 region replays exactly K of them, bracketed by synchronisation and HIP events
-on the replay stream.  A second, eager pass with the library's per-kernel
-event hook measures each kernel's average duration (the GPU is pre-loaded with
-a spin kernel so the host enqueues ahead and the kernels run back to back).
+on the replay stream.  A second, eager pass with the library's event hook
+measures the step kernel's average duration (the GPU is pre-loaded with a spin
+kernel so the host enqueues ahead and the kernels run back to back).
 
 Prints one JSON line (see the design doc for every field).
 """
@@ -34,9 +35,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "attention_swa_decode_counters.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fused_step_swa_decode_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_decode_qk_amd", "csrc", f)
-                  for f in ("attention.hip", "kernels.h")]
+                  for f in ("step_kernel.hip", "kernels.h", "numerics.h")]
 
 
 def kernel_source_hash() -> str:
@@ -62,8 +63,10 @@ def attended_keys(w, cache_seqlens) -> int:
 
 
 def algorithmic_bytes(w, x):
-    """Per step: KV bytes (the metric's numerator), and the attention kernel's
-    algorithmic bytes (KV rows + page-table entries of the attended keys + q)."""
+    """Per step: KV bytes (the metric's numerator), and the step kernel's
+    algorithmic bytes: KV rows and page-table entries of the attended keys, plus
+    per token the projection row, its two K/V row stores, its output row and its
+    position and cache row."""
     keys = attended_keys(w, x.cache_seqlens)
     kv = keys * w.num_kv_heads * w.head_dim * 2
     pages = 0
@@ -71,8 +74,9 @@ def algorithmic_bytes(w, x):
         first = cs - w.q_len - (w.window - 1 if w.window > 0 else cs)
         first = max(first, 0)
         pages += (cs - 1) // w.page_size - first // w.page_size + 1
-    q = x.tokens * w.num_q_heads * w.head_dim
-    return kv, kv + 4 * pages + q
+    per_token = (w.width * 2 + 2 * w.num_kv_heads * w.head_dim
+                 + w.num_q_heads * w.head_dim * 2 + 16)
+    return kv, kv + 4 * pages + x.tokens * per_token
 
 
 def load_traffic():
@@ -160,7 +164,7 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     x0 = synth.make_inputs(w)
-    kv_bytes, attn_bytes = algorithmic_bytes(w, x0)
+    kv_bytes, step_bytes = algorithmic_bytes(w, x0)
     pool_bytes = x0.k_cache.nbytes + x0.v_cache.nbytes + x0.page_table.nbytes
     n_layers = max(1, int(np.ceil(args.cold_bytes * (1 << 30) / pool_bytes)))
     print(f"[bench] {w.name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}; "
@@ -250,8 +254,8 @@ def main():
     us_step = 1000.0 * ms_total / args.steps
     us_warm = 1000.0 * ms_warm / args.steps
 
-    # Per-kernel durations: eager steps with the event hook, host enqueueing
-    # ahead of a spinning GPU so the three kernels run back to back.
+    # Kernel duration: eager steps with the event hook, host enqueueing ahead of
+    # a spinning GPU so the kernels run back to back.
     n_k = min(args.steps, 200)
     torch.cuda.synchronize()
     ga.mi355x_gated_attn_timing(step.ctx, True)
@@ -261,10 +265,9 @@ def main():
     kernel_ms, n_timed = ga.mi355x_gated_attn_timing_read(step.ctx)
     ga.mi355x_gated_attn_timing(step.ctx, False)
     torch.cuda.synchronize()
-    k_us = [1000.0 * v / max(1, n_timed) for v in kernel_ms]
-    attn_us = k_us[1]
+    kernel_us = 1000.0 * kernel_ms / max(1, n_timed)
 
-    achieved = attn_bytes / (attn_us * 1e-6) / 1e9
+    achieved = step_bytes / (kernel_us * 1e-6) / 1e9
     traffic = load_traffic()
     result = {
         "metric": METRIC,
@@ -288,15 +291,14 @@ def main():
         "us_per_layer_step": round(us_step, 3),
         "kv_bytes_per_step": kv_bytes,
         "kv_gbs_pct_of_peak": round(100.0 * kv_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
-        "kernel_us": {"prologue": round(k_us[0], 3), "attention": round(k_us[1], 3),
-                      "combine_epilogue": round(k_us[2], 3)},
-        "attention_kv_gbs": round(kv_bytes / (attn_us * 1e-6) / 1e9, 1),
+        "kernel_us": round(kernel_us, 3),
+        "kernel_kv_gbs": round(kv_bytes / (kernel_us * 1e-6) / 1e9, 1),
         "warm_single_pool": {"us_per_layer_step": round(us_warm, 3),
                              "kv_gbs": round(kv_bytes / (us_warm * 1e-6) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": attn_bytes,
-                     "kernel": "attn_split_kernel<1>", "kernel_source": kernel_source_hash()},
+                     "traffic": traffic, "algorithmic_bytes": step_bytes,
+                     "kernel": f"fused_step_kernel<{w.q_len}>", "kernel_source": kernel_source_hash()},
         "timed_wall_s": round(wall_s, 3),
     }
     if not args.no_cpu_baseline:

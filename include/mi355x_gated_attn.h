@@ -101,12 +101,22 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
                            size_t* workspace_bytes, int32_t* num_splits_out);
 
 /*
+ * Zero the cross-workgroup counters of a freshly allocated workspace.  Call
+ * once per workspace (per ctx plan) before its first step; every completed step
+ * leaves the workspace ready for the next one.  Asynchronous on `stream`; a
+ * kernel launch, never a memset, so it may also be captured in a HIP graph.
+ */
+int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/*
  * One layer-step, asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream); the calling thread's current device must be the ctx's device.
  * No host synchronisation, allocation or device-value read: capturable.
+ * The whole step is one kernel launch.
  *
  *   qkv            bf16 [B, L, (2Hq + 2Hkv) * D], rows contiguous: q heads |
- *                  k heads | v heads | gate logits (Hq*D)
+ *                  k heads | v heads | gate logits (Hq*D); 16-byte aligned
  *   positions      int64 [B*L]  RoPE position of each new token (read iff
  *                  rope_theta != 0; must be < 2^21 as on the page)
  *   cache_loc      int64 [B*L]  flat cache row of each new token; rows outside
@@ -114,18 +124,23 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
  *   cache_seqlens  int32 [B]    keys per request including the L new tokens;
  *                  query i of request b sits at p = cache_seqlens[b] - L + i
  *   page_table     int32 [B, max_pages]  physical page of each logical page,
- *                  -1 where unused (never read beyond a request's keys)
+ *                  -1 where unused (never read beyond a request's keys).  The
+ *                  rows it gives for the new tokens' positions must be their
+ *                  cache_loc rows (as when both come from one allocator): the
+ *                  step attends to the new keys and values it computes, and
+ *                  stores them at cache_loc
  *   seq_lens       int32 [B]    cached tokens per request; accepted for parity
  *                  with the page's inputs and not read (the page's attention
  *                  call takes cache_seqlens); may be NULL
  *   k_cache, v_cache  float8 e4m3 (OCP) [num_pages, P, Hkv, D], written in
- *                  place at the cache_loc rows only
+ *                  place at the cache_loc rows only; 16-byte aligned
  *   k_scale, v_scale  device float32 scalars (read iff kv_scale != 1; may be
  *                  NULL otherwise)
- *   out            bf16 [B, L, Hq * D]
+ *   out            bf16 [B, L, Hq * D]; 8-byte aligned
  *   workspace      device memory of at least the planned size, 256-byte
- *                  aligned.  Layout after a step: bytes [0, B*L*Hq*D) hold q
- *                  as e4m3 [B*L, Hq, D]; the rest holds split partials.
+ *                  aligned, initialised once by mi355x_gated_attn_workspace_init.
+ *                  Layout after a step: bytes [0, B*L*Hq*D) hold q as e4m3
+ *                  [B*L, Hq, D]; then split partials and B int32 counters.
  * Calls that share a workspace, or write the same cache rows, must be ordered
  * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
  */
@@ -143,16 +158,15 @@ const char* mi355x_gated_attn_last_error(void);
 
 /*
  * Measurement hook (not part of the page's interface): while enabled, each
- * step records HIP events on its stream around each of its three kernels
- * (prologue, split attention, combine + gated epilogue).  `enable` != 0
- * starts a fresh accumulation, 0 stops recording.  Not for use under graph
- * capture.
+ * step records a HIP event pair on its stream around its kernel.  `enable`
+ * != 0 starts a fresh accumulation, 0 stops recording.  Not for use under
+ * graph capture.
  */
 int mi355x_gated_attn_timing(mi355x_gated_attn_ctx* ctx, int enable);
 
 /*
- * Wait for the recorded events and return the summed per-kernel durations in
- * milliseconds (kernel_ms[3]) and the number of timed steps; then clear the
+ * Wait for the recorded events and return the summed kernel duration in
+ * milliseconds (*kernel_ms) and the number of timed steps; then clear the
  * accumulation.
  */
 int mi355x_gated_attn_timing_read(mi355x_gated_attn_ctx* ctx, double* kernel_ms,
