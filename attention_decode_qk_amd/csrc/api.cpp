@@ -43,9 +43,11 @@ int ok() {
 }
 
 constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs x 32 CUs
-// Work units resident per compute unit: the q_len 1-2 kernels fit two 4-wave
-// workgroups per CU (<= 256 registers per lane), longer blocks one.
-int units_per_cu(int q_len) { return q_len <= 2 ? 2 : 1; }
+// Work units per compute unit the automatic plan aims for.  Measured on the
+// B=32, L=1, window-2048 decode (units of 4 waves each): one unit per CU (S=8)
+// 19.9 us per step, two (S=16) 25.0 us -- fewer, longer units shorten the
+// merge of the partials more than they lengthen each unit's key walk.
+int units_per_cu(int q_len) { (void)q_len; return 1; }
 constexpr int kMaxSplits = 256;
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -145,15 +145,14 @@ __device__ inline uint2 pack_e4m3x8(const float (&y)[8]) {
 template <int L>
 __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   constexpr int NRB = (L * kGroup + 15) / 16;  // 16-row blocks per KV head
-  constexpr int kLdsRows = kKvHeads * NRB * 16;
   constexpr int kItems = L * kHeadRows * 8;    // (token, head row, 8-column slice)
   constexpr int kItemIters = (kItems + 255) / 256;
   __shared__ __align__(16) uint8_t s_q[L][kQHeads][kHeadDim];
   __shared__ __align__(16) uint8_t s_newk[L][kRowBytes];
   __shared__ __align__(16) uint8_t s_newv[L][kRowBytes];
   __shared__ float s_cs[L][kHeadDim / 2][2];
-  __shared__ __align__(16) float s_mo[2][kLdsRows][kHeadDim];
-  __shared__ float s_ml[2][kLdsRows][2];
+  __shared__ __align__(16) float s_mo[kAttnWaves][L * kQHeads][kHeadDim];
+  __shared__ __align__(16) float s_ml[kAttnWaves][L * kQHeads][2];
   __shared__ int s_last;
 
   const int b = blockIdx.x / p.splits;
@@ -450,71 +449,53 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
     }
 
   // ---------------- C. merge the waves, publish the partial ----------------
-  auto put = [&](int slot) {
+  // Every wave parks (m, l, o) of its valid rows in its LDS slot (compact row
+  // i*16 + h); after one barrier all 256 threads merge 4 columns of a row each
+  // and publish the unit's partial.
 #pragma unroll
-    for (int g = 0; g < kKvHeads; ++g)
+  for (int g = 0; g < kKvHeads; ++g)
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int row = (g * NRB + rb) * 16 + j;
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int r = 16 * rb + j;
+      const int i = r >> 3;
+      if (i >= L) continue;
+      const int cr = i * kQHeads + g * kGroup + (r & 7);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-          *reinterpret_cast<float4*>(&s_mo[slot][row][16 * q4 + 4 * ii]) =
-              make_float4(acc[g][rb][0][ii], acc[g][rb][1][ii], acc[g][rb][2][ii], acc[g][rb][3][ii]);
-        if (q4 == 0) {
-          s_ml[slot][row][0] = mrow[g][rb];
-          s_ml[slot][row][1] = lrow[g][rb];
-        }
-      }
-  };
-  auto take = [&](int slot) {
+      for (int ii = 0; ii < 4; ++ii)
+        *reinterpret_cast<float4*>(&s_mo[wave][cr][16 * q4 + 4 * ii]) =
+            make_float4(acc[g][rb][0][ii], acc[g][rb][1][ii], acc[g][rb][2][ii], acc[g][rb][3][ii]);
+      if (q4 == 0) *reinterpret_cast<float2*>(&s_ml[wave][cr][0]) = make_float2(mrow[g][rb], lrow[g][rb]);
+    }
+  lds_barrier();
+  const int64_t prow0 = (int64_t)(b * p.splits + s) * (L * kQHeads);
+  for (int idx = tid; idx < L * kQHeads * 16; idx += 256) {
+    const int cr = idx >> 4, c4 = (idx & 15) * 4;
+    float mw[kAttnWaves], lw[kAttnWaves];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int g = 0; g < kKvHeads; ++g)
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float2 ml = *reinterpret_cast<const float2*>(&s_ml[w][cr][0]);
+      mw[w] = ml.x;
+      lw[w] = ml.y;
+      mx = fmaxf(mx, ml.x);
+    }
+    const float muse = mx == -INFINITY ? 0.0f : mx;
+    float lsum = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int row = (g * NRB + rb) * 16 + j;
-        const float mo = s_ml[slot][row][0];
-        const float lo = s_ml[slot][row][1];
-        const float mnew = fmaxf(mrow[g][rb], mo);
-        const float muse = mnew == -INFINITY ? 0.0f : mnew;
-        const float a = __builtin_amdgcn_exp2f(mrow[g][rb] - muse);
-        const float bo = __builtin_amdgcn_exp2f(mo - muse);
-        mrow[g][rb] = mnew;
-        lrow[g][rb] = lrow[g][rb] * a + lo * bo;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const float4 v = *reinterpret_cast<const float4*>(&s_mo[slot][row][16 * q4 + 4 * ii]);
-          acc[g][rb][0][ii] = acc[g][rb][0][ii] * a + v.x * bo;
-          acc[g][rb][1][ii] = acc[g][rb][1][ii] * a + v.y * bo;
-          acc[g][rb][2][ii] = acc[g][rb][2][ii] * a + v.z * bo;
-          acc[g][rb][3][ii] = acc[g][rb][3][ii] * a + v.w * bo;
-        }
-      }
-  };
-  if (wave >= 2) put(wave - 2);
-  __syncthreads();
-  if (wave < 2) take(wave);
-  __syncthreads();
-  if (wave == 1) put(0);
-  __syncthreads();
-  if (wave == 0) {
-    take(0);
-#pragma unroll
-    for (int g = 0; g < kKvHeads; ++g)
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const int r = 16 * rb + j;
-        const int i = r >> 3;
-        if (i >= L) continue;
-        const int h = g * kGroup + (r & 7);
-        const int64_t prow = ((int64_t)(b * p.splits + s) * L + i) * kQHeads + h;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          float* dst = p.part_o + prow * kHeadDim + 16 * q4 + 4 * ii;
-          store_coherent(dst, acc[g][rb][0][ii], acc[g][rb][1][ii]);
-          store_coherent(dst + 2, acc[g][rb][2][ii], acc[g][rb][3][ii]);
-        }
-        if (q4 == 0) store_coherent(p.part_ml + prow * 2, mrow[g][rb], lrow[g][rb]);
-      }
+    for (int w = 0; w < kAttnWaves; ++w) {
+      const float a = __builtin_amdgcn_exp2f(mw[w] - muse);
+      const float4 v = *reinterpret_cast<const float4*>(&s_mo[w][cr][c4]);
+      lsum += a * lw[w];
+      o.x += a * v.x;
+      o.y += a * v.y;
+      o.z += a * v.z;
+      o.w += a * v.w;
+    }
+    float* dst = p.part_o + (prow0 + cr) * kHeadDim + c4;
+    store_coherent(dst, o.x, o.y);
+    store_coherent(dst + 2, o.z, o.w);
+    if (c4 == 0) store_coherent(p.part_ml + (prow0 + cr) * 2, mx, lsum);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
   __syncthreads();
