@@ -375,12 +375,16 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       }
     }
 
+    // Per KV head: the scores of all its row blocks first (their MFMAs overlap),
+    // then one wave-uniform running-max decision, then P and PV.
     const bool full = kbase >= lo_all && kbase + kKeyBlock - 1 <= hi_all;
 #pragma unroll
     for (int g = 0; g < kKvHeads; ++g) {
+      float sv[NRB][8];
+      float lmx[NRB];     // this lane's maximum over its 8 keys
+      bool grow = false;  // some lane's maximum passes its row's lazy bound
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        float sv[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           v4f z = {0.f, 0.f, 0.f, 0.f};
@@ -389,36 +393,47 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
           z = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(d.k[t][g].z, d.k[t][g].w),
                                                           qop[g][rb][1], z, 0, 0, 0);
 #pragma unroll
-          for (int ii = 0; ii < 4; ++ii) sv[t * 4 + ii] = z[ii] * scale;
+          for (int ii = 0; ii < 4; ++ii) sv[rb][t * 4 + ii] = z[ii] * scale;
         }
         if (!full) {
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
             const bool vis = key < end && key >= rlo[rb] && key <= rhi[rb];
-            sv[k] = vis ? sv[k] : -INFINITY;
+            sv[rb][k] = vis ? sv[rb][k] : -INFINITY;
           }
         }
-        float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mold = mrow[g][rb];
-        const bool move = mx > mold + kLazyRescale;
-        const float mnew = move ? mx : mold;
-        const float muse = mnew == -INFINITY ? 0.0f : mnew;
-        if (__any(move)) {
-          const float alpha = __builtin_amdgcn_exp2f(mold - muse);
-          lrow[g][rb] *= alpha;
+        const float* v = sv[rb];
+        lmx[rb] = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
+                        fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+        grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
+      }
+      // A row's maximum moves only when its full maximum (over the four lane
+      // groups) passes the bound, which no lane's own maximum does in the common
+      // case: then nothing moves and the cross-lane reduction is skipped.
+      if (__any(grow)) {
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          float mx = lmx[rb];
+          mx = fmaxf(mx, __shfl_xor(mx, 16));
+          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mold = mrow[g][rb];
+          const float mnew = mx > mold + kLazyRescale ? mx : mold;
+          const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
+          lrow[g][rb] *= alpha;  // alpha is exactly 1 for a row that kept its maximum
 #pragma unroll
           for (int c = 0; c < 4; ++c) acc[g][rb][c] *= alpha;
+          mrow[g][rb] = mnew;
         }
-        mrow[g][rb] = mnew;
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const float muse = mrow[g][rb] == -INFINITY ? 0.0f : mrow[g][rb];
         v8h pb;
         float psum = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float pk = __builtin_amdgcn_exp2f(sv[k] - muse);
+          const float pk = __builtin_amdgcn_exp2f(sv[rb][k] - muse);
           psum += pk;
           pb[k] = (_Float16)pk;
         }
@@ -506,66 +521,86 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   if (!s_last) return;
 
   // ---------------- D. combine + gated epilogue (last unit) ----------------
-  // 16 lanes per (token, head) row, 4 columns each; 16 rows per pass.
+  // Thread (h, c4) takes columns c4..c4+3 of head h for every token of the
+  // request.  The partials are read KS splits at a time for all tokens at once,
+  // so the chain of device-coherent round trips is ceil(splits / KS) long
+  // whatever the number of tokens.
+  constexpr int KS = L >= 8 ? 4 : (32 / L > 16 ? 16 : 32 / L);
   const int c4 = (tid & 15) * 4;
   const int h = tid >> 4;
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
-  for (int i = 0; i < L; ++i) {
-    const int64_t t = tok0 + i;
-    const uint2 graw = *reinterpret_cast<const uint2*>(p.qkv + t * kWidth + kGateOffset + h * kHeadDim + c4);
-    const int64_t base = (int64_t)b * p.splits * stride + (int64_t)i * kQHeads + h;
-    float mrun = -INFINITY, lrun = 0.0f;
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < p.splits; s0 += 16) {
-      float2 ml[16], o01[16], o23[16];
+  const int64_t base = (int64_t)b * p.splits * stride + h;
+  uint2 graw[L];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        ml[k] = make_float2(-INFINITY, 0.0f);
-        o01[k] = o23[k] = make_float2(0.0f, 0.0f);
+  for (int i = 0; i < L; ++i)
+    graw[i] = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + i) * kWidth + kGateOffset + h * kHeadDim + c4);
+  float mrun[L], lrun[L], o[L][4];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    mrun[i] = -INFINITY;
+    lrun[i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[i][c] = 0.0f;
+  }
+  for (int s0 = 0; s0 < p.splits; s0 += KS) {
+    float2 ml[L][KS], o01[L][KS], o23[L][KS];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) {
+        ml[i][k] = make_float2(-INFINITY, 0.0f);
+        o01[i][k] = o23[i][k] = make_float2(0.0f, 0.0f);
         if (s0 + k < p.splits) {
-          const int64_t pr = base + (int64_t)(s0 + k) * stride;
-          ml[k] = load_coherent(p.part_ml + pr * 2);
-          o01[k] = load_coherent(p.part_o + pr * kHeadDim + c4);
-          o23[k] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
+          const int64_t pr = base + (int64_t)(s0 + k) * stride + i * kQHeads;
+          ml[i][k] = load_coherent(p.part_ml + pr * 2);
+          o01[i][k] = load_coherent(p.part_o + pr * kHeadDim + c4);
+          o23[i][k] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
         }
       }
-      float mc = mrun;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) mc = fmaxf(mc, ml[k].x);
-      const float muse = mc == -INFINITY ? 0.0f : mc;
-      const float a = __builtin_amdgcn_exp2f(mrun - muse);
-      lrun *= a;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[c] *= a;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const float wk = __builtin_amdgcn_exp2f(ml[k].x - muse);
-        lrun += wk * ml[k].y;
-        o[0] += wk * o01[k].x;
-        o[1] += wk * o01[k].y;
-        o[2] += wk * o23[k].x;
-        o[3] += wk * o23[k].y;
-      }
-      mrun = mc;
     }
-    const float inv = lrun > 0.0f ? vs / lrun : 0.0f;
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      float mc = mrun[i];
+#pragma unroll
+      for (int k = 0; k < KS; ++k) mc = fmaxf(mc, ml[i][k].x);
+      const float muse = mc == -INFINITY ? 0.0f : mc;
+      const float a = __builtin_amdgcn_exp2f(mrun[i] - muse);
+      lrun[i] *= a;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[i][c] *= a;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const float wk = __builtin_amdgcn_exp2f(ml[i][k].x - muse);
+        lrun[i] += wk * ml[i][k].y;
+        o[i][0] += wk * o01[i][k].x;
+        o[i][1] += wk * o01[i][k].y;
+        o[i][2] += wk * o23[i][k].x;
+        o[i][3] += wk * o23[i][k].y;
+      }
+      mrun[i] = mc;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const float inv = lrun[i] > 0.0f ? vs / lrun[i] : 0.0f;
+    float y[4];
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      o[c] = round_bf16(o[c] * inv);  // the attention result is bf16 before the epilogue
-      ss += o[c] * o[c];
+      y[c] = round_bf16(o[i][c] * inv);  // the attention result is bf16 before the epilogue
+      ss += y[c] * y[c];
     }
     ss += __shfl_xor(ss, 1, 16);
     ss += __shfl_xor(ss, 2, 16);
     ss += __shfl_xor(ss, 4, 16);
     ss += __shfl_xor(ss, 8, 16);
     const float r = (float)(1.0 / sqrt((double)ss / 64.0 + 1.0e-5));
-    const float gate[4] = {bf16_value(graw.x & 0xffffu), bf16_value(graw.x >> 16),
-                           bf16_value(graw.y & 0xffffu), bf16_value(graw.y >> 16)};
+    const float gate[4] = {bf16_value(graw[i].x & 0xffffu), bf16_value(graw[i].x >> 16),
+                           bf16_value(graw[i].y & 0xffffu), bf16_value(graw[i].y >> 16)};
     uint32_t ob[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(o[c] * r * (1.0f / (1.0f + __expf(-gate[c]))));
-    *reinterpret_cast<uint2*>(p.out + t * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
+    for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * (1.0f / (1.0f + __expf(-gate[c]))));
+    *reinterpret_cast<uint2*>(p.out + (tok0 + i) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
         make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
   }
   if (tid == 0) __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

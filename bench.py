@@ -55,10 +55,7 @@ def attended_keys(w, cache_seqlens) -> int:
     total = 0
     for cs in cache_seqlens.tolist():
         last = cs - 1
-        first = cs - w.q_len
-        if w.window > 0:
-            first = first - w.window + 1
-        first = max(first, 0)
+        first = max(cs - w.q_len - w.window + 1, 0) if w.window > 0 else 0
         total += max(0, last - first + 1)
     return total
 

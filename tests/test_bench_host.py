@@ -1,0 +1,48 @@
+"""Host-side byte accounting of bench.py: the keys a step must read are the
+union of its queries' visible ranges (page "012-attention-local-splits.py",
+kernel_fn's flash_attn_with_kvcache call: causal, with window_size (W-1, 0)
+on sliding layers and no window on full layers), checked against a brute-force
+union over the queries."""
+import numpy as np
+import pytest
+
+import bench
+import synth
+
+
+def _brute_keys(w, cache_seqlens):
+    total = 0
+    for cs in cache_seqlens.tolist():
+        seen = set()
+        for i in range(w.q_len):
+            p = cs - w.q_len + i
+            lo = max(0, p - w.window + 1) if w.window > 0 else 0
+            seen.update(range(lo, p + 1))
+        total += len(seen)
+    return total
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3, q_len=1, window=0), dict(batch=3, q_len=1, window=16),
+    dict(batch=4, q_len=8, window=0, page_size=4), dict(batch=2, q_len=8, window=32, page_size=16),
+])
+def test_attended_keys_is_the_union_of_the_visible_ranges(kw):
+    w = synth.small(**kw)
+    x = synth.make_inputs(w)
+    assert bench.attended_keys(w, x.cache_seqlens) == _brute_keys(w, x.cache_seqlens)
+
+
+def test_full_attention_reads_every_cached_key():
+    w = synth.small(batch=5, q_len=2, window=0)
+    x = synth.make_inputs(w)
+    assert bench.attended_keys(w, x.cache_seqlens) == int(np.sum(x.cache_seqlens))
+
+
+def test_algorithmic_bytes_count_kv_rows_pages_and_token_rows():
+    w = synth.small(batch=2, q_len=1, window=0, page_size=4)
+    x = synth.make_inputs(w)
+    kv, total = bench.algorithmic_bytes(w, x)
+    assert kv == int(np.sum(x.cache_seqlens)) * w.num_kv_heads * w.head_dim * 2
+    pages = int(np.sum((x.cache_seqlens + w.page_size - 1) // w.page_size))
+    per_token = w.width * 2 + 2 * w.num_kv_heads * w.head_dim + w.num_q_heads * w.head_dim * 2 + 16
+    assert total == kv + 4 * pages + x.tokens * per_token
