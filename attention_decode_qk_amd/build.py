@@ -3,8 +3,11 @@
     python -m attention_decode_qk_amd.build [--force]
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instructions
-disabled (-Xclang -target-feature -Xclang -packed-fp32-ops), then linked into
-one shared library next to this file.
+disabled (-Xclang -target-feature -Xclang -packed-fp32-ops) and MFMA results
+kept in ordinary VGPRs (-mllvm -amdgpu-mfma-vgpr-form: the scores and
+accumulators are read and rescaled by vector ALU code, which otherwise pays a
+move out of the accumulation registers for every value), then linked into one
+shared library next to this file.
 """
 from __future__ import annotations
 
@@ -25,6 +28,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wall", "-Wno-unused-result"]
 
 

@@ -164,16 +164,19 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
     const int64_t min_keys_per_split = (int64_t)kAttnWaves * kKeyBlock;  // a block per wave
     const int64_t by_len = std::max<int64_t>(1, (keys + min_keys_per_split - 1) / min_keys_per_split);
     const int64_t target = (int64_t)kComputeUnits * units_per_cu(c.q_len);
-    const int64_t by_batch = c.batch > 0 ? (target + c.batch - 1) / c.batch : 1;
+    const int64_t groups = (int64_t)c.batch * token_groups(c.q_len);  // units per split
+    const int64_t by_batch = groups > 0 ? (target + groups - 1) / groups : 1;
     s = (int32_t)std::max<int64_t>(1, std::min<int64_t>({by_len, by_batch, (int64_t)kMaxSplits}));
   }
+  if ((int64_t)c.batch * token_groups(c.q_len) * s > (int64_t)INT32_MAX)
+    return fail(MI355X_GA_UNSUPPORTED, "batch %d x %d splits exceeds one launch's workgroups", c.batch, s);
   const size_t T = (size_t)c.batch * c.q_len;
   const size_t rows = T * kQHeads;  // (token, q head) rows
   ctx->q_bytes = T * kQHeads * kHeadDim;
   ctx->po_off = align_up(ctx->q_bytes, 256);
   ctx->pml_off = align_up(ctx->po_off + (size_t)s * rows * kHeadDim * sizeof(float), 256);
   ctx->cnt_off = align_up(ctx->pml_off + (size_t)s * rows * 2 * sizeof(float), 256);
-  ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)c.batch * sizeof(int32_t), 256);
+  ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)c.batch * token_groups(c.q_len) * sizeof(int32_t), 256);
   if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
   ctx->splits = s;
   ctx->planned = true;
@@ -192,7 +195,8 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
   rc = check_device(ctx);
   if (rc) return rc;
   int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) + ctx->cnt_off);
-  hipError_t e = launch_zero_counters(counters, ctx->cfg.batch, reinterpret_cast<hipStream_t>(stream));
+  hipError_t e = launch_zero_counters(counters, ctx->cfg.batch * token_groups(ctx->cfg.q_len),
+                                     reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -244,6 +248,8 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   sp.num_pages = c.num_pages;
   sp.num_rows = c.num_pages * (int64_t)c.page_size;
   sp.batch = c.batch;
+  sp.q_len = c.q_len;
+  sp.tgroups = token_groups(c.q_len);
   sp.splits = ctx->splits;
   sp.max_pages = c.max_pages;
   sp.page_size = c.page_size;
@@ -268,7 +274,7 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   }
   hipError_t e = hipSuccess;
   if (ev) e = hipEventRecord(ev[0], st);
-  if (e == hipSuccess) e = launch_step(sp, c.q_len, st);
+  if (e == hipSuccess) e = launch_step(sp, st);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -18,10 +18,14 @@ constexpr int kMaxQLen = 8;
 constexpr int kWidth = (2 * kQHeads + 2 * kKvHeads) * kHeadDim;  // 2304 projection columns
 constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
 
-// Work unit = (request, split): a workgroup of kAttnWaves waves walks the
-// split's key chunk in blocks of kKeyBlock keys, one block per wave at a time.
+// Work unit = (request, token group, split): a workgroup of kAttnWaves waves
+// walks the split's key chunk in blocks of kKeyBlock keys, one block per wave
+// at a time, for the query rows of the group's tokens.  A request's q_len
+// tokens form token_groups(q_len) groups of consecutive tokens.
 constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
+constexpr int kMaxTokensPerUnit = 4;
+inline int token_groups(int q_len) { return (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit; }
 
 struct StepParams {
   const uint16_t* qkv;           // bf16 [T, kWidth]
@@ -37,10 +41,12 @@ struct StepParams {
   uint8_t* q_out;                // e4m3 [T, kQHeads, kHeadDim] (workspace)
   float* part_o;                 // fp32 [B, S, L*kQHeads, kHeadDim]
   float* part_ml;                // fp32 [B, S, L*kQHeads, 2]: running max (log2 units), sum
-  int32_t* counters;             // [B] finished units per request, 0 between steps
+  int32_t* counters;             // [B, G] finished units per (request, token group), 0 between steps
   int64_t num_pages;
   int64_t num_rows;              // num_pages * page_size (< 2^31)
   int32_t batch;
+  int32_t q_len;                 // L
+  int32_t tgroups;               // G = token_groups(L), 1 or 2
   int32_t splits;                // S
   int32_t max_pages;
   int32_t page_size;
@@ -52,7 +58,7 @@ struct StepParams {
   float inv_freq[kHeadDim / 2];
 };
 
-hipError_t launch_step(const StepParams& p, int q_len, hipStream_t stream);
+hipError_t launch_step(const StepParams& p, hipStream_t stream);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t stream);
 
 }  // namespace mi355x_ga

@@ -5,17 +5,23 @@
 // frequencies), kernel_fn's flash_attn_with_kvcache call (paged causal window
 // attention over the e4m3 cache, split-KV) and its rms_norm_gate epilogue.
 //
-// One workgroup (4 waves) per work unit (request b, split s).  A unit covers all
-// 16 query heads of its request, i.e. both KV heads, so every 128-byte cache row
-// it fetches (one key, both heads) is used whole.
+// One workgroup (4 waves) per work unit (request b, token group tg, split s).  A
+// request's L new tokens form one group (L <= 4) or two groups of at most four
+// consecutive tokens; a unit covers all 16 query heads of its group's tokens,
+// i.e. both KV heads, so every 128-byte cache row it fetches (one key, both
+// heads) is used whole.  Two groups halve the rows a unit carries, and with them
+// the partials its group's combine reads, for the price of reading each key
+// chunk twice (workgroups are dealt to the 8 XCDs round-robin, so the two units
+// of a chunk share an XCD and its L2 when batch x splits is a multiple of 8).
 //
 //  A. Geometry and early loads: cache_seqlens[b] gives the request's key range
 //     and this unit's chunk; the projection rows, positions and the page-table
 //     entries of the first key blocks are requested, then the first two blocks'
-//     K/V rows.  While those are in flight the unit computes its request's q
-//     (norm, RoPE, e4m3) into LDS; the unit whose chunk holds a new token's key
-//     also computes that token's K/V codes, stores them at cache_loc and uses
-//     them in place of the cache row, so no unit reads a row being written.
+//     K/V rows.  While those are in flight the unit computes its group's q
+//     (norm, RoPE, e4m3) into LDS; the units whose chunk holds a new token's key
+//     also compute that token's K/V codes and use them in place of the cache
+//     row (the group-0 one stores them at cache_loc), so no unit reads a row
+//     being written.
 //  B. Key loop (waves take 32-key blocks round-robin, two blocks in flight):
 //     QK^T on v_mfma_f32_16x16x32_fp8_fp8 straight from the cache bytes; base-2
 //     softmax with a lazily moved running max (rescale only when the max grows
@@ -23,10 +29,10 @@
 //     v_mfma_f32_16x16x32_f16 with V transposed in registers and widened
 //     exactly to f16.
 //  C. The four waves merge through LDS and publish the unit's partial (o, m, l)
-//     with device-coherent stores; an atomic counter per request elects the last
-//     unit, which reads the request's partials with device-coherent loads,
-//     merges them, rounds the attention output to bf16, applies RMSNorm x
-//     sigmoid(gate), writes bf16 out and re-arms the counter.
+//     with device-coherent stores; an atomic counter per (request, token group)
+//     elects the group's last unit, which reads the group's partials with
+//     device-coherent loads, merges them, rounds the attention output to bf16,
+//     applies RMSNorm x sigmoid(gate), writes bf16 out and re-arms the counter.
 //
 // Cross-workgroup visibility (C): partials are written and read only with
 // agent-scope atomic accesses (sc1: coherent across the XCDs' L2 caches), and
@@ -61,6 +67,65 @@ __device__ inline float2 load_coherent(const float* src) {
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
 
+// Cross-lane moves on the VALU (DPP and the gfx950 lane swaps) rather than LDS
+// permutes.  DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
+// (lane ^ 2), row_half_mirror (lane i <-> 7 - i in each 8), row_mirror (lane
+// i <-> 15 - i in each 16-lane row), row_newbcast n (lane n of each row to the
+// whole row).
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppRowBcast = 0x150;
+
+template <int C>
+__device__ inline int dpp(int x) { return __builtin_amdgcn_mov_dpp(x, C, 0xF, 0xF, false); }
+template <int C>
+__device__ inline float dpp(float x) { return __int_as_float(dpp<C>(__float_as_int(x))); }
+template <int C>
+__device__ inline double dpp(double x) {
+  const long v = __double_as_longlong(x);
+  const int lo = dpp<C>((int)v), hi = dpp<C>((int)(v >> 32));
+  return __longlong_as_double((long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Sum over each aligned group of 8 (16) lanes.  Every step adds the same two
+// values in every lane of a pair, so all lanes of a group end with one value.
+__device__ inline double sum8(double s) {
+  s += dpp<kDppXor1>(s);
+  s += dpp<kDppXor2>(s);
+  return s + dpp<kDppHalfMirror>(s);
+}
+__device__ inline float sum16(float s) {
+  s += dpp<kDppXor1>(s);
+  s += dpp<kDppXor2>(s);
+  s += dpp<kDppHalfMirror>(s);
+  return s + dpp<kDppMirror>(s);
+}
+
+// Maximum of three values in one v_max3_f32, without the quieting moves the
+// compiler puts before fmaxf on values it cannot prove canonical (MFMA results).
+__device__ inline float fmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Maximum / sum of lane j over the four 16-lane rows: the 16-row swap pairs
+// rows (0,1) and (2,3), the 32-row swap then pairs the halves.
+__device__ inline float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ inline float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Page-table entry of logical key `key` (the load only; nothing waits on it).
 __device__ inline int page_entry(const StepParams& p, const int32_t* pt, int key) {
   const int page = p.page_shift >= 0 ? key >> p.page_shift : key / p.page_size;
@@ -84,25 +149,43 @@ struct KvBlock {
   uint32_t v[kKvHeads][8];   // lane (q4, j): columns 4j..4j+3 of keys 16(r/4)+4q4+r%4
 };
 
-// `entry`: this lane's page-table entry for key `key` (= block base + lane % 32,
-// clamped); the rows are shared by lane shuffles, so each lane issues one
-// page-table load per block.
-__device__ inline KvBlock load_kv(const StepParams& p, int entry, int key, int j, int q4) {
-  const int myrow = key_row(p, entry, key);
+// Offset in a 32-key block of the key whose page-table entry lane l fetches for
+// the V operand: lane (q4, n) of row q4, n < 8, takes key 16(n/4) + 4q4 + n%4,
+// the keys every lane of row q4 reads V from.
+__device__ inline int v_key_offset(int lane) {
+  return 16 * ((lane & 7) >> 2) + 4 * (lane >> 4) + (lane & 3);
+}
+
+// `kk`, `kv`: this lane's keys and page-table entries for the K operand (block
+// base + lane % 32) and the V operand (block base + v_key_offset), clamped.
+// Rows reach the lanes that read them by lane swaps and row broadcasts.
+__device__ inline KvBlock load_kv(const StepParams& p, int2 entry, int kk, int kv, int j, int q4) {
+  const int krow = key_row(p, entry.x, kk);
+  const int vrow = key_row(p, entry.y, kv);
+  // Lanes 32..63 repeat lanes 0..31, so the 16-row swap leaves row 0's rows
+  // (keys 0..15) in a[0] and row 1's (keys 16..31) in a[1], in every row.
+  const auto a = __builtin_amdgcn_permlane16_swap((unsigned)krow, (unsigned)krow, false, false);
   KvBlock d;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = __shfl(myrow, 16 * t + j);
-    const uint8_t* kr = p.k_cache + (int64_t)row * kRowBytes + 16 * q4;
+    const uint8_t* kr = p.k_cache + (int64_t)(int)a[t] * kRowBytes + 16 * q4;
     d.k[t][0] = *reinterpret_cast<const uint4*>(kr);
     d.k[t][1] = *reinterpret_cast<const uint4*>(kr + kHeadDim);
   }
+  int vr[8];
+  vr[0] = dpp<kDppRowBcast + 0>(vrow);
+  vr[1] = dpp<kDppRowBcast + 1>(vrow);
+  vr[2] = dpp<kDppRowBcast + 2>(vrow);
+  vr[3] = dpp<kDppRowBcast + 3>(vrow);
+  vr[4] = dpp<kDppRowBcast + 4>(vrow);
+  vr[5] = dpp<kDppRowBcast + 5>(vrow);
+  vr[6] = dpp<kDppRowBcast + 6>(vrow);
+  vr[7] = dpp<kDppRowBcast + 7>(vrow);
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const int row = __shfl(myrow, 16 * (r >> 2) + 4 * q4 + (r & 3));
-    const uint8_t* vr = p.v_cache + (int64_t)row * kRowBytes + 4 * j;
-    d.v[0][r] = *reinterpret_cast<const uint32_t*>(vr);
-    d.v[1][r] = *reinterpret_cast<const uint32_t*>(vr + kHeadDim);
+    const uint8_t* vp = p.v_cache + (int64_t)vr[r] * kRowBytes + 4 * j;
+    d.v[0][r] = *reinterpret_cast<const uint32_t*>(vp);
+    d.v[1][r] = *reinterpret_cast<const uint32_t*>(vp + kHeadDim);
   }
   return d;
 }
@@ -117,9 +200,7 @@ __device__ inline void norm_rope8(const float (&x)[8], bool rope, const float (*
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < 8; ++k) ss += (double)(x[k] * x[k]);
-  ss += __shfl_xor(ss, 1, 8);
-  ss += __shfl_xor(ss, 2, 8);
-  ss += __shfl_xor(ss, 4, 8);
+  ss = sum8(ss);
   const float ms = (float)ss / 64.0f;
   const float inv = rsqrt_exact(ms + 1.0e-5f);
 #pragma unroll
@@ -142,41 +223,60 @@ __device__ inline uint2 pack_e4m3x8(const float (&y)[8]) {
   return make_uint2(lo, hi);
 }
 
-template <int L>
+template <int LU>
 __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
-  constexpr int NRB = (L * kGroup + 15) / 16;  // 16-row blocks per KV head
-  constexpr int kItems = L * kHeadRows * 8;    // (token, head row, 8-column slice)
-  constexpr int kItemIters = (kItems + 255) / 256;
-  __shared__ __align__(16) uint8_t s_q[L][kQHeads][kHeadDim];
-  __shared__ __align__(16) uint8_t s_newk[L][kRowBytes];
-  __shared__ __align__(16) uint8_t s_newv[L][kRowBytes];
-  __shared__ float s_cs[L][kHeadDim / 2][2];
-  __shared__ __align__(16) float s_mo[kAttnWaves][L * kQHeads][kHeadDim];
-  __shared__ __align__(16) float s_ml[kAttnWaves][L * kQHeads][2];
+  // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
+  // LU consecutive tokens; the unit (request b, token group tg, key chunk kc)
+  // attends its group's query rows over chunk kc of the request's keys.
+  constexpr int NRB = (LU * kGroup + 15) / 16;  // 16-row blocks per KV head
+  constexpr int kQItems = LU * kQHeads * 8;     // (token, q head, 8-column slice)
+  constexpr int kMaxItems = kQItems + 2 * LU * 2 * kKvHeads * 8;  // + K/V rows of <= 2*LU tokens
+  constexpr int kItemIters = (kMaxItems + 255) / 256;
+  constexpr int kRows = LU * kQHeads;           // partial rows of a unit
+  __shared__ __align__(16) uint8_t s_q[LU][kQHeads][kHeadDim];
+  __shared__ __align__(16) uint8_t s_newk[kMaxQLen][kRowBytes];
+  __shared__ __align__(16) uint8_t s_newv[kMaxQLen][kRowBytes];
+  __shared__ float s_cs[kMaxQLen][kHeadDim / 2][2];
+  __shared__ __align__(16) float s_mo[kAttnWaves][kRows][kHeadDim];
+  __shared__ __align__(16) float s_ml[kAttnWaves][kRows][2];
   __shared__ int s_last;
 
-  const int b = blockIdx.x / p.splits;
-  const int s = blockIdx.x - b * p.splits;
+  // q_len 1 and 2 are the only lengths served by LU = 1 and 2 (one group).
+  constexpr bool kOneGroup = LU <= 2;
+  const int L = kOneGroup ? LU : p.q_len;
+  const int kc = blockIdx.x % p.splits;
+  const int bt = blockIdx.x / p.splits;
+  const int b = kOneGroup ? bt : bt % p.batch;
+  const int tg = kOneGroup ? 0 : bt / p.batch;
+  const int t_lo = tg * LU;              // the group's first token (request-local)
+  const int t_n = min(LU, L - t_lo);     // its tokens, >= 1
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int j = lane & 15;
   const int q4 = lane >> 4;
   const int64_t tok0 = (int64_t)b * L;
+  const int kItems = kQItems + L * 2 * kKvHeads * 8;
 
   // ---------------- A. geometry and early loads ----------------
   const int cs = p.cache_seqlens[b];
   const uint16_t* qkv_b = p.qkv + tok0 * kWidth;
+  // Item -> (request-local token, head row, 8-column slice): q rows of the
+  // group's tokens first, then the K and V rows of every token.
+  auto item_token = [&](int item) {
+    return item < kQItems ? t_lo + (item >> 7) : (item - kQItems) >> 5;
+  };
+  auto item_row = [&](int item) {
+    return item < kQItems ? (item >> 3) & (kQHeads - 1) : kQHeads + (((item - kQItems) >> 3) & 3);
+  };
   uint4 xv[kItemIters];
 #pragma unroll
   for (int it = 0; it < kItemIters; ++it) {
     const int item = tid + 256 * it;
     xv[it] = make_uint4(0, 0, 0, 0);
-    if (item < kItems) {
-      const int i = item / (kHeadRows * 8), rem = item - i * (kHeadRows * 8);
-      xv[it] = *reinterpret_cast<const uint4*>(qkv_b + i * kWidth + (rem >> 3) * kHeadDim +
-                                                (rem & 7) * 8);
-    }
+    if (item < kItems && item_token(item) < L)
+      xv[it] = *reinterpret_cast<const uint4*>(qkv_b + item_token(item) * kWidth +
+                                                item_row(item) * kHeadDim + (item & 7) * 8);
   }
   const bool cs_thread = p.rope && tid < 32 * L;
   int64_t my_slot = p.cache_loc[tok0 + min(tid, L - 1)];
@@ -188,13 +288,13 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   // memory counters complete in order, waiting for it would wait for them too.
   asm volatile("" : "+v"(my_ang), "+v"(ks), "+v"(vs), "+v"(my_slot));
 
-  const int p0 = cs - L;  // key index (position) of the block's first new token
+  const int p0 = cs - L;  // key index (position) of the request's first new token
   const int last = cs - 1;
   const int first = p.window > 0 ? max(0, p0 - p.window + 1) : 0;
   const int n = max(0, last - first + 1);
   int chunk = (n + p.splits - 1) / p.splits;
   chunk = (chunk + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
-  const int start = first + s * chunk;
+  const int start = first + kc * chunk;
   const int end = min(start + chunk, last + 1);
   const int nblk = end > start ? (end - start + kKeyBlock - 1) / kKeyBlock : 0;
   const int nb = nblk > wave ? (nblk - wave + kAttnWaves - 1) / kAttnWaves : 0;  // this wave's
@@ -203,27 +303,32 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   // clamped to it, so the pipeline's loads are unconditional (which keeps the
   // compiler's memory-counter waits exact) and the extra ones hit cache lines
   // already fetched.
-  auto lane_key = [&](int i) {
+  const int voff = v_key_offset(lane);
+  auto block_key = [&](int i, int off) {
     const int blk = min(i, max(nb - 1, 0));
-    return max(0, min(start + (wave + kAttnWaves * blk) * kKeyBlock + (lane & 31), end - 1));
+    return max(0, min(start + (wave + kAttnWaves * blk) * kKeyBlock + off, end - 1));
   };
-  auto load_pte = [&](int i) { return page_entry(p, pt, lane_key(i)); };
+  auto k_key = [&](int i) { return block_key(i, lane & 31); };
+  auto v_key = [&](int i) { return block_key(i, voff); };
+  auto load_pte = [&](int i) { return make_int2(page_entry(p, pt, k_key(i)), page_entry(p, pt, v_key(i))); };
+  auto load_block = [&](int2 e, int i) { return load_kv(p, e, k_key(i), v_key(i), j, q4); };
 
   // Issue order matters (vector memory counters complete in order): each block's
   // page-table load follows the K/V loads two blocks earlier, so waiting for it
   // never waits for the next block's K/V.
-  const int pte0 = load_pte(0);
-  const int pte1 = load_pte(1);
-  KvBlock bufA = load_kv(p, pte0, lane_key(0), j, q4);
-  int pa = load_pte(2);
-  KvBlock bufB = load_kv(p, pte1, lane_key(1), j, q4);
-  int pb = load_pte(3);
+  const int2 pte0 = load_pte(0);
+  const int2 pte1 = load_pte(1);
+  KvBlock bufA = load_block(pte0, 0);
+  int2 pa = load_pte(2);
+  KvBlock bufB = load_block(pte1, 1);
+  int2 pb = load_pte(3);
 
-  // New token i's key is stored and substituted by the unit whose chunk holds
-  // it (by unit 0 when it has no place in any chunk, e.g. a padded slot).
-  auto owns = [&](int i) {
+  // New token i's K/V codes are needed by the units whose chunk holds its key
+  // (one per token group); the group-0 one stores them.  A key with no place in
+  // any chunk (a padded slot) goes to chunk 0.
+  auto chunk_has = [&](int i) {
     const int key = p0 + i;
-    return (key >= start && key < end) || (key < first && s == 0);
+    return (key >= start && key < end) || (key < first && kc == 0);
   };
 
   // RoPE table for the request's tokens: (token, frequency) per thread.
@@ -238,11 +343,11 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 #pragma unroll
   for (int it = 0; it < kItemIters; ++it) {
     const int item = tid + 256 * it;
-    const int i = min(item / (kHeadRows * 8), L - 1);
-    const int rem = item - (item / (kHeadRows * 8)) * (kHeadRows * 8);
-    const int hr = rem >> 3, c8 = rem & 7;
+    const int i = min(item_token(item), L - 1);
+    const int hr = item_row(item), c8 = item & 7;
+    const bool is_q = item < kQItems;
     // Whole 8-lane groups are skipped together (the norm shuffles stay in-group).
-    if (item >= kItems || (hr >= kQHeads && !owns(i))) continue;
+    if (item >= kItems || item_token(item) >= L || (!is_q && !chunk_has(i))) continue;
     float x[8], y[8];
     const uint32_t w[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
 #pragma unroll
@@ -261,9 +366,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       for (int k = 0; k < 8; ++k) y[k] = p.scaled ? round_bf16(x[k] / vs) : x[k];  // raw value
     }
     const uint2 codes = pack_e4m3x8(y);
-    if (hr < kQHeads) {
-      *reinterpret_cast<uint2*>(&s_q[i][hr][c8 * 8]) = codes;
-      if (s == 0)
+    if (is_q) {
+      *reinterpret_cast<uint2*>(&s_q[i - t_lo][hr][c8 * 8]) = codes;
+      if (kc == 0)
         *reinterpret_cast<uint2*>(p.q_out + ((tok0 + i) * kQHeads + hr) * kHeadDim + c8 * 8) = codes;
     } else if (hr < kQHeads + kKvHeads) {
       *reinterpret_cast<uint2*>(&s_newk[i][(hr - kQHeads) * kHeadDim + c8 * 8]) = codes;
@@ -273,7 +378,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   }
   lds_barrier();
 
-  if (tid < L && owns(tid) && my_slot >= 0 && my_slot < p.num_rows) {
+  if (tid < L && tg == 0 && chunk_has(tid) && my_slot >= 0 && my_slot < p.num_rows) {
     const uint4* kk = reinterpret_cast<const uint4*>(s_newk[tid]);
     const uint4* vv = reinterpret_cast<const uint4*>(s_newv[tid]);
     uint4* kd = reinterpret_cast<uint4*>(p.k_cache + my_slot * kRowBytes);
@@ -286,27 +391,27 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   }
 
   // q operands and per-row visible ranges.  Row r = 16*rb + j of KV head g is
-  // query token r / 8, query head 8g + r % 8.
+  // the group's token r / 8, query head 8g + r % 8.
   long qop[kKvHeads][NRB][2];
   int rlo[NRB], rhi[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     const int r = 16 * rb + j;
-    const int i = r >> 3;
-    const bool valid = i < L;
-    const int pi = p0 + i;
+    const int ti = r >> 3;
+    const bool valid = ti < t_n;
+    const int pi = p0 + t_lo + ti;
     rlo[rb] = valid ? (p.window > 0 ? max(0, pi - p.window + 1) : 0) : 1;
     rhi[rb] = valid ? pi : 0;
 #pragma unroll
     for (int g = 0; g < kKvHeads; ++g) {
-      const uint4 qv = *reinterpret_cast<const uint4*>(&s_q[min(i, L - 1)][g * kGroup + (r & 7)][16 * q4]);
+      const uint4 qv = *reinterpret_cast<const uint4*>(&s_q[min(ti, LU - 1)][g * kGroup + (r & 7)][16 * q4]);
       qop[g][rb][0] = valid ? as_long(qv.x, qv.y) : 0;
       qop[g][rb][1] = valid ? as_long(qv.z, qv.w) : 0;
     }
   }
-  // A block is visible to every row when it lies in [lo_all, hi_all].
-  const int lo_all = p.window > 0 ? max(0, p0 + L - 1 - p.window + 1) : 0;
-  const int hi_all = min(p0, end - 1);
+  // A block is visible to every row of the group when it lies in [lo_all, hi_all].
+  const int lo_all = p.window > 0 ? max(0, p0 + t_lo + t_n - 1 - p.window + 1) : 0;
+  const int hi_all = min(p0 + t_lo, end - 1);
   const float scale = p.sm_scale_log2 * ks;
 
   float mrow[kKvHeads][NRB], lrow[kKvHeads][NRB];
@@ -322,38 +427,39 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
     }
 
   // ---------------- B. key loop ----------------
-  auto process = [&](KvBlock& d, const int kbase) {
-    if (kbase + kKeyBlock - 1 >= p0) {  // the block holds new keys: use their codes
+  // New keys' codes replace the cache bytes of a block that holds them.
+  auto substitute = [&](KvBlock& d, const int kbase) {
+    if (kbase + kKeyBlock - 1 < p0) return;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int key = kbase + 16 * t + j;
-        const int i = min(max(key - p0, 0), L - 1);
-        const bool nk = key >= p0;
+    for (int t = 0; t < 2; ++t) {
+      const int key = kbase + 16 * t + j;
+      const int i = min(max(key - p0, 0), L - 1);
+      const bool nk = key >= p0;
 #pragma unroll
-        for (int g = 0; g < kKvHeads; ++g) {
-          const uint4 nv = *reinterpret_cast<const uint4*>(&s_newk[i][g * kHeadDim + 16 * q4]);
-          d.k[t][g].x = nk ? nv.x : d.k[t][g].x;
-          d.k[t][g].y = nk ? nv.y : d.k[t][g].y;
-          d.k[t][g].z = nk ? nv.z : d.k[t][g].z;
-          d.k[t][g].w = nk ? nv.w : d.k[t][g].w;
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int key = kbase + 16 * (r >> 2) + 4 * q4 + (r & 3);
-        const int i = min(max(key - p0, 0), L - 1);
-        const bool nk = key >= p0;
-#pragma unroll
-        for (int g = 0; g < kKvHeads; ++g) {
-          const uint32_t nv = *reinterpret_cast<const uint32_t*>(&s_newv[i][g * kHeadDim + 4 * j]);
-          d.v[g][r] = nk ? nv : d.v[g][r];
-        }
+      for (int g = 0; g < kKvHeads; ++g) {
+        const uint4 nv = *reinterpret_cast<const uint4*>(&s_newk[i][g * kHeadDim + 16 * q4]);
+        d.k[t][g].x = nk ? nv.x : d.k[t][g].x;
+        d.k[t][g].y = nk ? nv.y : d.k[t][g].y;
+        d.k[t][g].z = nk ? nv.z : d.k[t][g].z;
+        d.k[t][g].w = nk ? nv.w : d.k[t][g].w;
       }
     }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int key = kbase + 16 * (r >> 2) + 4 * q4 + (r & 3);
+      const int i = min(max(key - p0, 0), L - 1);
+      const bool nk = key >= p0;
+#pragma unroll
+      for (int g = 0; g < kKvHeads; ++g) {
+        const uint32_t nv = *reinterpret_cast<const uint32_t*>(&s_newv[i][g * kHeadDim + 4 * j]);
+        d.v[g][r] = nk ? nv : d.v[g][r];
+      }
+    }
+  };
 
-    // V^T operand: per KV head and column c (of the lane's 4), the 8 keys as f16
-    // pairs; perm gathers byte c (and c+1) of two key rows.
-    v8h va[kKvHeads][4];
+  // V^T operand: per KV head and column c (of the lane's 4), the 8 keys as f16
+  // pairs; perm gathers byte c (and c+1) of two key rows.
+  auto v_operand = [&](const KvBlock& d, v8h (&va)[kKvHeads][4]) {
 #pragma unroll
     for (int g = 0; g < kKvHeads; ++g) {
 #pragma unroll
@@ -374,38 +480,76 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
         va[g][3][2 * rp + 1] = c3[1];
       }
     }
+  };
 
-    // Per KV head: the scores of all its row blocks first (their MFMAs overlap),
-    // then one wave-uniform running-max decision, then P and PV.
-    const bool full = kbase >= lo_all && kbase + kKeyBlock - 1 <= hi_all;
+  // Raw q.k of one block for every row block: lane (q4, j) gets keys
+  // 16t + 4q4 + i (slot 4t + i) of row j.
+  auto qk = [&](const KvBlock& d, float (&z)[kKvHeads][NRB][8]) {
+#pragma unroll
+    for (int g = 0; g < kKvHeads; ++g)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          v4f c = {0.f, 0.f, 0.f, 0.f};
+          c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(d.k[t][g].x, d.k[t][g].y),
+                                                          qop[g][rb][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(d.k[t][g].z, d.k[t][g].w),
+                                                          qop[g][rb][1], c, 0, 0, 0);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) z[g][rb][t * 4 + ii] = c[ii];
+        }
+  };
+
+  // Invisible keys (outside the chunk or a row's window) get a -inf score.
+  auto mask = [&](const int kbase, float (&z)[kKvHeads][NRB][8]) {
+    if (kbase >= lo_all && kbase + kKeyBlock - 1 <= hi_all) return;  // visible to every row
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        const bool vis = key < end && key >= rlo[rb] && key <= rhi[rb];
+#pragma unroll
+        for (int g = 0; g < kKvHeads; ++g) z[g][rb][k] = vis ? z[g][rb][k] : -INFINITY;
+      }
+    }
+  };
+
+  // Blocks are taken in pairs: the scores and V^T operands of both, then the
+  // next pair's loads are issued, then per KV head one running-max decision for
+  // the pair and P / PV for both.  Scores stay raw (q.k): the scale (> 0) goes
+  // into the exponent's fma, so the maximum is taken on raw scores.
+  for (int bi = 0; bi < nb; bi += 2) {
+    const bool has_b = bi + 1 < nb;
+    // An absent second block sits past the chunk: every key masked, no codes substituted.
+    const int kb0 = start + (wave + kAttnWaves * bi) * kKeyBlock;
+    const int kb1 = has_b ? kb0 + kAttnWaves * kKeyBlock : end;
+    substitute(bufA, kb0);
+    if (has_b) substitute(bufB, kb1);
+    float z0[kKvHeads][NRB][8], z1[kKvHeads][NRB][8];
+    qk(bufA, z0);
+    qk(bufB, z1);
+    v8h va0[kKvHeads][4], va1[kKvHeads][4];
+    v_operand(bufA, va0);
+    v_operand(bufB, va1);
+    bufA = load_block(pa, bi + 2);
+    bufB = load_block(pb, bi + 3);
+    pa = load_pte(bi + 4);
+    pb = load_pte(bi + 5);
+    mask(kb0, z0);
+    mask(kb1, z1);
 #pragma unroll
     for (int g = 0; g < kKvHeads; ++g) {
-      float sv[NRB][8];
-      float lmx[NRB];     // this lane's maximum over its 8 keys
+      float lmx[NRB];     // this lane's scaled maximum over its 16 keys of the pair
       bool grow = false;  // some lane's maximum passes its row's lazy bound
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          v4f z = {0.f, 0.f, 0.f, 0.f};
-          z = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(d.k[t][g].x, d.k[t][g].y),
-                                                          qop[g][rb][0], z, 0, 0, 0);
-          z = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(d.k[t][g].z, d.k[t][g].w),
-                                                          qop[g][rb][1], z, 0, 0, 0);
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) sv[rb][t * 4 + ii] = z[ii] * scale;
-        }
-        if (!full) {
-#pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
-            const bool vis = key < end && key >= rlo[rb] && key <= rhi[rb];
-            sv[rb][k] = vis ? sv[rb][k] : -INFINITY;
-          }
-        }
-        const float* v = sv[rb];
-        lmx[rb] = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])),
-                        fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
+        const float* u = z0[g][rb];
+        const float* v = z1[g][rb];
+        float m = fmax3(fmax3(u[0], u[1], u[2]), fmax3(u[3], u[4], u[5]), fmax3(u[6], u[7], v[0]));
+        m = fmax3(m, fmax3(v[1], v[2], v[3]), fmax3(v[4], v[5], v[6]));
+        lmx[rb] = fmax3(m, v[7], -INFINITY) * scale;
         grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
       }
       // A row's maximum moves only when its full maximum (over the four lane
@@ -414,9 +558,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       if (__any(grow)) {
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          float mx = lmx[rb];
-          mx = fmaxf(mx, __shfl_xor(mx, 16));
-          mx = fmaxf(mx, __shfl_xor(mx, 32));
+          const float mx = rows_max(lmx[rb]);
           const float mold = mrow[g][rb];
           const float mnew = mx > mold + kLazyRescale ? mx : mold;
           const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
@@ -428,30 +570,25 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       }
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const float muse = mrow[g][rb] == -INFINITY ? 0.0f : mrow[g][rb];
-        v8h pb;
+        const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
+        v8h p0v, p1v;
         float psum = 0.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float pk = __builtin_amdgcn_exp2f(sv[rb][k] - muse);
-          psum += pk;
-          pb[k] = (_Float16)pk;
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z0[g][rb][k], scale, nmuse));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z1[g][rb][k], scale, nmuse));
+          psum += e0 + e1;
+          p0v[k] = (_Float16)e0;
+          p1v[k] = (_Float16)e1;
         }
         lrow[g][rb] += psum;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[g][c], pb, acc[g][rb][c], 0, 0, 0);
+        for (int c = 0; c < 4; ++c) {
+          acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0[g][c], p0v, acc[g][rb][c], 0, 0, 0);
+          acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1[g][c], p1v, acc[g][rb][c], 0, 0, 0);
+        }
       }
     }
-  };
-
-  for (int bi = 0; bi < nb; bi += 2) {
-    process(bufA, start + (wave + kAttnWaves * bi) * kKeyBlock);
-    bufA = load_kv(p, pa, lane_key(bi + 2), j, q4);
-    pa = load_pte(bi + 4);
-    if (bi + 1 < nb) process(bufB, start + (wave + kAttnWaves * (bi + 1)) * kKeyBlock);
-    bufB = load_kv(p, pb, lane_key(bi + 3), j, q4);
-    pb = load_pte(bi + 5);
   }
 
   // Row sums: each lane summed its own keys; add the four lane groups of a row.
@@ -459,22 +596,21 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   for (int g = 0; g < kKvHeads; ++g)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
-      lrow[g][rb] += __shfl_xor(lrow[g][rb], 16);
-      lrow[g][rb] += __shfl_xor(lrow[g][rb], 32);
+      lrow[g][rb] = rows_sum(lrow[g][rb]);
     }
 
   // ---------------- C. merge the waves, publish the partial ----------------
   // Every wave parks (m, l, o) of its valid rows in its LDS slot (compact row
-  // i*16 + h); after one barrier all 256 threads merge 4 columns of a row each
-  // and publish the unit's partial.
+  // ti*16 + h for the group's token ti); after one barrier all 256 threads merge
+  // 4 columns of a row each and publish the unit's partial.
 #pragma unroll
   for (int g = 0; g < kKvHeads; ++g)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = 16 * rb + j;
-      const int i = r >> 3;
-      if (i >= L) continue;
-      const int cr = i * kQHeads + g * kGroup + (r & 7);
+      const int ti = r >> 3;
+      if (ti >= t_n) continue;
+      const int cr = ti * kQHeads + g * kGroup + (r & 7);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         *reinterpret_cast<float4*>(&s_mo[wave][cr][16 * q4 + 4 * ii]) =
@@ -482,8 +618,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       if (q4 == 0) *reinterpret_cast<float2*>(&s_ml[wave][cr][0]) = make_float2(mrow[g][rb], lrow[g][rb]);
     }
   lds_barrier();
-  const int64_t prow0 = (int64_t)(b * p.splits + s) * (L * kQHeads);
-  for (int idx = tid; idx < L * kQHeads * 16; idx += 256) {
+  // Partial rows are ((b * splits + kc) * L + token) * 16 + head.
+  const int64_t prow0 = (((int64_t)b * p.splits + kc) * L + t_lo) * kQHeads;
+  for (int idx = tid; idx < t_n * kQHeads * 16; idx += 256) {
     const int cr = idx >> 4, c4 = (idx & 15) * 4;
     float mw[kAttnWaves], lw[kAttnWaves];
     float mx = -INFINITY;
@@ -514,102 +651,107 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
   __syncthreads();
+  int32_t* counter = p.counters + (kOneGroup ? b : b * p.tgroups + tg);
   if (tid == 0)
-    s_last = __hip_atomic_fetch_add(&p.counters[b], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             p.splits - 1;
+    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
   __syncthreads();
   if (!s_last) return;
 
-  // ---------------- D. combine + gated epilogue (last unit) ----------------
+  // ---------------- D. combine + gated epilogue (last unit of the group) ----------------
   // Thread (h, c4) takes columns c4..c4+3 of head h for every token of the
-  // request.  The partials are read KS splits at a time for all tokens at once,
-  // so the chain of device-coherent round trips is ceil(splits / KS) long
-  // whatever the number of tokens.
-  constexpr int KS = L >= 8 ? 4 : (32 / L > 16 ? 16 : 32 / L);
+  // group.  The partials are read KS splits at a time for all the group's
+  // tokens at once, so the chain of device-coherent round trips is
+  // ceil(splits / KS) long whatever the number of tokens.
+  constexpr int KS = LU >= 4 ? 4 : (LU == 3 ? 5 : (LU == 2 ? 8 : 16));
   const int c4 = (tid & 15) * 4;
   const int h = tid >> 4;
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
-  const int64_t base = (int64_t)b * p.splits * stride + h;
-  uint2 graw[L];
+  const int64_t base = (int64_t)b * p.splits * stride + (int64_t)t_lo * kQHeads + h;
+  uint2 graw[LU];
 #pragma unroll
-  for (int i = 0; i < L; ++i)
-    graw[i] = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + i) * kWidth + kGateOffset + h * kHeadDim + c4);
-  float mrun[L], lrun[L], o[L][4];
+  for (int ti = 0; ti < LU; ++ti) {
+    graw[ti] = make_uint2(0, 0);
+    if (ti < t_n)
+      graw[ti] = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + t_lo + ti) * kWidth + kGateOffset +
+                                                  h * kHeadDim + c4);
+  }
+  float mrun[LU], lrun[LU], o[LU][4];
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    mrun[i] = -INFINITY;
-    lrun[i] = 0.0f;
+  for (int ti = 0; ti < LU; ++ti) {
+    mrun[ti] = -INFINITY;
+    lrun[ti] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[i][c] = 0.0f;
+    for (int c = 0; c < 4; ++c) o[ti][c] = 0.0f;
   }
   for (int s0 = 0; s0 < p.splits; s0 += KS) {
-    float2 ml[L][KS], o01[L][KS], o23[L][KS];
+    float2 ml[LU][KS], o01[LU][KS], o23[LU][KS];
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
 #pragma unroll
-      for (int i = 0; i < L; ++i) {
-        ml[i][k] = make_float2(-INFINITY, 0.0f);
-        o01[i][k] = o23[i][k] = make_float2(0.0f, 0.0f);
-        if (s0 + k < p.splits) {
-          const int64_t pr = base + (int64_t)(s0 + k) * stride + i * kQHeads;
-          ml[i][k] = load_coherent(p.part_ml + pr * 2);
-          o01[i][k] = load_coherent(p.part_o + pr * kHeadDim + c4);
-          o23[i][k] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
+      for (int ti = 0; ti < LU; ++ti) {
+        ml[ti][k] = make_float2(-INFINITY, 0.0f);
+        o01[ti][k] = o23[ti][k] = make_float2(0.0f, 0.0f);
+        if (ti < t_n && s0 + k < p.splits) {
+          const int64_t pr = base + (int64_t)(s0 + k) * stride + ti * kQHeads;
+          ml[ti][k] = load_coherent(p.part_ml + pr * 2);
+          o01[ti][k] = load_coherent(p.part_o + pr * kHeadDim + c4);
+          o23[ti][k] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < L; ++i) {
-      float mc = mrun[i];
+    for (int ti = 0; ti < LU; ++ti) {
+      float mc = mrun[ti];
 #pragma unroll
-      for (int k = 0; k < KS; ++k) mc = fmaxf(mc, ml[i][k].x);
+      for (int k = 0; k < KS; ++k) mc = fmaxf(mc, ml[ti][k].x);
       const float muse = mc == -INFINITY ? 0.0f : mc;
-      const float a = __builtin_amdgcn_exp2f(mrun[i] - muse);
-      lrun[i] *= a;
+      const float a = __builtin_amdgcn_exp2f(mrun[ti] - muse);
+      lrun[ti] *= a;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[i][c] *= a;
+      for (int c = 0; c < 4; ++c) o[ti][c] *= a;
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
-        const float wk = __builtin_amdgcn_exp2f(ml[i][k].x - muse);
-        lrun[i] += wk * ml[i][k].y;
-        o[i][0] += wk * o01[i][k].x;
-        o[i][1] += wk * o01[i][k].y;
-        o[i][2] += wk * o23[i][k].x;
-        o[i][3] += wk * o23[i][k].y;
+        const float wk = __builtin_amdgcn_exp2f(ml[ti][k].x - muse);
+        lrun[ti] += wk * ml[ti][k].y;
+        o[ti][0] += wk * o01[ti][k].x;
+        o[ti][1] += wk * o01[ti][k].y;
+        o[ti][2] += wk * o23[ti][k].x;
+        o[ti][3] += wk * o23[ti][k].y;
       }
-      mrun[i] = mc;
+      mrun[ti] = mc;
     }
   }
+  // The tokens' epilogues are independent chains (shuffles, fp64 rsqrt, gate):
+  // computed for every slot without branches so they interleave; only the
+  // stores of the group's real tokens are kept.
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const float inv = lrun[i] > 0.0f ? vs / lrun[i] : 0.0f;
+  for (int ti = 0; ti < LU; ++ti) {
+    const float inv = lrun[ti] > 0.0f ? vs / lrun[ti] : 0.0f;
     float y[4];
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      y[c] = round_bf16(o[i][c] * inv);  // the attention result is bf16 before the epilogue
+      y[c] = round_bf16(o[ti][c] * inv);  // the attention result is bf16 before the epilogue
       ss += y[c] * y[c];
     }
-    ss += __shfl_xor(ss, 1, 16);
-    ss += __shfl_xor(ss, 2, 16);
-    ss += __shfl_xor(ss, 4, 16);
-    ss += __shfl_xor(ss, 8, 16);
+    ss = sum16(ss);
     const float r = (float)(1.0 / sqrt((double)ss / 64.0 + 1.0e-5));
-    const float gate[4] = {bf16_value(graw[i].x & 0xffffu), bf16_value(graw[i].x >> 16),
-                           bf16_value(graw[i].y & 0xffffu), bf16_value(graw[i].y >> 16)};
+    const float gate[4] = {bf16_value(graw[ti].x & 0xffffu), bf16_value(graw[ti].x >> 16),
+                           bf16_value(graw[ti].y & 0xffffu), bf16_value(graw[ti].y >> 16)};
     uint32_t ob[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * (1.0f / (1.0f + __expf(-gate[c]))));
-    *reinterpret_cast<uint2*>(p.out + (tok0 + i) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
-        make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
+    if (ti < t_n)
+      *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
+          make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
   }
-  if (tid == 0) __hip_atomic_store(&p.counters[b], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int L>
-hipError_t launch_l(const StepParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)p.batch * (unsigned)p.splits;
-  hipLaunchKernelGGL(fused_step_kernel<L>, dim3(grid), dim3(64 * kAttnWaves), 0, stream, p);
+template <int LU>
+hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
+  const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
+  hipLaunchKernelGGL(fused_step_kernel<LU>, dim3(grid), dim3(64 * kAttnWaves), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -620,17 +762,15 @@ __global__ void zero_counters_kernel(int32_t* c, int n) {
 
 }  // namespace
 
-hipError_t launch_step(const StepParams& p, int q_len, hipStream_t stream) {
+hipError_t launch_step(const StepParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
-  switch (q_len) {
-    case 1: return launch_l<1>(p, stream);
-    case 2: return launch_l<2>(p, stream);
-    case 3: return launch_l<3>(p, stream);
-    case 4: return launch_l<4>(p, stream);
-    case 5: return launch_l<5>(p, stream);
-    case 6: return launch_l<6>(p, stream);
-    case 7: return launch_l<7>(p, stream);
-    case 8: return launch_l<8>(p, stream);
+  if (p.q_len < 1 || p.q_len > kMaxQLen || p.tgroups < 1 || p.tgroups > 2) return hipErrorInvalidValue;
+  const int lu = (p.q_len + p.tgroups - 1) / p.tgroups;  // tokens per unit
+  switch (lu) {
+    case 1: return launch_lu<1>(p, stream);
+    case 2: return launch_lu<2>(p, stream);
+    case 3: return launch_lu<3>(p, stream);
+    case 4: return launch_lu<4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -94,6 +94,7 @@ int mi355x_gated_attn_prepare(const mi355x_gated_attn_config* cfg, int device,
  * metadata and its split-count heuristic.  max_context bounds
  * cache_seqlens[b] (keys per request including the new tokens) and only steers
  * the split count; num_splits > 0 forces the count (1..256), 0 chooses it.
+ * A step launches B * ceil(L/4) * splits workgroups (UNSUPPORTED beyond 2^31-1).
  * Outputs (either may be NULL): *workspace_bytes = the workspace a step needs,
  * *num_splits_out = the chosen split count.  Host-only.
  */
@@ -140,7 +141,8 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
  *   workspace      device memory of at least the planned size, 256-byte
  *                  aligned, initialised once by mi355x_gated_attn_workspace_init.
  *                  Layout after a step: bytes [0, B*L*Hq*D) hold q as e4m3
- *                  [B*L, Hq, D]; then split partials and B int32 counters.
+ *                  [B*L, Hq, D]; then split partials and B*G int32
+ *                  counters, G = ceil(L / 4) token groups per request.
  * Calls that share a workspace, or write the same cache rows, must be ordered
  * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
  */

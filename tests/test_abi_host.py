@@ -90,7 +90,7 @@ def test_prepare_plan_workspace_layout(L):
         po = -(-q // 256) * 256
         pml = -(-(po + s * T * 16 * 64 * 4) // 256) * 256
         cnt = -(-(pml + s * T * 16 * 2 * 4) // 256) * 256
-        assert ws == -(-(cnt + 32 * 4) // 256) * 256
+        assert ws == -(-(cnt + 32 * 2 * 4) // 256) * 256  # two token groups of 4 per request
         ws0, s0 = ga.mi355x_gated_attn_plan(ctx, 32776, 0)
         assert 1 <= s0 <= 256
         with pytest.raises(ga.GatedAttnError):
@@ -102,7 +102,7 @@ def test_prepare_plan_workspace_layout(L):
 
 
 def test_auto_split_count_fills_the_chip(L):
-    """Automatic plans: about two work units per compute unit, at least one
+    """Automatic plans: about one work unit per compute unit, at least one
     32-key block per wave, never more than 256 splits."""
     cases = [(1, 1, 0, 513), (32, 1, 2048, 16385), (64, 1, 0, 32769), (32, 8, 2048, 32776),
              (8, 8, 0, 131080)]
@@ -113,7 +113,8 @@ def test_auto_split_count_fills_the_chip(L):
             keys = min(ctxlen, W + Lq - 1) if W else ctxlen
             assert s <= max(1, -(-keys // 128))
             assert s <= 256
-            assert B * s <= (512 if Lq <= 2 else 256) + B
+            groups = B * -(-Lq // 4)  # work units per split
+            assert groups * s <= 256 + groups
         finally:
             ga.mi355x_gated_attn_destroy(ctx)
 
@@ -200,5 +201,17 @@ def test_timing_hook_without_steps(L):
         ga.mi355x_gated_attn_timing(ctx, True)
         ms, n = ga.mi355x_gated_attn_timing_read(ctx)
         assert n == 0 and ms == 0.0
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_plan_rejects_a_launch_beyond_the_grid_limit(L):
+    """B * token groups * splits workgroups must fit one launch (2^31 - 1)."""
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=1 << 28, q_len=8))
+    try:
+        ga.mi355x_gated_attn_plan(ctx, 1000, 3)  # 2^28 * 2 * 3 < 2^31
+        with pytest.raises(ga.GatedAttnError) as e:
+            ga.mi355x_gated_attn_plan(ctx, 1000, 4)  # 2^28 * 2 * 4 = 2^31
+        assert e.value.status == ga.MI355X_GA_UNSUPPORTED
     finally:
         ga.mi355x_gated_attn_destroy(ctx)
