@@ -35,29 +35,25 @@ __device__ inline uint32_t e4m3x2(float a, float b) {
   return w;
 }
 
-// Correctly rounded fp32 1/sqrt(a) for finite a > 0: the hardware estimate is
-// within two fp32 steps; each neighbour midpoint m (25 significant bits, m*m
-// exact in fp64) is tested exactly through the sign of fma(m*m, a, -1).
+// Correctly rounded fp32 1/sqrt(a) for finite a > 0.  The hardware estimate y
+// is within two fp32 steps of the true value t; the result is y moved by one
+// step for each of the four midpoints between y-2..y+2 that t lies beyond.
+// Each midpoint m has 25 significant bits, so m*m is exact in fp64 and the
+// sign of fma(m*m, a, -1) tells exactly whether t > m (negative) or t < m.
 __device__ inline float rsqrt_exact(float a) {
-  float y = __builtin_amdgcn_rsqf(a);
-#pragma unroll
-  for (int it = 0; it < 3; ++it) {
-    const uint32_t yb = __float_as_uint(y);
-    const float up = __uint_as_float(yb + 1u);
-    const double mu = ((double)y + (double)up) * 0.5;
-    if (fma(mu * mu, (double)a, -1.0) < 0.0) {
-      y = up;
-      continue;
-    }
-    const float dn = __uint_as_float(yb - 1u);
-    const double md = ((double)y + (double)dn) * 0.5;
-    if (fma(md * md, (double)a, -1.0) > 0.0) {
-      y = dn;
-      continue;
-    }
-    break;
-  }
-  return y;
+  const float y = __builtin_amdgcn_rsqf(a);
+  const uint32_t yb = __float_as_uint(y);
+  const double ad = (double)a;
+  auto side = [&](uint32_t lo) {  // fma(m*m, a, -1) for m between lo and lo + 1
+    const double m = ((double)__uint_as_float(lo) + (double)__uint_as_float(lo + 1u)) * 0.5;
+    return fma(m * m, ad, -1.0);
+  };
+  int step = 0;
+  step += side(yb) < 0.0;           // t above the midpoint y | y+1
+  step += side(yb + 1u) < 0.0;      // t above y+1 | y+2
+  step -= side(yb - 1u) > 0.0;      // t below y-1 | y
+  step -= side(yb - 2u) > 0.0;      // t below y-2 | y-1
+  return __uint_as_float(yb + (uint32_t)step);
 }
 
 }  // namespace mi355x_ga

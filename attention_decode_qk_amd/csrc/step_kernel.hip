@@ -726,7 +726,10 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   // stores of the group's real tokens are kept.
 #pragma unroll
   for (int ti = 0; ti < LU; ++ti) {
-    const float inv = lrun[ti] > 0.0f ? vs / lrun[ti] : 0.0f;
+    // Output-side arithmetic runs in fp32 on the hardware reciprocal, rsqrt and
+    // exp (each within a couple of fp32 ulps); the result is rounded to bf16
+    // (2^-9 relative) once at the end.
+    const float inv = lrun[ti] > 0.0f ? vs * __builtin_amdgcn_rcpf(lrun[ti]) : 0.0f;
     float y[4];
     float ss = 0.0f;
 #pragma unroll
@@ -735,12 +738,12 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       ss += y[c] * y[c];
     }
     ss = sum16(ss);
-    const float r = (float)(1.0 / sqrt((double)ss / 64.0 + 1.0e-5));
+    const float r = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + 1.0e-5f);
     const float gate[4] = {bf16_value(graw[ti].x & 0xffffu), bf16_value(graw[ti].x >> 16),
                            bf16_value(graw[ti].y & 0xffffu), bf16_value(graw[ti].y >> 16)};
     uint32_t ob[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * (1.0f / (1.0f + __expf(-gate[c]))));
+    for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[c])));
     if (ti < t_n)
       *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
           make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
