@@ -259,35 +259,17 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   const int kItems = kQItems + L * 2 * kKvHeads * 8;
 
   // ---------------- A. geometry and early loads ----------------
+  // The chain cache_seqlens -> page table -> K/V rows bounds the step's
+  // latency, so the first two blocks' page-table entries are requested before
+  // any load off that chain: vector memory counters complete in order, and a
+  // slower load issued earlier (a cold projection row) would hold up the wait
+  // for the page table.  The other small loads follow, then the K/V loads.
   const int cs = p.cache_seqlens[b];
-  const uint16_t* qkv_b = p.qkv + tok0 * kWidth;
-  // Item -> (request-local token, head row, 8-column slice): q rows of the
-  // group's tokens first, then the K and V rows of every token.
-  auto item_token = [&](int item) {
-    return item < kQItems ? t_lo + (item >> 7) : (item - kQItems) >> 5;
-  };
-  auto item_row = [&](int item) {
-    return item < kQItems ? (item >> 3) & (kQHeads - 1) : kQHeads + (((item - kQItems) >> 3) & 3);
-  };
-  uint4 xv[kItemIters];
-#pragma unroll
-  for (int it = 0; it < kItemIters; ++it) {
-    const int item = tid + 256 * it;
-    xv[it] = make_uint4(0, 0, 0, 0);
-    if (item < kItems && item_token(item) < L)
-      xv[it] = *reinterpret_cast<const uint4*>(qkv_b + item_token(item) * kWidth +
-                                                item_row(item) * kHeadDim + (item & 7) * 8);
-  }
-  const bool cs_thread = p.rope && tid < 32 * L;
-  int64_t my_slot = p.cache_loc[tok0 + min(tid, L - 1)];
-  float my_ang = p.rope ? (float)p.positions[tok0 + min(tid >> 5, L - 1)] * p.inv_freq[tid & 31] : 0.0f;
-  float ks = p.scaled ? *p.k_scale : 1.0f;
-  float vs = p.scaled ? *p.v_scale : 1.0f;
-  // Take these small values now, while waiting for cache_seqlens anyway: a load
-  // left for later would be consumed after the K/V loads, and since vector
-  // memory counters complete in order, waiting for it would wait for them too.
-  asm volatile("" : "+v"(my_ang), "+v"(ks), "+v"(vs), "+v"(my_slot));
-
+  // The cache scales: tiny, shared by every unit, issued with cache_seqlens so
+  // that every path reaches the page-table wait with the same loads in flight.
+  const float ks = p.scaled ? *p.k_scale : 1.0f;
+  const float vs = p.scaled ? *p.v_scale : 1.0f;
+  asm volatile("" ::: "memory");
   const int p0 = cs - L;  // key index (position) of the request's first new token
   const int last = cs - 1;
   const int first = p.window > 0 ? max(0, p0 - p.window + 1) : 0;
@@ -313,15 +295,50 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   auto load_pte = [&](int i) { return make_int2(page_entry(p, pt, k_key(i)), page_entry(p, pt, v_key(i))); };
   auto load_block = [&](int2 e, int i) { return load_kv(p, e, k_key(i), v_key(i), j, q4); };
 
-  // Issue order matters (vector memory counters complete in order): each block's
-  // page-table load follows the K/V loads two blocks earlier, so waiting for it
-  // never waits for the next block's K/V.
   const int2 pte0 = load_pte(0);
   const int2 pte1 = load_pte(1);
+  asm volatile("" ::: "memory");  // the loads below stay behind the page-table loads
+
+  const uint16_t* qkv_b = p.qkv + tok0 * kWidth;
+  // Item -> (request-local token, head row, 8-column slice): q rows of the
+  // group's tokens first, then the K and V rows of every token.
+  auto item_token = [&](int item) {
+    return item < kQItems ? t_lo + (item >> 7) : (item - kQItems) >> 5;
+  };
+  auto item_row = [&](int item) {
+    return item < kQItems ? (item >> 3) & (kQHeads - 1) : kQHeads + (((item - kQItems) >> 3) & 3);
+  };
+  // Unconditional loads (slots past the items read a valid row and are never
+  // used): a load skipped on some path would leave the compiler's memory-counter
+  // waits counting for the longest path, and the page-table wait would then
+  // also wait for a projection row.
+  uint4 xv[kItemIters];
+#pragma unroll
+  for (int it = 0; it < kItemIters; ++it) {
+    const int item = min(tid + 256 * it, kItems - 1);
+    xv[it] = *reinterpret_cast<const uint4*>(qkv_b + min(item_token(item), L - 1) * kWidth +
+                                              item_row(item) * kHeadDim + (item & 7) * 8);
+  }
+  const bool cs_thread = p.rope && tid < 32 * L;
+  int64_t my_slot = p.cache_loc[tok0 + min(tid, L - 1)];
+  // Raw position and frequency now; the angle (which waits for them) after the
+  // K/V loads.  Without RoPE, positions may be absent: read a cache row index
+  // instead (same type, always present) and ignore it.
+  const int64_t* pos_src = p.rope ? p.positions : p.cache_loc;
+  int64_t my_pos = pos_src[tok0 + min(tid >> 5, L - 1)];
+  float my_freq = p.inv_freq[tid & 31];
+  asm volatile("" ::: "memory");  // ... and ahead of the K/V loads, so waiting for them never waits for K/V
+
+  // Each block's page-table load follows the K/V loads two blocks earlier, so
+  // waiting for it never waits for the next block's K/V.
   KvBlock bufA = load_block(pte0, 0);
   int2 pa = load_pte(2);
   KvBlock bufB = load_block(pte1, 1);
   int2 pb = load_pte(3);
+  // The small values are taken only now (the compiler would otherwise move
+  // them, uniform ones into scalar registers, right after their loads, and
+  // that wait would also wait for the page table's slower neighbours).
+  asm volatile("" : "+v"(my_pos), "+v"(my_freq), "+v"(my_slot));
 
   // New token i's K/V codes are needed by the units whose chunk holds its key
   // (one per token group); the group-0 one stores them.  A key with no place in
@@ -333,6 +350,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // RoPE table for the request's tokens: (token, frequency) per thread.
   if (cs_thread) {
+    const float my_ang = (float)my_pos * my_freq;
     double sd, cd;
     sincos((double)my_ang, &sd, &cd);
     s_cs[tid >> 5][tid & 31][0] = (float)cd;
