@@ -21,11 +21,24 @@ constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
 // Work unit = (request, token group, split): a workgroup of kAttnWaves waves
 // walks the split's key chunk in blocks of kKeyBlock keys, one block per wave
 // at a time, for the query rows of the group's tokens.  A request's q_len
-// tokens form token_groups(q_len) groups of consecutive tokens.
+// tokens form G groups of consecutive tokens, G = ceil(q_len / 4) or, for short
+// key ranges, ceil(q_len / 2) (the plan's choice); a unit carries
+// ceil(q_len / G) tokens.
 constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
 constexpr int kMaxTokensPerUnit = 4;
-inline int token_groups(int q_len) { return (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit; }
+constexpr int token_groups(int q_len, bool short_keys) {
+  return short_keys ? (q_len + 1) / 2 : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit;
+}
+constexpr int tokens_per_unit(int q_len, int groups) { return (q_len + groups - 1) / groups; }
+// The longest q_len served by units of lu tokens under either grouping (0 if none).
+constexpr int max_q_len_for(int lu) {
+  int m = 0;
+  for (int l = 1; l <= kMaxQLen; ++l)
+    if (tokens_per_unit(l, token_groups(l, false)) == lu || tokens_per_unit(l, token_groups(l, true)) == lu)
+      m = l;
+  return m;
+}
 
 struct StepParams {
   const uint16_t* qkv;           // bf16 [T, kWidth]
@@ -46,7 +59,7 @@ struct StepParams {
   int64_t num_rows;              // num_pages * page_size (< 2^31)
   int32_t batch;
   int32_t q_len;                 // L
-  int32_t tgroups;               // G = token_groups(L), 1 or 2
+  int32_t tgroups;               // G: token_groups(L, short or not)
   int32_t splits;                // S
   int32_t max_pages;
   int32_t page_size;

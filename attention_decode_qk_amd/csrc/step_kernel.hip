@@ -230,7 +230,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   // attends its group's query rows over chunk kc of the request's keys.
   constexpr int NRB = (LU * kGroup + 15) / 16;  // 16-row blocks per KV head
   constexpr int kQItems = LU * kQHeads * 8;     // (token, q head, 8-column slice)
-  constexpr int kMaxItems = kQItems + 2 * LU * 2 * kKvHeads * 8;  // + K/V rows of <= 2*LU tokens
+  constexpr int kMaxL = max_q_len_for(LU);
+  static_assert(kMaxL >= LU, "no q_len is served by this unit size");
+  constexpr int kMaxItems = kQItems + kMaxL * 2 * kKvHeads * 8;  // + K/V rows of every token
   constexpr int kItemIters = (kMaxItems + 255) / 256;
   constexpr int kRows = LU * kQHeads;           // partial rows of a unit
   __shared__ __align__(16) uint8_t s_q[LU][kQHeads][kHeadDim];
@@ -241,8 +243,8 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   __shared__ __align__(16) float s_ml[kAttnWaves][kRows][2];
   __shared__ int s_last;
 
-  // q_len 1 and 2 are the only lengths served by LU = 1 and 2 (one group).
-  constexpr bool kOneGroup = LU <= 2;
+  // A unit size that serves a single q_len (LU = 1: q_len 1) serves it as one group.
+  constexpr bool kOneGroup = kMaxL == LU;
   const int L = kOneGroup ? LU : p.q_len;
   const int kc = blockIdx.x % p.splits;
   const int bt = blockIdx.x / p.splits;
@@ -776,6 +778,12 @@ hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int LU>
+hipError_t launch_served(const StepParams& p, hipStream_t stream) {
+  if constexpr (max_q_len_for(LU) >= LU) return launch_lu<LU>(p, stream);
+  return hipErrorInvalidValue;
+}
+
 __global__ void zero_counters_kernel(int32_t* c, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) c[i] = 0;
@@ -785,13 +793,15 @@ __global__ void zero_counters_kernel(int32_t* c, int n) {
 
 hipError_t launch_step(const StepParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
-  if (p.q_len < 1 || p.q_len > kMaxQLen || p.tgroups < 1 || p.tgroups > 2) return hipErrorInvalidValue;
-  const int lu = (p.q_len + p.tgroups - 1) / p.tgroups;  // tokens per unit
+  if (p.q_len < 1 || p.q_len > kMaxQLen ||
+      (p.tgroups != token_groups(p.q_len, false) && p.tgroups != token_groups(p.q_len, true)))
+    return hipErrorInvalidValue;
+  const int lu = tokens_per_unit(p.q_len, p.tgroups);
   switch (lu) {
-    case 1: return launch_lu<1>(p, stream);
-    case 2: return launch_lu<2>(p, stream);
-    case 3: return launch_lu<3>(p, stream);
-    case 4: return launch_lu<4>(p, stream);
+    case 1: return launch_served<1>(p, stream);
+    case 2: return launch_served<2>(p, stream);
+    case 3: return launch_served<3>(p, stream);
+    case 4: return launch_served<4>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

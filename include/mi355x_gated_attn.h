@@ -94,7 +94,10 @@ int mi355x_gated_attn_prepare(const mi355x_gated_attn_config* cfg, int device,
  * metadata and its split-count heuristic.  max_context bounds
  * cache_seqlens[b] (keys per request including the new tokens) and only steers
  * the split count; num_splits > 0 forces the count (1..256), 0 chooses it.
- * A step launches B * ceil(L/4) * splits workgroups (UNSUPPORTED beyond 2^31-1).
+ * The plan also groups each request's L tokens into G token groups, one work
+ * unit per (request, group, split): G = ceil(L/2) when the key range (the
+ * window + L - 1, or max_context) is at most 4096 keys, else ceil(L/4).  A step
+ * launches B * G * splits workgroups (UNSUPPORTED beyond 2^31-1).
  * Outputs (either may be NULL): *workspace_bytes = the workspace a step needs,
  * *num_splits_out = the chosen split count.  Host-only.
  */
@@ -142,7 +145,7 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
  *                  aligned, initialised once by mi355x_gated_attn_workspace_init.
  *                  Layout after a step: bytes [0, B*L*Hq*D) hold q as e4m3
  *                  [B*L, Hq, D]; then split partials and B*G int32
- *                  counters, G = ceil(L / 4) token groups per request.
+ *                  counters (G token groups per request, from the plan).
  * Calls that share a workspace, or write the same cache rows, must be ordered
  * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
  */
