@@ -48,6 +48,21 @@ def test_small_case_matches_oracle(name):
     check_full(x, res, Reference(x), name)
 
 
+@pytest.mark.parametrize("q_len", range(1, 9))
+@pytest.mark.parametrize("grouping", ["short", "long"])
+def test_every_q_len_under_both_token_groupings(q_len, grouping):
+    """Every q_len with the plan's two token groupings: a short key bound makes
+    ceil(L/2) groups of at most two tokens, a long one ceil(L/4) groups of at
+    most four (plan(); with the long bound most splits are empty here)."""
+    w = synth.small(name="groups", batch=3, q_len=q_len, window=0 if grouping == "long" else 96,
+                    rope_theta=500000.0, seq_lo=30, seq_hi=400, page_size=4)
+    x = synth.make_inputs(w, seed=300 + q_len)
+    bound = 100000 if grouping == "long" else None
+    _say(f"[gpu] groups {grouping}: L={q_len}")
+    res = run_gpu(x, ctx_bound=bound)
+    check_full(x, res, Reference(x), f"groups {grouping} L={q_len}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
 def test_split_count_invariance(splits):
     """Any split count gives oracle-level results (partials merge exactly in form)."""
