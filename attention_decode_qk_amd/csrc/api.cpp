@@ -53,6 +53,7 @@ constexpr int64_t kShortKeys = 4096;  // key ranges up to this use groups of two
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+
 }  // namespace
 
 struct mi355x_gated_attn_ctx {
@@ -62,6 +63,7 @@ struct mi355x_gated_attn_ctx {
   bool planned = false;
   int32_t splits = 0;
   int32_t groups = 1;  // token groups per request
+  bool head_split = false;
   size_t q_bytes = 0, po_off = 0, pml_off = 0, cnt_off = 0, ws_bytes = 0;
   bool timing = false;
   std::vector<hipEvent_t> events;  // 2 per timed step, reused
@@ -168,6 +170,13 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   // W = 2048): 20.5 us with groups of two, 22.7 with four; (B = 8, L = 8, 64k-128k
   // keys): 116 us with two, 97 with four.
   const int groups = token_groups(c.q_len, keys <= kShortKeys);
+  // Eight waves per unit (one KV head each, two waves per SIMD) pay where the
+  // key loop is short and compute-heavy (q_len > 1 over a short key range:
+  // 19.2 against 20.7 us at B = 32, L = 8, W = 2048).  Elsewhere the two halves
+  // of a cache row, fetched by different waves, cost HBM efficiency (B = 64,
+  // L = 1, 32k keys: 160 against 113 us; B = 32, L = 1, W = 2048: 13.0 against
+  // 12.5 us), so four waves keep both heads.
+  const bool head_split = keys <= kShortKeys && c.q_len > 1;
   int32_t s = num_splits;
   if (s == 0) {
     const int64_t min_keys_per_split = (int64_t)kAttnWaves * kKeyBlock;  // a block per wave
@@ -189,6 +198,7 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
   ctx->splits = s;
   ctx->groups = groups;
+  ctx->head_split = head_split;
   ctx->planned = true;
   if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
   if (num_splits_out) *num_splits_out = s;
@@ -261,6 +271,7 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   sp.q_len = c.q_len;
   sp.tgroups = ctx->groups;
   sp.splits = ctx->splits;
+  sp.head_split = ctx->head_split ? 1 : 0;
   sp.max_pages = c.max_pages;
   sp.page_size = c.page_size;
   sp.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;

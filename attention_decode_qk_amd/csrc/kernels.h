@@ -61,6 +61,7 @@ struct StepParams {
   int32_t q_len;                 // L
   int32_t tgroups;               // G: token_groups(L, short or not)
   int32_t splits;                // S
+  int32_t head_split;            // 1: eight waves per unit, one KV head each
   int32_t max_pages;
   int32_t page_size;
   int32_t page_shift;            // log2(page_size) if a power of two, else -1

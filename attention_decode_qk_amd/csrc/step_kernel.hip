@@ -144,9 +144,11 @@ __device__ inline int key_row(const StepParams& p, int entry, int key) {
 // kept in flight across the prologue.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// K/V operands of one 32-key block for NG KV heads starting at head g0.
+template <int NG>
 struct KvBlock {
-  uint4 k[2][kKvHeads];      // lane (q4, j): 16 bytes of key 16t+j, both KV heads
-  uint32_t v[kKvHeads][8];   // lane (q4, j): columns 4j..4j+3 of keys 16(r/4)+4q4+r%4
+  uint4 k[2][NG];      // lane (q4, j): 16 bytes of key 16t+j per head
+  uint32_t v[NG][8];   // lane (q4, j): columns 4j..4j+3 of keys 16(r/4)+4q4+r%4 per head
 };
 
 // Offset in a 32-key block of the key whose page-table entry lane l fetches for
@@ -159,18 +161,20 @@ __device__ inline int v_key_offset(int lane) {
 // `kk`, `kv`: this lane's keys and page-table entries for the K operand (block
 // base + lane % 32) and the V operand (block base + v_key_offset), clamped.
 // Rows reach the lanes that read them by lane swaps and row broadcasts.
-__device__ inline KvBlock load_kv(const StepParams& p, int2 entry, int kk, int kv, int j, int q4) {
+template <int NG>
+__device__ inline KvBlock<NG> load_kv(const StepParams& p, int2 entry, int kk, int kv, int g0, int j,
+                                      int q4) {
   const int krow = key_row(p, entry.x, kk);
   const int vrow = key_row(p, entry.y, kv);
   // Lanes 32..63 repeat lanes 0..31, so the 16-row swap leaves row 0's rows
   // (keys 0..15) in a[0] and row 1's (keys 16..31) in a[1], in every row.
   const auto a = __builtin_amdgcn_permlane16_swap((unsigned)krow, (unsigned)krow, false, false);
-  KvBlock d;
+  KvBlock<NG> d;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const uint8_t* kr = p.k_cache + (int64_t)(int)a[t] * kRowBytes + 16 * q4;
-    d.k[t][0] = *reinterpret_cast<const uint4*>(kr);
-    d.k[t][1] = *reinterpret_cast<const uint4*>(kr + kHeadDim);
+    const uint8_t* kr = p.k_cache + (int64_t)(int)a[t] * kRowBytes + g0 * kHeadDim + 16 * q4;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) d.k[t][g] = *reinterpret_cast<const uint4*>(kr + g * kHeadDim);
   }
   int vr[8];
   vr[0] = dpp<kDppRowBcast + 0>(vrow);
@@ -183,9 +187,9 @@ __device__ inline KvBlock load_kv(const StepParams& p, int2 entry, int kk, int k
   vr[7] = dpp<kDppRowBcast + 7>(vrow);
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
-    const uint8_t* vp = p.v_cache + (int64_t)vr[r] * kRowBytes + 4 * j;
-    d.v[0][r] = *reinterpret_cast<const uint32_t*>(vp);
-    d.v[1][r] = *reinterpret_cast<const uint32_t*>(vp + kHeadDim);
+    const uint8_t* vp = p.v_cache + (int64_t)vr[r] * kRowBytes + g0 * kHeadDim + 4 * j;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) d.v[g][r] = *reinterpret_cast<const uint32_t*>(vp + g * kHeadDim);
   }
   return d;
 }
@@ -223,17 +227,24 @@ __device__ inline uint2 pack_e4m3x8(const float (&y)[8]) {
   return make_uint2(lo, hi);
 }
 
-template <int LU>
-__global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
+template <int LU, bool HS>
+__global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p) {
   // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
   // LU consecutive tokens; the unit (request b, token group tg, key chunk kc)
   // attends its group's query rows over chunk kc of the request's keys.
+  // HS (head split): eight waves, four per KV head, each wave working on one
+  // head's rows (two waves per SIMD); otherwise four waves working on both.
+  // Either way the four waves of a head take the chunk's 32-key blocks
+  // round-robin.
+  constexpr int NG = HS ? 1 : kKvHeads;           // KV heads a wave works on
+  constexpr int kWaves = HS ? 2 * kAttnWaves : kAttnWaves;
+  constexpr int kThreads = 64 * kWaves;
   constexpr int NRB = (LU * kGroup + 15) / 16;  // 16-row blocks per KV head
   constexpr int kQItems = LU * kQHeads * 8;     // (token, q head, 8-column slice)
   constexpr int kMaxL = max_q_len_for(LU);
   static_assert(kMaxL >= LU, "no q_len is served by this unit size");
   constexpr int kMaxItems = kQItems + kMaxL * 2 * kKvHeads * 8;  // + K/V rows of every token
-  constexpr int kItemIters = (kMaxItems + 255) / 256;
+  constexpr int kItemIters = (kMaxItems + kThreads - 1) / kThreads;
   constexpr int kRows = LU * kQHeads;           // partial rows of a unit
   __shared__ __align__(16) uint8_t s_q[LU][kQHeads][kHeadDim];
   __shared__ __align__(16) uint8_t s_newk[kMaxQLen][kRowBytes];
@@ -255,6 +266,8 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int kw = wave % kAttnWaves;            // this wave's place among its head's waves
+  const int g0 = HS ? wave / kAttnWaves : 0;   // first KV head this wave works on
   const int j = lane & 15;
   const int q4 = lane >> 4;
   const int64_t tok0 = (int64_t)b * L;
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   const int start = first + kc * chunk;
   const int end = min(start + chunk, last + 1);
   const int nblk = end > start ? (end - start + kKeyBlock - 1) / kKeyBlock : 0;
-  const int nb = nblk > wave ? (nblk - wave + kAttnWaves - 1) / kAttnWaves : 0;  // this wave's
+  const int nb = nblk > kw ? (nblk - kw + kAttnWaves - 1) / kAttnWaves : 0;  // this wave's
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
   // Key of this lane in the wave's block i.  Blocks past the wave's last are
   // clamped to it, so the pipeline's loads are unconditional (which keeps the
@@ -290,12 +303,12 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   const int voff = v_key_offset(lane);
   auto block_key = [&](int i, int off) {
     const int blk = min(i, max(nb - 1, 0));
-    return max(0, min(start + (wave + kAttnWaves * blk) * kKeyBlock + off, end - 1));
+    return max(0, min(start + (kw + kAttnWaves * blk) * kKeyBlock + off, end - 1));
   };
   auto k_key = [&](int i) { return block_key(i, lane & 31); };
   auto v_key = [&](int i) { return block_key(i, voff); };
   auto load_pte = [&](int i) { return make_int2(page_entry(p, pt, k_key(i)), page_entry(p, pt, v_key(i))); };
-  auto load_block = [&](int2 e, int i) { return load_kv(p, e, k_key(i), v_key(i), j, q4); };
+  auto load_block = [&](int2 e, int i) { return load_kv<NG>(p, e, k_key(i), v_key(i), g0, j, q4); };
 
   const int2 pte0 = load_pte(0);
   const int2 pte1 = load_pte(1);
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   uint4 xv[kItemIters];
 #pragma unroll
   for (int it = 0; it < kItemIters; ++it) {
-    const int item = min(tid + 256 * it, kItems - 1);
+    const int item = min(tid + kThreads * it, kItems - 1);
     xv[it] = *reinterpret_cast<const uint4*>(qkv_b + min(item_token(item), L - 1) * kWidth +
                                               item_row(item) * kHeadDim + (item & 7) * 8);
   }
@@ -333,9 +346,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // Each block's page-table load follows the K/V loads two blocks earlier, so
   // waiting for it never waits for the next block's K/V.
-  KvBlock bufA = load_block(pte0, 0);
+  KvBlock<NG> bufA = load_block(pte0, 0);
   int2 pa = load_pte(2);
-  KvBlock bufB = load_block(pte1, 1);
+  KvBlock<NG> bufB = load_block(pte1, 1);
   int2 pb = load_pte(3);
   // The small values are taken only now (the compiler would otherwise move
   // them, uniform ones into scalar registers, right after their loads, and
@@ -362,7 +375,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
 #pragma unroll
   for (int it = 0; it < kItemIters; ++it) {
-    const int item = tid + 256 * it;
+    const int item = tid + kThreads * it;
     const int i = min(item_token(item), L - 1);
     const int hr = item_row(item), c8 = item & 7;
     const bool is_q = item < kQItems;
@@ -412,7 +425,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // q operands and per-row visible ranges.  Row r = 16*rb + j of KV head g is
   // the group's token r / 8, query head 8g + r % 8.
-  long qop[kKvHeads][NRB][2];
+  long qop[NG][NRB][2];
   int rlo[NRB], rhi[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
@@ -423,8 +436,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
     rlo[rb] = valid ? (p.window > 0 ? max(0, pi - p.window + 1) : 0) : 1;
     rhi[rb] = valid ? pi : 0;
 #pragma unroll
-    for (int g = 0; g < kKvHeads; ++g) {
-      const uint4 qv = *reinterpret_cast<const uint4*>(&s_q[min(ti, LU - 1)][g * kGroup + (r & 7)][16 * q4]);
+    for (int g = 0; g < NG; ++g) {
+      const uint4 qv =
+          *reinterpret_cast<const uint4*>(&s_q[min(ti, LU - 1)][(g0 + g) * kGroup + (r & 7)][16 * q4]);
       qop[g][rb][0] = valid ? as_long(qv.x, qv.y) : 0;
       qop[g][rb][1] = valid ? as_long(qv.z, qv.w) : 0;
     }
@@ -434,10 +448,10 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   const int hi_all = min(p0 + t_lo, end - 1);
   const float scale = p.sm_scale_log2 * ks;
 
-  float mrow[kKvHeads][NRB], lrow[kKvHeads][NRB];
-  v4f acc[kKvHeads][NRB][4];
+  float mrow[NG][NRB], lrow[NG][NRB];
+  v4f acc[NG][NRB][4];
 #pragma unroll
-  for (int g = 0; g < kKvHeads; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       mrow[g][rb] = -INFINITY;
@@ -448,7 +462,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // ---------------- B. key loop ----------------
   // New keys' codes replace the cache bytes of a block that holds them.
-  auto substitute = [&](KvBlock& d, const int kbase) {
+  auto substitute = [&](KvBlock<NG>& d, const int kbase) {
     if (kbase + kKeyBlock - 1 < p0) return;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -456,8 +470,8 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       const int i = min(max(key - p0, 0), L - 1);
       const bool nk = key >= p0;
 #pragma unroll
-      for (int g = 0; g < kKvHeads; ++g) {
-        const uint4 nv = *reinterpret_cast<const uint4*>(&s_newk[i][g * kHeadDim + 16 * q4]);
+      for (int g = 0; g < NG; ++g) {
+        const uint4 nv = *reinterpret_cast<const uint4*>(&s_newk[i][(g0 + g) * kHeadDim + 16 * q4]);
         d.k[t][g].x = nk ? nv.x : d.k[t][g].x;
         d.k[t][g].y = nk ? nv.y : d.k[t][g].y;
         d.k[t][g].z = nk ? nv.z : d.k[t][g].z;
@@ -470,8 +484,8 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       const int i = min(max(key - p0, 0), L - 1);
       const bool nk = key >= p0;
 #pragma unroll
-      for (int g = 0; g < kKvHeads; ++g) {
-        const uint32_t nv = *reinterpret_cast<const uint32_t*>(&s_newv[i][g * kHeadDim + 4 * j]);
+      for (int g = 0; g < NG; ++g) {
+        const uint32_t nv = *reinterpret_cast<const uint32_t*>(&s_newv[i][(g0 + g) * kHeadDim + 4 * j]);
         d.v[g][r] = nk ? nv : d.v[g][r];
       }
     }
@@ -479,9 +493,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // V^T operand: per KV head and column c (of the lane's 4), the 8 keys as f16
   // pairs; perm gathers byte c (and c+1) of two key rows.
-  auto v_operand = [&](const KvBlock& d, v8h (&va)[kKvHeads][4]) {
+  auto v_operand = [&](const KvBlock<NG>& d, v8h (&va)[NG][4]) {
 #pragma unroll
-    for (int g = 0; g < kKvHeads; ++g) {
+    for (int g = 0; g < NG; ++g) {
 #pragma unroll
       for (int rp = 0; rp < 4; ++rp) {
         const uint32_t lo = __builtin_amdgcn_perm(d.v[g][2 * rp + 1], d.v[g][2 * rp], 0x05010400u);
@@ -504,9 +518,9 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // Raw q.k of one block for every row block: lane (q4, j) gets keys
   // 16t + 4q4 + i (slot 4t + i) of row j.
-  auto qk = [&](const KvBlock& d, float (&z)[kKvHeads][NRB][8]) {
+  auto qk = [&](const KvBlock<NG>& d, float (&z)[NG][NRB][8]) {
 #pragma unroll
-    for (int g = 0; g < kKvHeads; ++g)
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
@@ -522,7 +536,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   };
 
   // Invisible keys (outside the chunk or a row's window) get a -inf score.
-  auto mask = [&](const int kbase, float (&z)[kKvHeads][NRB][8]) {
+  auto mask = [&](const int kbase, float (&z)[NG][NRB][8]) {
     if (kbase >= lo_all && kbase + kKeyBlock - 1 <= hi_all) return;  // visible to every row
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -531,7 +545,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
       for (int rb = 0; rb < NRB; ++rb) {
         const bool vis = key < end && key >= rlo[rb] && key <= rhi[rb];
 #pragma unroll
-        for (int g = 0; g < kKvHeads; ++g) z[g][rb][k] = vis ? z[g][rb][k] : -INFINITY;
+        for (int g = 0; g < NG; ++g) z[g][rb][k] = vis ? z[g][rb][k] : -INFINITY;
       }
     }
   };
@@ -543,14 +557,14 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   for (int bi = 0; bi < nb; bi += 2) {
     const bool has_b = bi + 1 < nb;
     // An absent second block sits past the chunk: every key masked, no codes substituted.
-    const int kb0 = start + (wave + kAttnWaves * bi) * kKeyBlock;
+    const int kb0 = start + (kw + kAttnWaves * bi) * kKeyBlock;
     const int kb1 = has_b ? kb0 + kAttnWaves * kKeyBlock : end;
     substitute(bufA, kb0);
     if (has_b) substitute(bufB, kb1);
-    float z0[kKvHeads][NRB][8], z1[kKvHeads][NRB][8];
+    float z0[NG][NRB][8], z1[NG][NRB][8];
     qk(bufA, z0);
     qk(bufB, z1);
-    v8h va0[kKvHeads][4], va1[kKvHeads][4];
+    v8h va0[NG][4], va1[NG][4];
     v_operand(bufA, va0);
     v_operand(bufB, va1);
     bufA = load_block(pa, bi + 2);
@@ -560,7 +574,7 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
     mask(kb0, z0);
     mask(kb1, z1);
 #pragma unroll
-    for (int g = 0; g < kKvHeads; ++g) {
+    for (int g = 0; g < NG; ++g) {
       float lmx[NRB];     // this lane's scaled maximum over its 16 keys of the pair
       bool grow = false;  // some lane's maximum passes its row's lazy bound
 #pragma unroll
@@ -613,34 +627,33 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
 
   // Row sums: each lane summed its own keys; add the four lane groups of a row.
 #pragma unroll
-  for (int g = 0; g < kKvHeads; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      lrow[g][rb] = rows_sum(lrow[g][rb]);
-    }
+    for (int rb = 0; rb < NRB; ++rb) lrow[g][rb] = rows_sum(lrow[g][rb]);
 
   // ---------------- C. merge the waves, publish the partial ----------------
-  // Every wave parks (m, l, o) of its valid rows in its LDS slot (compact row
-  // ti*16 + h for the group's token ti); after one barrier all 256 threads merge
-  // 4 columns of a row each and publish the unit's partial.
+  // Every wave parks (m, l, o) of its valid rows in the LDS slot of its place
+  // among its head's waves (compact row ti*16 + h for the group's token ti);
+  // after one barrier all threads merge 4 columns of a row each and publish the
+  // unit's partial.
 #pragma unroll
-  for (int g = 0; g < kKvHeads; ++g)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int r = 16 * rb + j;
       const int ti = r >> 3;
       if (ti >= t_n) continue;
-      const int cr = ti * kQHeads + g * kGroup + (r & 7);
+      const int cr = ti * kQHeads + (g0 + g) * kGroup + (r & 7);
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
-        *reinterpret_cast<float4*>(&s_mo[wave][cr][16 * q4 + 4 * ii]) =
+        *reinterpret_cast<float4*>(&s_mo[kw][cr][16 * q4 + 4 * ii]) =
             make_float4(acc[g][rb][0][ii], acc[g][rb][1][ii], acc[g][rb][2][ii], acc[g][rb][3][ii]);
-      if (q4 == 0) *reinterpret_cast<float2*>(&s_ml[wave][cr][0]) = make_float2(mrow[g][rb], lrow[g][rb]);
+      if (q4 == 0) *reinterpret_cast<float2*>(&s_ml[kw][cr][0]) = make_float2(mrow[g][rb], lrow[g][rb]);
     }
   lds_barrier();
   // Partial rows are ((b * splits + kc) * L + token) * 16 + head.
   const int64_t prow0 = (((int64_t)b * p.splits + kc) * L + t_lo) * kQHeads;
-  for (int idx = tid; idx < t_n * kQHeads * 16; idx += 256) {
+  for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
     const int cr = idx >> 4, c4 = (idx & 15) * 4;
     float mw[kAttnWaves], lw[kAttnWaves];
     float mx = -INFINITY;
@@ -678,89 +691,95 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   if (!s_last) return;
 
   // ---------------- D. combine + gated epilogue (last unit of the group) ----------------
-  // Thread (h, c4) takes columns c4..c4+3 of head h for every token of the
-  // group.  The partials are read KS splits at a time for all the group's
-  // tokens at once, so the chain of device-coherent round trips is
-  // ceil(splits / KS) long whatever the number of tokens.
-  constexpr int KS = LU >= 4 ? 4 : (LU == 3 ? 5 : (LU == 2 ? 8 : 16));
+  // Thread (th, h, c4) takes columns c4..c4+3 of head h for the group's tokens
+  // th, th + TS, ... (TS = threads / 256).  The partials are read KS splits at a
+  // time for all the thread's tokens at once, so the chain of device-coherent
+  // round trips is ceil(splits / KS) long whatever the number of tokens.
+  constexpr int TS = kThreads / 256;            // token stride between thread groups
+  constexpr int TPT = (LU + TS - 1) / TS;       // token slots per thread
+  constexpr int KS = TPT >= 4 ? 4 : (TPT == 3 ? 5 : (TPT == 2 ? 8 : 16));
   const int c4 = (tid & 15) * 4;
-  const int h = tid >> 4;
+  const int h = (tid >> 4) & (kQHeads - 1);
+  const int th = tid >> 8;
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
   const int64_t base = (int64_t)b * p.splits * stride + (int64_t)t_lo * kQHeads + h;
-  uint2 graw[LU];
+  uint2 graw[TPT];
 #pragma unroll
-  for (int ti = 0; ti < LU; ++ti) {
-    graw[ti] = make_uint2(0, 0);
+  for (int k = 0; k < TPT; ++k) {
+    const int ti = th + TS * k;
+    graw[k] = make_uint2(0, 0);
     if (ti < t_n)
-      graw[ti] = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + t_lo + ti) * kWidth + kGateOffset +
-                                                  h * kHeadDim + c4);
+      graw[k] = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + t_lo + ti) * kWidth + kGateOffset +
+                                                 h * kHeadDim + c4);
   }
-  float mrun[LU], lrun[LU], o[LU][4];
+  float mrun[TPT], lrun[TPT], o[TPT][4];
 #pragma unroll
-  for (int ti = 0; ti < LU; ++ti) {
-    mrun[ti] = -INFINITY;
-    lrun[ti] = 0.0f;
+  for (int k = 0; k < TPT; ++k) {
+    mrun[k] = -INFINITY;
+    lrun[k] = 0.0f;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) o[ti][c] = 0.0f;
+    for (int c = 0; c < 4; ++c) o[k][c] = 0.0f;
   }
   for (int s0 = 0; s0 < p.splits; s0 += KS) {
-    float2 ml[LU][KS], o01[LU][KS], o23[LU][KS];
+    float2 ml[TPT][KS], o01[TPT][KS], o23[TPT][KS];
 #pragma unroll
-    for (int k = 0; k < KS; ++k) {
+    for (int q = 0; q < KS; ++q) {
 #pragma unroll
-      for (int ti = 0; ti < LU; ++ti) {
-        ml[ti][k] = make_float2(-INFINITY, 0.0f);
-        o01[ti][k] = o23[ti][k] = make_float2(0.0f, 0.0f);
-        if (ti < t_n && s0 + k < p.splits) {
-          const int64_t pr = base + (int64_t)(s0 + k) * stride + ti * kQHeads;
-          ml[ti][k] = load_coherent(p.part_ml + pr * 2);
-          o01[ti][k] = load_coherent(p.part_o + pr * kHeadDim + c4);
-          o23[ti][k] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
+      for (int k = 0; k < TPT; ++k) {
+        const int ti = th + TS * k;
+        ml[k][q] = make_float2(-INFINITY, 0.0f);
+        o01[k][q] = o23[k][q] = make_float2(0.0f, 0.0f);
+        if (ti < t_n && s0 + q < p.splits) {
+          const int64_t pr = base + (int64_t)(s0 + q) * stride + ti * kQHeads;
+          ml[k][q] = load_coherent(p.part_ml + pr * 2);
+          o01[k][q] = load_coherent(p.part_o + pr * kHeadDim + c4);
+          o23[k][q] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
         }
       }
     }
 #pragma unroll
-    for (int ti = 0; ti < LU; ++ti) {
-      float mc = mrun[ti];
+    for (int k = 0; k < TPT; ++k) {
+      float mc = mrun[k];
 #pragma unroll
-      for (int k = 0; k < KS; ++k) mc = fmaxf(mc, ml[ti][k].x);
+      for (int q = 0; q < KS; ++q) mc = fmaxf(mc, ml[k][q].x);
       const float muse = mc == -INFINITY ? 0.0f : mc;
-      const float a = __builtin_amdgcn_exp2f(mrun[ti] - muse);
-      lrun[ti] *= a;
+      const float a = __builtin_amdgcn_exp2f(mrun[k] - muse);
+      lrun[k] *= a;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[ti][c] *= a;
+      for (int c = 0; c < 4; ++c) o[k][c] *= a;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const float wk = __builtin_amdgcn_exp2f(ml[ti][k].x - muse);
-        lrun[ti] += wk * ml[ti][k].y;
-        o[ti][0] += wk * o01[ti][k].x;
-        o[ti][1] += wk * o01[ti][k].y;
-        o[ti][2] += wk * o23[ti][k].x;
-        o[ti][3] += wk * o23[ti][k].y;
+      for (int q = 0; q < KS; ++q) {
+        const float wk = __builtin_amdgcn_exp2f(ml[k][q].x - muse);
+        lrun[k] += wk * ml[k][q].y;
+        o[k][0] += wk * o01[k][q].x;
+        o[k][1] += wk * o01[k][q].y;
+        o[k][2] += wk * o23[k][q].x;
+        o[k][3] += wk * o23[k][q].y;
       }
-      mrun[ti] = mc;
+      mrun[k] = mc;
     }
   }
-  // The tokens' epilogues are independent chains (shuffles, fp64 rsqrt, gate):
+  // The tokens' epilogues are independent chains (reductions, rsqrt, gate):
   // computed for every slot without branches so they interleave; only the
   // stores of the group's real tokens are kept.
 #pragma unroll
-  for (int ti = 0; ti < LU; ++ti) {
+  for (int k = 0; k < TPT; ++k) {
+    const int ti = th + TS * k;
     // Output-side arithmetic runs in fp32 on the hardware reciprocal, rsqrt and
     // exp (each within a couple of fp32 ulps); the result is rounded to bf16
     // (2^-9 relative) once at the end.
-    const float inv = lrun[ti] > 0.0f ? vs * __builtin_amdgcn_rcpf(lrun[ti]) : 0.0f;
+    const float inv = lrun[k] > 0.0f ? vs * __builtin_amdgcn_rcpf(lrun[k]) : 0.0f;
     float y[4];
     float ss = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      y[c] = round_bf16(o[ti][c] * inv);  // the attention result is bf16 before the epilogue
+      y[c] = round_bf16(o[k][c] * inv);  // the attention result is bf16 before the epilogue
       ss += y[c] * y[c];
     }
     ss = sum16(ss);
     const float r = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + 1.0e-5f);
-    const float gate[4] = {bf16_value(graw[ti].x & 0xffffu), bf16_value(graw[ti].x >> 16),
-                           bf16_value(graw[ti].y & 0xffffu), bf16_value(graw[ti].y >> 16)};
+    const float gate[4] = {bf16_value(graw[k].x & 0xffffu), bf16_value(graw[k].x >> 16),
+                           bf16_value(graw[k].y & 0xffffu), bf16_value(graw[k].y >> 16)};
     uint32_t ob[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[c])));
@@ -771,16 +790,18 @@ __global__ __launch_bounds__(256) void fused_step_kernel(StepParams p) {
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int LU>
+template <int LU, bool HS>
 hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
-  hipLaunchKernelGGL(fused_step_kernel<LU>, dim3(grid), dim3(64 * kAttnWaves), 0, stream, p);
+  hipLaunchKernelGGL((fused_step_kernel<LU, HS>), dim3(grid), dim3(64 * (HS ? 2 : 1) * kAttnWaves), 0,
+                     stream, p);
   return hipGetLastError();
 }
 
 template <int LU>
 hipError_t launch_served(const StepParams& p, hipStream_t stream) {
-  if constexpr (max_q_len_for(LU) >= LU) return launch_lu<LU>(p, stream);
+  if constexpr (max_q_len_for(LU) >= LU)
+    return p.head_split ? launch_lu<LU, true>(p, stream) : launch_lu<LU, false>(p, stream);
   return hipErrorInvalidValue;
 }
 
