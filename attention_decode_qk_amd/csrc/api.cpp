@@ -64,6 +64,7 @@ struct mi355x_gated_attn_ctx {
   int32_t splits = 0;
   int32_t groups = 1;  // token groups per request
   bool head_split = false;
+  int32_t key_waves = kAttnWaves;
   size_t q_bytes = 0, po_off = 0, pml_off = 0, cnt_off = 0, ws_bytes = 0;
   bool timing = false;
   std::vector<hipEvent_t> events;  // 2 per timed step, reused
@@ -177,9 +178,14 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   // L = 1, 32k keys: 160 against 113 us; B = 32, L = 1, W = 2048: 13.0 against
   // 12.5 us), so four waves keep both heads.
   const bool head_split = keys <= kShortKeys && c.q_len > 1;
+  // Decode over long key ranges keeps more K/V blocks in flight with eight
+  // waves per unit, both heads each (B = 64, 32k keys: 106 against 113 us); over
+  // a window the extra merge and barrier cost more (B = 32, W = 2048: 15.7
+  // against 12.5 us).
+  const int key_waves = (c.q_len == 1 && keys > kShortKeys) ? 2 * kAttnWaves : kAttnWaves;
   int32_t s = num_splits;
   if (s == 0) {
-    const int64_t min_keys_per_split = (int64_t)kAttnWaves * kKeyBlock;  // a block per wave
+    const int64_t min_keys_per_split = (int64_t)key_waves * kKeyBlock;  // a block per wave
     const int64_t by_len = std::max<int64_t>(1, (keys + min_keys_per_split - 1) / min_keys_per_split);
     const int64_t target = (int64_t)kComputeUnits * units_per_cu(c.q_len);
     const int64_t units = (int64_t)c.batch * groups;  // units per split
@@ -199,6 +205,7 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   ctx->splits = s;
   ctx->groups = groups;
   ctx->head_split = head_split;
+  ctx->key_waves = key_waves;
   ctx->planned = true;
   if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
   if (num_splits_out) *num_splits_out = s;
@@ -272,6 +279,7 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   sp.tgroups = ctx->groups;
   sp.splits = ctx->splits;
   sp.head_split = ctx->head_split ? 1 : 0;
+  sp.key_waves = ctx->key_waves;
   sp.max_pages = c.max_pages;
   sp.page_size = c.page_size;
   sp.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;

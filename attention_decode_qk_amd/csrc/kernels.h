@@ -62,6 +62,7 @@ struct StepParams {
   int32_t tgroups;               // G: token_groups(L, short or not)
   int32_t splits;                // S
   int32_t head_split;            // 1: eight waves per unit, one KV head each
+  int32_t key_waves;             // waves per KV head taking blocks round-robin (4, or 8 at q_len 1)
   int32_t max_pages;
   int32_t page_size;
   int32_t page_shift;            // log2(page_size) if a power of two, else -1

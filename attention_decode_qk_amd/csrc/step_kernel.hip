@@ -227,17 +227,16 @@ __device__ inline uint2 pack_e4m3x8(const float (&y)[8]) {
   return make_uint2(lo, hi);
 }
 
-template <int LU, bool HS>
-__global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p) {
+template <int LU, bool HS, int KW>
+__global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(StepParams p) {
   // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
   // LU consecutive tokens; the unit (request b, token group tg, key chunk kc)
   // attends its group's query rows over chunk kc of the request's keys.
-  // HS (head split): eight waves, four per KV head, each wave working on one
-  // head's rows (two waves per SIMD); otherwise four waves working on both.
-  // Either way the four waves of a head take the chunk's 32-key blocks
-  // round-robin.
+  // KW waves per KV head take the chunk's 32-key blocks round-robin.  HS (head
+  // split): 2*KW waves, each working on one KV head's rows; otherwise KW waves
+  // working on both heads.
   constexpr int NG = HS ? 1 : kKvHeads;           // KV heads a wave works on
-  constexpr int kWaves = HS ? 2 * kAttnWaves : kAttnWaves;
+  constexpr int kWaves = HS ? 2 * KW : KW;
   constexpr int kThreads = 64 * kWaves;
   constexpr int NRB = (LU * kGroup + 15) / 16;  // 16-row blocks per KV head
   constexpr int kQItems = LU * kQHeads * 8;     // (token, q head, 8-column slice)
@@ -250,8 +249,8 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   __shared__ __align__(16) uint8_t s_newk[kMaxQLen][kRowBytes];
   __shared__ __align__(16) uint8_t s_newv[kMaxQLen][kRowBytes];
   __shared__ float s_cs[kMaxQLen][kHeadDim / 2][2];
-  __shared__ __align__(16) float s_mo[kAttnWaves][kRows][kHeadDim];
-  __shared__ __align__(16) float s_ml[kAttnWaves][kRows][2];
+  __shared__ __align__(16) float s_mo[KW][kRows][kHeadDim];
+  __shared__ __align__(16) float s_ml[KW][kRows][2];
   __shared__ int s_last;
 
   // A unit size that serves a single q_len (LU = 1: q_len 1) serves it as one group.
@@ -266,8 +265,8 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int kw = wave % kAttnWaves;            // this wave's place among its head's waves
-  const int g0 = HS ? wave / kAttnWaves : 0;   // first KV head this wave works on
+  const int kw = wave % KW;            // this wave's place among its head's waves
+  const int g0 = HS ? wave / KW : 0;   // first KV head this wave works on
   const int j = lane & 15;
   const int q4 = lane >> 4;
   const int64_t tok0 = (int64_t)b * L;
@@ -294,7 +293,7 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   const int start = first + kc * chunk;
   const int end = min(start + chunk, last + 1);
   const int nblk = end > start ? (end - start + kKeyBlock - 1) / kKeyBlock : 0;
-  const int nb = nblk > kw ? (nblk - kw + kAttnWaves - 1) / kAttnWaves : 0;  // this wave's
+  const int nb = nblk > kw ? (nblk - kw + KW - 1) / KW : 0;  // this wave's
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
   // Key of this lane in the wave's block i.  Blocks past the wave's last are
   // clamped to it, so the pipeline's loads are unconditional (which keeps the
@@ -303,7 +302,7 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   const int voff = v_key_offset(lane);
   auto block_key = [&](int i, int off) {
     const int blk = min(i, max(nb - 1, 0));
-    return max(0, min(start + (kw + kAttnWaves * blk) * kKeyBlock + off, end - 1));
+    return max(0, min(start + (kw + KW * blk) * kKeyBlock + off, end - 1));
   };
   auto k_key = [&](int i) { return block_key(i, lane & 31); };
   auto v_key = [&](int i) { return block_key(i, voff); };
@@ -557,8 +556,8 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   for (int bi = 0; bi < nb; bi += 2) {
     const bool has_b = bi + 1 < nb;
     // An absent second block sits past the chunk: every key masked, no codes substituted.
-    const int kb0 = start + (kw + kAttnWaves * bi) * kKeyBlock;
-    const int kb1 = has_b ? kb0 + kAttnWaves * kKeyBlock : end;
+    const int kb0 = start + (kw + KW * bi) * kKeyBlock;
+    const int kb1 = has_b ? kb0 + KW * kKeyBlock : end;
     substitute(bufA, kb0);
     if (has_b) substitute(bufB, kb1);
     float z0[NG][NRB][8], z1[NG][NRB][8];
@@ -655,10 +654,10 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   const int64_t prow0 = (((int64_t)b * p.splits + kc) * L + t_lo) * kQHeads;
   for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
     const int cr = idx >> 4, c4 = (idx & 15) * 4;
-    float mw[kAttnWaves], lw[kAttnWaves];
+    float mw[KW], lw[KW];
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = 0; w < KW; ++w) {
       const float2 ml = *reinterpret_cast<const float2*>(&s_ml[w][cr][0]);
       mw[w] = ml.x;
       lw[w] = ml.y;
@@ -668,7 +667,7 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
     float lsum = 0.0f;
     float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int w = 0; w < kAttnWaves; ++w) {
+    for (int w = 0; w < KW; ++w) {
       const float a = __builtin_amdgcn_exp2f(mw[w] - muse);
       const float4 v = *reinterpret_cast<const float4*>(&s_mo[w][cr][c4]);
       lsum += a * lw[w];
@@ -790,18 +789,22 @@ __global__ __launch_bounds__(HS ? 512 : 256) void fused_step_kernel(StepParams p
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int LU, bool HS>
+template <int LU, bool HS, int KW>
 hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
-  hipLaunchKernelGGL((fused_step_kernel<LU, HS>), dim3(grid), dim3(64 * (HS ? 2 : 1) * kAttnWaves), 0,
+  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
                      stream, p);
   return hipGetLastError();
 }
 
 template <int LU>
 hipError_t launch_served(const StepParams& p, hipStream_t stream) {
-  if constexpr (max_q_len_for(LU) >= LU)
-    return p.head_split ? launch_lu<LU, true>(p, stream) : launch_lu<LU, false>(p, stream);
+  if constexpr (max_q_len_for(LU) >= LU) {
+    if (p.head_split) return launch_lu<LU, true, kAttnWaves>(p, stream);
+    if constexpr (LU == 1)
+      if (p.key_waves == 2 * kAttnWaves) return launch_lu<LU, false, 2 * kAttnWaves>(p, stream);
+    return launch_lu<LU, false, kAttnWaves>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 
