@@ -9,12 +9,12 @@ workload is the decode batch the headline metric is quoted on: B=32, L=1,
 16 query / 2 KV heads, head_dim 64, page_size 1, window 2048, RoPE theta
 5e5, cached lengths uniform in [4096, 16384], shuffled page table.
 
-Cold-cache discipline: the steps round-robin over enough per-layer KV pools
-(own K/V caches and projection rows) to exceed 1 GiB, four times the 256 MB
-Infinity Cache, as a model's layers would.  The step's page table, cache rows,
-positions and lengths are shared by all layers, as the serving engine builds
-them once per step for every layer (--table-per-layer gives each pool its own
-page-table permutation instead: a colder, less faithful variant).  The layer-
+Cold-cache discipline: the steps round-robin over enough per-layer pools (own
+K/V caches, own page-table permutation and cache rows, own projection rows,
+same lengths) to exceed 1 GiB, four times the 256 MB Infinity Cache, as a
+model's layers would.  --shared-table shares pool 0's page table and cache rows
+instead, as a serving engine that builds them once per step for every layer
+would (measured within noise of the default).  The layer-
 steps are captured in HIP graphs outside the timed region (one graph of W
 warm-up steps, one of exactly K timed steps) and the timed region is one
 replay of the K-step graph, bracketed by synchronisation and HIP events on the
@@ -127,8 +127,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="swa_decode")
     ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of layer pools (cold cache)")
-    ap.add_argument("--table-per-layer", action="store_true",
-                    help="give every layer pool its own page-table permutation")
+    ap.add_argument("--shared-table", action="store_true",
+                    help="share layer pool 0's page table and cache rows among the pools")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = plan)")
@@ -169,7 +169,7 @@ def main():
     w = synth.WORKLOADS[args.workload]
     x0 = synth.make_inputs(w)
     kv_bytes, step_bytes = algorithmic_bytes(w, x0)
-    pool_bytes = x0.k_cache.nbytes + x0.v_cache.nbytes + (x0.page_table.nbytes if args.table_per_layer else 0)
+    pool_bytes = x0.k_cache.nbytes + x0.v_cache.nbytes + (0 if args.shared_table else x0.page_table.nbytes)
     n_layers = max(1, int(np.ceil(args.cold_bytes * (1 << 30) / pool_bytes)))
     print(f"[bench] {w.name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}; "
           f"{n_layers} layer pools of {pool_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
@@ -179,8 +179,8 @@ def main():
     step = ga.GatedAttnStep(cfg, int(w.seq_hi + w.q_len), args.splits)
 
     # Layer pools: pool 0 is the tests' seeded input; the others are drawn on
-    # the device with the same recipe (own caches and projection rows; the
-    # page table and cache rows of pool 0 unless --table-per-layer).
+    # the device with the same recipe (own caches, page-table permutation and
+    # projection rows; pool 0's table and cache rows with --shared-table).
     gen = torch.Generator(device=dev)
     gen.manual_seed(w.seed)
     P = w.page_size
@@ -200,7 +200,7 @@ def main():
             vc = torch.from_numpy(x0.v_cache).to(dev)
             qkv = torch.from_numpy(x0.qkv.view(np.int16)).to(dev)
         else:
-            if args.table_per_layer:
+            if not args.shared_table:
                 perm = torch.randperm(x0.num_pages, generator=gen, device=dev).to(torch.int32)
                 pt = torch.full((w.batch, x0.max_pages), -1, dtype=torch.int32, device=dev)
                 off = 0
@@ -303,7 +303,7 @@ def main():
                    "rope_theta": w.rope_theta, "sm_scale": w.sm_scale, "kv_scale": w.kv_scale,
                    "seq_lens": [w.seq_lo, w.seq_hi], "splits": step.splits,
                    "layer_pools": n_layers, "cold_cache_bytes": n_layers * pool_bytes,
-                   "page_table": "per layer" if args.table_per_layer else "shared by the layers"},
+                   "page_table": "shared by the layers" if args.shared_table else "per layer"},
         "us_per_layer_step": round(us_step, 3),
         "kv_bytes_per_step": kv_bytes,
         "kv_gbs_pct_of_peak": round(100.0 * kv_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),

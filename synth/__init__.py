@@ -62,6 +62,15 @@ WORKLOADS = {
 }
 ORDER = ["tiny_decode", "swa_decode", "full_decode_32k", "swa_verify", "paged_scaled_long"]
 
+# Supplementary benchmark rows: the headline's shape with every request at
+# 16,384 cached tokens, windowed and full (the "16k ctx" of the headline read
+# either way).  Not part of ORDER.
+SUPPLEMENTARY = {
+    "swa_decode_16k": Workload("swa_decode_16k", 32, 1, 16384, 16384, 2048, 500000.0, seed=1006),
+    "full_decode_16k": Workload("full_decode_16k", 32, 1, 16384, 16384, 0, 500000.0, seed=1007),
+}
+WORKLOADS.update(SUPPLEMENTARY)
+
 
 @dataclass
 class Inputs:

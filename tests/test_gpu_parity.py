@@ -127,7 +127,7 @@ def _sample_rows(T, hq, rng, n=64):
     return np.array(t, np.int64), np.array(h, np.int32)
 
 
-@pytest.mark.parametrize("name", synth.ORDER)
+@pytest.mark.parametrize("name", synth.ORDER + list(synth.SUPPLEMENTARY))
 def test_full_size_workload(name):
     """Every q and cache byte, and sampled output rows, of one full-size step."""
     w = synth.WORKLOADS[name]
