@@ -197,6 +197,19 @@ def epilogue(cfg: Config, o: np.ndarray, qkv: np.ndarray, sel_t: np.ndarray | No
     return out
 
 
+def step_meta(cfg: Config, seq_lens: np.ndarray, page_table: np.ndarray):
+    """(positions int64 [T], cache_loc int64 [T], cache_seqlens int32 [B]) of a step."""
+    T = cfg.batch * cfg.q_len
+    seq = np.ascontiguousarray(seq_lens, np.int32)
+    pt = np.ascontiguousarray(page_table, np.int32)
+    pos = np.empty(T, np.int64)
+    loc = np.empty(T, np.int64)
+    cs = np.empty(cfg.batch, np.int32)
+    _check(lib().orc_step_meta(ctypes.byref(cfg.c()), _p(seq), _p(pt), _p(pos), _p(loc), _p(cs)),
+           "step_meta")
+    return pos, loc, cs
+
+
 def step(cfg: Config, qkv, positions, cache_loc, cache_seqlens, page_table, k_cache, v_cache,
          k_scale: float, v_scale: float):
     """Whole step; caches updated in place.  Returns (q codes, out bf16 bits [B, L, Hq*D],

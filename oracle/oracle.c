@@ -458,3 +458,45 @@ int orc_step(const orc_config* cfg, const uint16_t* qkv, const int64_t* position
   if (rc) return rc;
   return orc_epilogue(cfg, o_scratch, qkv, 0, NULL, NULL, out);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Step metadata: the per-token positions and cache rows and the per-request */
+/* key counts that every layer of a step shares, from the cached lengths and */
+/* the page table.                                                           */
+/*                                                                          */
+/* Page "012-attention-local-splits.py", `Inputs`: token t = b*L + i sits at */
+/* position seq_lens[b] + i; cache_loc[t] is the flat cache row the page     */
+/* table gives that position (physical page * page_size + offset in page);   */
+/* cache_seqlens = seq_lens + L.  Page "msa.py" (update_msa_decode_cg_meta): */
+/* graph replay pads the batch with seq_len == 0 slots, masked by a zero key */
+/* count.                                                                    */
+/* READING: a slot with seq_lens[b] <= 0 is padding: its tokens get position */
+/* 0 and cache row -1 (nothing is stored) and the slot key count 0 (no key,  */
+/* output 0).  A position whose page-table entry lies beyond max_pages or is */
+/* negative also gets cache row -1.                                          */
+/* ------------------------------------------------------------------------ */
+int orc_step_meta(const orc_config* cfg, const int32_t* seq_lens, const int32_t* page_table,
+                  int64_t* positions, int64_t* cache_loc, int32_t* cache_seqlens) {
+  if (!cfg_ok(cfg)) return ORC_BAD_ARG;
+  const int64_t P = cfg->page_size;
+  for (int64_t b = 0; b < cfg->batch; ++b) {
+    const int64_t len = seq_lens[b];
+    const int pad = len <= 0;
+    cache_seqlens[b] = pad ? 0 : (int32_t)(len + cfg->q_len);
+    for (int64_t i = 0; i < cfg->q_len; ++i) {
+      const int64_t t = b * cfg->q_len + i;
+      if (pad) {
+        positions[t] = 0;
+        cache_loc[t] = -1;
+        continue;
+      }
+      const int64_t p = len + i;
+      positions[t] = p;
+      const int64_t page = p / P;
+      int64_t entry = -1;
+      if (page < cfg->max_pages) entry = page_table[b * cfg->max_pages + page];
+      cache_loc[t] = entry < 0 ? -1 : entry * P + p % P;
+    }
+  }
+  return ORC_OK;
+}
