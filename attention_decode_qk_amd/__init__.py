@@ -24,7 +24,7 @@ MI355X_GA_HIP_ERROR = 4
 EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_gated_attn_plan",
             "mi355x_gated_attn_workspace_init", "mi355x_gated_attn_step", "mi355x_gated_attn_destroy",
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
-            "mi355x_gated_attn_timing_read"]
+            "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta"]
 
 
 class GatedAttnError(RuntimeError):
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(ctypes.c_int32)]
         L.mi355x_gated_attn_workspace_init.argtypes = [P, P, ctypes.c_size_t, P]
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
+        L.mi355x_gated_attn_step_meta.argtypes = [P] * 7
         L.mi355x_gated_attn_destroy.argtypes = [P]
         L.mi355x_gated_attn_destroy.restype = None
         L.mi355x_gated_attn_last_error.argtypes = []
@@ -148,6 +149,24 @@ def mi355x_gated_attn_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_t
         _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
 
 
+def mi355x_gated_attn_step_meta(ctx, seq_lens, page_table, positions, cache_loc, cache_seqlens,
+                                stream=None):
+    """Build a step's positions, cache rows and key counts on the device (int32
+    seq_lens [B] and page_table [B, max_pages] in; int64 positions and cache_loc
+    [B*L], int32 cache_seqlens [B] out)."""
+    import torch
+    for name, t in dict(seq_lens=seq_lens, page_table=page_table, positions=positions,
+                        cache_loc=cache_loc, cache_seqlens=cache_seqlens).items():
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(seq_lens.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_step_meta(ctx, _ptr(seq_lens), _ptr(page_table), _ptr(positions),
+                                             _ptr(cache_loc), _ptr(cache_seqlens),
+                                             ctypes.c_void_p(handle)))
+
+
 def mi355x_gated_attn_workspace_init(ctx, workspace, stream=None):
     """Zero a new workspace's counters (once, before its first step)."""
     import torch
@@ -199,6 +218,11 @@ class GatedAttnStep:
                                seq_lens, k_cache, v_cache, k_scale, v_scale, out, self.workspace,
                                stream)
         return out
+
+    def meta(self, seq_lens, page_table, positions, cache_loc, cache_seqlens, stream=None):
+        """Build the step's positions, cache rows and key counts on the device."""
+        mi355x_gated_attn_step_meta(self.ctx, seq_lens, page_table, positions, cache_loc,
+                                    cache_seqlens, stream)
 
     def close(self):
         if self.ctx is not None:

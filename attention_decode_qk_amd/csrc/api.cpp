@@ -228,6 +228,32 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
   return ok();
 }
 
+int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_lens,
+                                const int32_t* page_table, int64_t* positions, int64_t* cache_loc,
+                                int32_t* cache_seqlens, void* stream) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  const auto& c = ctx->cfg;
+  if (c.batch == 0) return ok();
+  if (!seq_lens || !page_table || !positions || !cache_loc || !cache_seqlens)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "a required pointer is NULL");
+  int rc = check_device(ctx);
+  if (rc) return rc;
+  MetaParams m{};
+  m.seq_lens = seq_lens;
+  m.page_table = page_table;
+  m.positions = positions;
+  m.cache_loc = cache_loc;
+  m.cache_seqlens = cache_seqlens;
+  m.batch = c.batch;
+  m.q_len = c.q_len;
+  m.max_pages = c.max_pages;
+  m.page_size = c.page_size;
+  m.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;
+  const hipError_t e = launch_step_meta(m, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
                            const int64_t* cache_loc, const int32_t* cache_seqlens,
                            const int32_t* page_table, const int32_t* seq_lens, void* k_cache,

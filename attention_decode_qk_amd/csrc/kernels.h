@@ -74,6 +74,21 @@ struct StepParams {
 };
 
 hipError_t launch_step(const StepParams& p, hipStream_t stream);
+
+// Per-step metadata shared by every layer (meta_kernel.hip).
+struct MetaParams {
+  const int32_t* seq_lens;       // [B]
+  const int32_t* page_table;     // [B, max_pages]
+  int64_t* positions;            // [B*L] out
+  int64_t* cache_loc;            // [B*L] out
+  int32_t* cache_seqlens;        // [B] out
+  int32_t batch;
+  int32_t q_len;
+  int32_t max_pages;
+  int32_t page_size;
+  int32_t page_shift;            // log2(page_size) if a power of two, else -1
+};
+hipError_t launch_step_meta(const MetaParams& m, hipStream_t stream);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t stream);
 
 }  // namespace mi355x_ga

@@ -114,6 +114,33 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
                                      size_t workspace_bytes, void* stream);
 
 /*
+ * The step metadata every layer of a step shares, built on the device once per
+ * step (page "012-attention-local-splits.py", `Inputs`: token t = b*L + i sits
+ * at position seq_lens[b] + i, its cache row is the flat row the page table
+ * gives that position, cache_seqlens = seq_lens + L; page "msa.py",
+ * update_msa_decode_cg_meta: graph replay pads the batch with seq_len == 0
+ * slots).  Asynchronous on `stream`; no host synchronisation or allocation, so
+ * capturable; the calling thread's current device must be the ctx's device.
+ *
+ *   seq_lens       int32 [B]    cached tokens per request; a slot with
+ *                  seq_lens[b] <= 0 is padding
+ *   page_table     int32 [B, max_pages]  physical page of each logical page,
+ *                  already covering the step's new positions (-1 unused)
+ *   positions      int64 [B*L]  out: seq_lens[b] + i (0 in a padded slot)
+ *   cache_loc      int64 [B*L]  out: page_table[b, p / P] * P + p % P, or -1
+ *                  for a padded slot or a position whose page entry is
+ *                  negative or beyond max_pages (the step then stores nothing)
+ *   cache_seqlens  int32 [B]    out: seq_lens[b] + L (0 in a padded slot: the
+ *                  step then outputs zeros for it)
+ * Needs only `prepare` (B, L, page_size, max_pages of the ctx's config).
+ * Returns MI355X_GA_OK with no launch when B == 0; INVALID_ARGUMENT for a NULL
+ * pointer.
+ */
+int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_lens,
+                                const int32_t* page_table, int64_t* positions, int64_t* cache_loc,
+                                int32_t* cache_seqlens, void* stream);
+
+/*
  * One layer-step, asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream); the calling thread's current device must be the ctx's device.
  * No host synchronisation, allocation or device-value read: capturable.

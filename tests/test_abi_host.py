@@ -235,3 +235,23 @@ def test_short_key_ranges_use_groups_of_two_tokens(L):
             assert ws == -(-(cnt + 7 * groups * 4) // 256) * 256, (Lq, max_context)
         finally:
             ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_step_meta_validates_before_launch(L):
+    """Metadata builder: NULL pointers are rejected on the host, B == 0 is a no-op."""
+    P = ctypes.c_void_p
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=4, q_len=2))
+    try:
+        args = [P(0x1000), P(0x2000), P(0x3000), P(0x4000), P(0x5000)]
+        for k in range(5):
+            bad = list(args)
+            bad[k] = None
+            assert L.mi355x_gated_attn_step_meta(ctx, *bad, None) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert L.mi355x_gated_attn_step_meta(None, *args, None) == ga.MI355X_GA_INVALID_ARGUMENT
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=0))
+    try:
+        assert L.mi355x_gated_attn_step_meta(ctx, None, None, None, None, None, None) == ga.MI355X_GA_OK
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
