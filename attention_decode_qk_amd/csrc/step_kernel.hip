@@ -650,10 +650,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       if (q4 == 0) *reinterpret_cast<float2*>(&s_ml[kw][cr][0]) = make_float2(mrow[g][rb], lrow[g][rb]);
     }
   lds_barrier();
-  // Partial rows are ((b * splits + kc) * L + token) * 16 + head.
-  const int64_t prow0 = (((int64_t)b * p.splits + kc) * L + t_lo) * kQHeads;
-  for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
-    const int cr = idx >> 4, c4 = (idx & 15) * 4;
+  // Merge of one (row, 4 columns) over the waves' LDS slots.
+  auto merge = [&](int cr, int c4, float& m_out, float& l_out, float4& o_out) {
     float mw[KW], lw[KW];
     float mx = -INFINITY;
 #pragma unroll
@@ -676,32 +674,61 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       o.z += a * v.z;
       o.w += a * v.w;
     }
-    float* dst = p.part_o + (prow0 + cr) * kHeadDim + c4;
-    store_coherent(dst, o.x, o.y);
-    store_coherent(dst + 2, o.z, o.w);
-    if (c4 == 0) store_coherent(p.part_ml + (prow0 + cr) * 2, mx, lsum);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
-  __syncthreads();
-  int32_t* counter = p.counters + (kOneGroup ? b : b * p.tgroups + tg);
-  if (tid == 0)
-    s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
-  __syncthreads();
-  if (!s_last) return;
-
-  // ---------------- D. combine + gated epilogue (last unit of the group) ----------------
-  // Thread (th, h, c4) takes columns c4..c4+3 of head h for the group's tokens
-  // th, th + TS, ... (TS = threads / 256).  The partials are read KS splits at a
-  // time for all the thread's tokens at once, so the chain of device-coherent
-  // round trips is ceil(splits / KS) long whatever the number of tokens.
+    m_out = mx;
+    l_out = lsum;
+    o_out = o;
+  };
+  // The combine's thread mapping: thread (th, h, c4) takes columns c4..c4+3 of
+  // head h for the group's tokens th, th + TS, ... (TS = threads / 256).
   constexpr int TS = kThreads / 256;            // token stride between thread groups
   constexpr int TPT = (LU + TS - 1) / TS;       // token slots per thread
-  constexpr int KS = TPT >= 4 ? 4 : (TPT == 3 ? 5 : (TPT == 2 ? 8 : 16));
   const int c4 = (tid & 15) * 4;
   const int h = (tid >> 4) & (kQHeads - 1);
   const int th = tid >> 8;
+  // Partial rows are ((b * splits + kc) * L + token) * 16 + head.
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
   const int64_t base = (int64_t)b * p.splits * stride + (int64_t)t_lo * kQHeads + h;
+  int32_t* counter = p.counters + (kOneGroup ? b : b * p.tgroups + tg);
+  float own_m[TPT], own_l[TPT], own_o[TPT][4];  // a single split's result
+  if (p.splits > 1) {
+    const int64_t prow0 = (((int64_t)b * p.splits + kc) * L + t_lo) * kQHeads;
+    for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
+      const int cr = idx >> 4, cc = (idx & 15) * 4;
+      float mx, lsum;
+      float4 o;
+      merge(cr, cc, mx, lsum, o);
+      float* dst = p.part_o + (prow0 + cr) * kHeadDim + cc;
+      store_coherent(dst, o.x, o.y);
+      store_coherent(dst + 2, o.z, o.w);
+      if (cc == 0) store_coherent(p.part_ml + (prow0 + cr) * 2, mx, lsum);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
+    __syncthreads();
+    if (!s_last) return;
+  } else {  // a single split is its own combine: no publish, no counter
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      const int ti = th + TS * k;
+      own_m[k] = -INFINITY;
+      own_l[k] = 0.0f;
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (ti < t_n) merge(ti * kQHeads + h, c4, own_m[k], own_l[k], o);
+      own_o[k][0] = o.x;
+      own_o[k][1] = o.y;
+      own_o[k][2] = o.z;
+      own_o[k][3] = o.w;
+    }
+  }
+
+  // ---------------- D. combine + gated epilogue (last unit of the group) ----------------
+  // With several splits the partials (the unit's own included, as published)
+  // are read KS splits at a time for all the thread's tokens at once, so the
+  // chain of device-coherent round trips is ceil(splits / KS) long whatever the
+  // number of tokens; a single split is taken from registers.
+  constexpr int KS = TPT >= 4 ? 4 : (TPT == 3 ? 5 : (TPT == 2 ? 8 : 16));
   uint2 graw[TPT];
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
@@ -719,7 +746,16 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[k][c] = 0.0f;
   }
-  for (int s0 = 0; s0 < p.splits; s0 += KS) {
+  if (p.splits == 1) {
+#pragma unroll
+    for (int k = 0; k < TPT; ++k) {
+      mrun[k] = own_m[k];
+      lrun[k] = own_l[k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[k][c] = own_o[k][c];
+    }
+  }
+  for (int s0 = 0; p.splits > 1 && s0 < p.splits; s0 += KS) {
     float2 ml[TPT][KS], o01[TPT][KS], o23[TPT][KS];
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
@@ -786,7 +822,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
           make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
   }
-  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && p.splits > 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int LU, bool HS, int KW>

@@ -63,6 +63,20 @@ def test_every_q_len_under_both_token_groupings(q_len, grouping):
     check_full(x, res, Reference(x), f"groups {grouping} L={q_len}")
 
 
+@pytest.mark.parametrize("q_len", [1, 8])
+def test_large_batch_single_split(q_len):
+    """A batch large enough for the plan to give one split per request (more
+    units than compute units): each unit is its own combine (no partials, no
+    counter)."""
+    w = synth.small(name="wide", batch=300, q_len=q_len, window=64, rope_theta=500000.0,
+                    seq_lo=30, seq_hi=200, page_size=4)
+    x = synth.make_inputs(w, seed=91)
+    _say(f"[gpu] large batch B=300 L={q_len}")
+    res = run_gpu(x)
+    assert res.splits == 1
+    check_full(x, res, Reference(x), f"B=300 L={q_len}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 16, 64])
 def test_split_count_invariance(splits):
     """Any split count gives oracle-level results (partials merge exactly in form)."""
