@@ -9,10 +9,11 @@ workload is the decode batch the headline metric is quoted on: B=32, L=1,
 16 query / 2 KV heads, head_dim 64, page_size 1, window 2048, RoPE theta
 5e5, cached lengths uniform in [4096, 16384], shuffled page table.
 
-Cold-cache discipline: the steps round-robin over enough per-layer pools (own
-K/V caches, own page-table permutation and cache rows, own projection rows,
-same lengths) to exceed 1 GiB, four times the 256 MB Infinity Cache, as a
-model's layers would.  --shared-table shares pool 0's page table and cache rows
+Cold-cache discipline: the steps round-robin over per-layer pools (own K/V
+caches, own page-table permutation and cache rows, own projection rows, same
+lengths), enough of them that one round touches at least 1 GiB -- the bytes
+the steps read and write, not the pools' size -- four times the 256 MB Infinity
+Cache, as a model's layers would.  --shared-table shares pool 0's page table and cache rows
 instead, as a serving engine that builds them once per step for every layer
 would (measured within noise of the default).  The layer-
 steps are captured in HIP graphs outside the timed region (one graph of W
@@ -39,7 +40,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "fused_step_swa_decode_counters.md")
+def counters_file(workload: str) -> str:
+    """The committed rocprofv3 counter summary of one workload."""
+    return os.path.join(ROOT, "profiles", f"fused_step_{workload}_counters.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "attention_decode_qk_amd", "csrc", f)
                   for f in ("step_kernel.hip", "kernels.h", "numerics.h")] + \
                  [os.path.join(ROOT, "attention_decode_qk_amd", "build.py")]  # compiler flags
@@ -81,12 +84,24 @@ def algorithmic_bytes(w, x):
     return kv, kv + 4 * pages + x.tokens * per_token
 
 
-def load_traffic():
-    """HBM traffic per attention launch from the committed counter summary, or
-    None when the kernel source changed since the counters were taken."""
-    if not os.path.exists(COUNTERS_FILE):
+POOL_MEMORY_LIMIT = 64 << 30  # device bytes the layer pools may take
+
+
+def layer_pool_count(step_bytes: int, pool_bytes: int, cold_bytes: float) -> int:
+    """Layer pools to round-robin over: enough that one round touches at least
+    cold_bytes (a step touches step_bytes of its pool, whatever the pool's size),
+    within POOL_MEMORY_LIMIT of device memory."""
+    n = max(1, -(-int(cold_bytes) // max(1, int(step_bytes))))
+    return max(1, min(n, POOL_MEMORY_LIMIT // max(1, int(pool_bytes))))
+
+
+def load_traffic(workload: str):
+    """HBM traffic per launch from the workload's committed counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = counters_file(workload)
+    if not os.path.exists(path):
         return None
-    text = open(COUNTERS_FILE).read()
+    text = open(path).read()
     m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", text, re.M)
     if not m:
         return None
@@ -126,7 +141,8 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="swa_decode")
-    ap.add_argument("--cold-bytes", type=float, default=1.0, help="GiB of layer pools (cold cache)")
+    ap.add_argument("--cold-bytes", type=float, default=1.0,
+                    help="GiB the steps touch in one round over the layer pools (cold cache)")
     ap.add_argument("--shared-table", action="store_true",
                     help="share layer pool 0's page table and cache rows among the pools")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -170,9 +186,10 @@ def main():
     x0 = synth.make_inputs(w)
     kv_bytes, step_bytes = algorithmic_bytes(w, x0)
     pool_bytes = x0.k_cache.nbytes + x0.v_cache.nbytes + (0 if args.shared_table else x0.page_table.nbytes)
-    n_layers = max(1, int(np.ceil(args.cold_bytes * (1 << 30) / pool_bytes)))
+    n_layers = layer_pool_count(step_bytes, pool_bytes, args.cold_bytes * (1 << 30))
     print(f"[bench] {w.name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}; "
-          f"{n_layers} layer pools of {pool_bytes / 1e6:.1f} MB", file=sys.stderr, flush=True)
+          f"{n_layers} layer pools of {pool_bytes / 1e6:.1f} MB, {step_bytes / 1e6:.2f} MB "
+          f"touched per step", file=sys.stderr, flush=True)
 
     cfg = ga.make_config(w.batch, w.q_len, w.page_size, w.window, x0.max_pages, x0.num_pages,
                          w.rope_theta, w.sm_scale, w.kv_scale)
@@ -298,7 +315,7 @@ def main():
     # The step is one kernel, so the graph-timed time per step is that kernel's
     # average duration over the timed region (rocprofv3's kernel trace agrees).
     achieved = step_bytes / (us_step * 1e-6) / 1e9
-    traffic = load_traffic()
+    traffic = load_traffic(w.name)
     result = {
         "metric": METRIC,
         "value": round(kv_bytes / (us_step * 1e-6) / 1e9, 1),
@@ -317,7 +334,8 @@ def main():
                    "head_dim": w.head_dim, "page_size": w.page_size, "window": w.window,
                    "rope_theta": w.rope_theta, "sm_scale": w.sm_scale, "kv_scale": w.kv_scale,
                    "seq_lens": [w.seq_lo, w.seq_hi], "splits": step.splits,
-                   "layer_pools": n_layers, "cold_cache_bytes": n_layers * pool_bytes,
+                   "layer_pools": n_layers, "touched_bytes_per_round": n_layers * step_bytes,
+                   "pool_bytes_allocated": n_layers * pool_bytes,
                    "page_table": "shared by the layers" if args.shared_table else "per layer"},
         "us_per_layer_step": round(us_step, 3),
         "kv_bytes_per_step": kv_bytes,

@@ -46,3 +46,22 @@ def test_algorithmic_bytes_count_kv_rows_pages_and_token_rows():
     pages = int(np.sum((x.cache_seqlens + w.page_size - 1) // w.page_size))
     per_token = w.width * 2 + 2 * w.num_kv_heads * w.head_dim + w.num_q_heads * w.head_dim * 2 + 16
     assert total == kv + 4 * pages + x.tokens * per_token
+
+
+def test_layer_pools_cover_the_cold_bytes_by_what_a_step_touches():
+    # A windowed step touches ~17 MB of a ~90 MB pool: the round must cover 1 GiB
+    # of touched bytes, not of allocated pools (the Infinity Cache is 256 MB).
+    n = bench.layer_pool_count(17_261_056, 89_500_000, 1 << 30)
+    assert n == 63 and n * 17_261_056 >= 1 << 30
+    assert bench.layer_pool_count(600_000_000, 600_000_000, 1 << 30) == 2
+    assert bench.layer_pool_count(1 << 31, 1 << 31, 1 << 30) == 1
+    # Device memory bounds the count.
+    assert bench.layer_pool_count(1000, 1 << 30, 1 << 30) == bench.POOL_MEMORY_LIMIT // (1 << 30)
+
+
+def test_traffic_comes_only_from_the_workloads_own_counters():
+    assert bench.load_traffic("no_such_workload") is None
+    import os
+    if os.path.exists(bench.counters_file("swa_decode")):
+        t = bench.load_traffic("swa_decode")
+        assert t is None or t > 0
