@@ -198,7 +198,7 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   const size_t rows = T * kQHeads;  // (token, q head) rows
   ctx->q_bytes = T * kQHeads * kHeadDim;
   ctx->po_off = align_up(ctx->q_bytes, 256);
-  ctx->pml_off = align_up(ctx->po_off + (size_t)s * rows * kHeadDim * sizeof(float), 256);
+  ctx->pml_off = align_up(ctx->po_off + (size_t)s * rows * kHeadDim * sizeof(uint16_t), 256);
   ctx->cnt_off = align_up(ctx->pml_off + (size_t)s * rows * 2 * sizeof(float), 256);
   ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)c.batch * groups * sizeof(int32_t), 256);
   if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
@@ -295,7 +295,7 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   sp.v_scale = v_scale;
   sp.out = reinterpret_cast<uint16_t*>(out);
   sp.q_out = ws;
-  sp.part_o = reinterpret_cast<float*>(ws + ctx->po_off);
+  sp.part_o = reinterpret_cast<_Float16*>(ws + ctx->po_off);
   sp.part_ml = reinterpret_cast<float*>(ws + ctx->pml_off);
   sp.counters = reinterpret_cast<int32_t*>(ws + ctx->cnt_off);
   sp.num_pages = c.num_pages;

@@ -52,7 +52,7 @@ struct StepParams {
   const float* v_scale;
   uint16_t* out;                 // bf16 [T, kQHeads * kHeadDim]
   uint8_t* q_out;                // e4m3 [T, kQHeads, kHeadDim] (workspace)
-  float* part_o;                 // fp32 [B, S, L*kQHeads, kHeadDim]
+  _Float16* part_o;              // f16 [B, S, L*kQHeads, kHeadDim]: o / l of the split
   float* part_ml;                // fp32 [B, S, L*kQHeads, 2]: running max (log2 units), sum
   int32_t* counters;             // [B, G] finished units per (request, token group), 0 between steps
   int64_t num_pages;

@@ -28,8 +28,8 @@
 //     by more than 2^8); P in f16; PV as O^T = V^T P^T on
 //     v_mfma_f32_16x16x32_f16 with V transposed in registers and widened
 //     exactly to f16.
-//  C. The four waves merge through LDS and publish the unit's partial (o, m, l)
-//     with device-coherent stores; an atomic counter per (request, token group)
+//  C. The four waves merge through LDS and publish the unit's partial (o / l
+//     in f16, m and l in fp32) with device-coherent stores; an atomic counter per (request, token group)
 //     elects the group's last unit, which reads the group's partials with
 //     device-coherent loads, merges them, rounds the attention output to bf16,
 //     applies RMSNorm x sigmoid(gate), writes bf16 out and re-arms the counter.
@@ -66,6 +66,22 @@ __device__ inline float2 load_coherent(const float* src) {
                                        __HIP_MEMORY_SCOPE_AGENT);
   return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
 }
+
+// Four f16 values (round to nearest even) in one 8-byte agent-scope store.
+__device__ inline void store_coherent_h4(_Float16* dst, float a, float b, float c, float d) {
+  const v2h lo = {(_Float16)a, (_Float16)b}, hi = {(_Float16)c, (_Float16)d};
+  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint2 load_coherent_h4(const _Float16* src) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+
+__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
+__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
 
 // Cross-lane moves on the VALU (DPP and the gfx950 lane swaps) rather than LDS
 // permutes.  DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
@@ -697,9 +713,9 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       float mx, lsum;
       float4 o;
       merge(cr, cc, mx, lsum, o);
-      float* dst = p.part_o + (prow0 + cr) * kHeadDim + cc;
-      store_coherent(dst, o.x, o.y);
-      store_coherent(dst + 2, o.z, o.w);
+      // o / l is a weighted mean of V codes (|.| <= 448): f16 holds it.
+      const float rl = lsum > 0.0f ? __builtin_amdgcn_rcpf(lsum) : 0.0f;
+      store_coherent_h4(p.part_o + (prow0 + cr) * kHeadDim + cc, o.x * rl, o.y * rl, o.z * rl, o.w * rl);
       if (cc == 0) store_coherent(p.part_ml + (prow0 + cr) * 2, mx, lsum);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
@@ -756,19 +772,19 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     }
   }
   for (int s0 = 0; p.splits > 1 && s0 < p.splits; s0 += KS) {
-    float2 ml[TPT][KS], o01[TPT][KS], o23[TPT][KS];
+    float2 ml[TPT][KS];
+    uint2 oh[TPT][KS];
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
         const int ti = th + TS * k;
         ml[k][q] = make_float2(-INFINITY, 0.0f);
-        o01[k][q] = o23[k][q] = make_float2(0.0f, 0.0f);
+        oh[k][q] = make_uint2(0, 0);
         if (ti < t_n && s0 + q < p.splits) {
           const int64_t pr = base + (int64_t)(s0 + q) * stride + ti * kQHeads;
           ml[k][q] = load_coherent(p.part_ml + pr * 2);
-          o01[k][q] = load_coherent(p.part_o + pr * kHeadDim + c4);
-          o23[k][q] = load_coherent(p.part_o + pr * kHeadDim + c4 + 2);
+          oh[k][q] = load_coherent_h4(p.part_o + pr * kHeadDim + c4);
         }
       }
     }
@@ -784,12 +800,13 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       for (int c = 0; c < 4; ++c) o[k][c] *= a;
 #pragma unroll
       for (int q = 0; q < KS; ++q) {
-        const float wk = __builtin_amdgcn_exp2f(ml[k][q].x - muse);
-        lrun[k] += wk * ml[k][q].y;
-        o[k][0] += wk * o01[k][q].x;
-        o[k][1] += wk * o01[k][q].y;
-        o[k][2] += wk * o23[k][q].x;
-        o[k][3] += wk * o23[k][q].y;
+        // A split's weight is its l times 2^(m - max); its partial is o / l.
+        const float wk = __builtin_amdgcn_exp2f(ml[k][q].x - muse) * ml[k][q].y;
+        lrun[k] += wk;
+        o[k][0] += wk * h_lo(oh[k][q].x);
+        o[k][1] += wk * h_hi(oh[k][q].x);
+        o[k][2] += wk * h_lo(oh[k][q].y);
+        o[k][3] += wk * h_hi(oh[k][q].y);
       }
       mrun[k] = mc;
     }

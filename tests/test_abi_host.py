@@ -88,7 +88,7 @@ def test_prepare_plan_workspace_layout(L):
         T = 32 * 8
         q = T * 16 * 64
         po = -(-q // 256) * 256
-        pml = -(-(po + s * T * 16 * 64 * 4) // 256) * 256
+        pml = -(-(po + s * T * 16 * 64 * 2) // 256) * 256  # partial o / l: f16
         cnt = -(-(pml + s * T * 16 * 2 * 4) // 256) * 256
         assert ws == -(-(cnt + 32 * 4 * 4) // 256) * 256  # window 2048: four token groups of two
         ws0, s0 = ga.mi355x_gated_attn_plan(ctx, 32776, 0)
@@ -230,7 +230,7 @@ def test_short_key_ranges_use_groups_of_two_tokens(L):
             ws, s = ga.mi355x_gated_attn_plan(ctx, max_context, 2)
             T = 7 * Lq
             po = -(-(T * 16 * 64) // 256) * 256
-            pml = -(-(po + s * T * 16 * 64 * 4) // 256) * 256
+            pml = -(-(po + s * T * 16 * 64 * 2) // 256) * 256  # partial o / l: f16
             cnt = -(-(pml + s * T * 16 * 2 * 4) // 256) * 256
             assert ws == -(-(cnt + 7 * groups * 4) // 256) * 256, (Lq, max_context)
         finally:
