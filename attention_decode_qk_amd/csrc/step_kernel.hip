@@ -582,10 +582,15 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     v8h va0[NG][4], va1[NG][4];
     v_operand(bufA, va0);
     v_operand(bufB, va1);
-    bufA = load_block(pa, bi + 2);
-    bufB = load_block(pb, bi + 3);
-    pa = load_pte(bi + 4);
-    pb = load_pte(bi + 5);
+    // The next pair's loads (wave-uniform branch): a wave's last pair issues
+    // none, which spares a short chunk (a decode window: one pair per wave)
+    // re-reading its blocks behind the softmax in issue order.
+    if (bi + 2 < nb) {
+      bufA = load_block(pa, bi + 2);
+      bufB = load_block(pb, bi + 3);
+      pa = load_pte(bi + 4);
+      pb = load_pte(bi + 5);
+    }
     mask(kb0, z0);
     mask(kb1, z1);
 #pragma unroll
