@@ -39,6 +39,8 @@
 // each wave waits for its own stores to complete (s_waitcnt vmcnt(0)) before
 // the workgroup barrier that precedes the counter increment.  No L2 write-back
 // or invalidate is needed, unlike a generic device-scope fence.
+#include <type_traits>
+
 #include "kernels.h"
 #include "numerics.h"
 
@@ -361,10 +363,20 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 
   // Each block's page-table load follows the K/V loads two blocks earlier, so
   // waiting for it never waits for the next block's K/V.
+  // Units of one or two tokens issue block A's loads only: a wave's loads
+  // issue slowly once the compute unit's misses in flight reach their limit,
+  // and in-order issue would hold the q prologue behind block B's loads, which
+  // follow the prologue instead (their chunks are often one pair per wave).
+  // Larger units keep both blocks ahead of their longer prologue.
+  constexpr bool kLateB = LU <= 2;
   KvBlock<NG> bufA = load_block(pte0, 0);
   int2 pa = load_pte(2);
-  KvBlock<NG> bufB = load_block(pte1, 1);
-  int2 pb = load_pte(3);
+  KvBlock<NG> bufB;
+  int2 pb;
+  if constexpr (!kLateB) {
+    bufB = load_block(pte1, 1);
+    pb = load_pte(3);
+  }
   // The small values are taken only now (the compiler would otherwise move
   // them, uniform ones into scalar registers, right after their loads, and
   // that wait would also wait for the page table's slower neighbours).
@@ -565,81 +577,164 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     }
   };
 
-  // Blocks are taken in pairs: the scores and V^T operands of both, then the
-  // next pair's loads are issued, then per KV head one running-max decision for
-  // the pair and P / PV for both.  Scores stay raw (q.k): the scale (> 0) goes
-  // into the exponent's fma, so the maximum is taken on raw scores.
-  for (int bi = 0; bi < nb; bi += 2) {
-    const bool has_b = bi + 1 < nb;
-    // An absent second block sits past the chunk: every key masked, no codes substituted.
-    const int kb0 = start + (kw + KW * bi) * kKeyBlock;
-    const int kb1 = has_b ? kb0 + KW * kKeyBlock : end;
-    substitute(bufA, kb0);
-    if (has_b) substitute(bufB, kb1);
-    float z0[NG][NRB][8], z1[NG][NRB][8];
-    qk(bufA, z0);
-    qk(bufB, z1);
-    v8h va0[NG][4], va1[NG][4];
-    v_operand(bufA, va0);
-    v_operand(bufB, va1);
-    // The next pair's loads (wave-uniform branch): a wave's last pair issues
-    // none, which spares a short chunk (a decode window: one pair per wave)
-    // re-reading its blocks behind the softmax in issue order.
-    if (bi + 2 < nb) {
-      bufA = load_block(pa, bi + 2);
-      bufB = load_block(pb, bi + 3);
-      pa = load_pte(bi + 4);
-      pb = load_pte(bi + 5);
+  if constexpr (kLateB) {
+    bufB = load_block(pte1, 1);
+    pb = load_pte(3);
+  }
+
+  // Scores of one block -> running max -> P and PV, for KV head g.  z holds
+  // raw q.k for NB blocks (the lazy max decision covers them all).
+  auto softmax_pv = [&](int g, auto& zs, auto& vas, auto nblocks) {
+    constexpr int NB = decltype(nblocks)::value;
+    float lmx[NRB];     // this lane's scaled maximum over its keys of the blocks
+    bool grow = false;  // some lane's maximum passes its row's lazy bound
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const float* u = zs[q][g][rb];
+        m = fmax3(m, fmax3(u[0], u[1], u[2]), fmax3(u[3], u[4], u[5]));
+        m = fmax3(m, u[6], u[7]);
+      }
+      lmx[rb] = m * scale;
+      grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
     }
-    mask(kb0, z0);
-    mask(kb1, z1);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      float lmx[NRB];     // this lane's scaled maximum over its 16 keys of the pair
-      bool grow = false;  // some lane's maximum passes its row's lazy bound
+    // A row's maximum moves only when its full maximum (over the four lane
+    // groups) passes the bound, which no lane's own maximum does in the common
+    // case: then nothing moves and the cross-lane reduction is skipped.
+    if (__any(grow)) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const float* u = z0[g][rb];
-        const float* v = z1[g][rb];
-        float m = fmax3(fmax3(u[0], u[1], u[2]), fmax3(u[3], u[4], u[5]), fmax3(u[6], u[7], v[0]));
-        m = fmax3(m, fmax3(v[1], v[2], v[3]), fmax3(v[4], v[5], v[6]));
-        lmx[rb] = fmax3(m, v[7], -INFINITY) * scale;
-        grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
-      }
-      // A row's maximum moves only when its full maximum (over the four lane
-      // groups) passes the bound, which no lane's own maximum does in the common
-      // case: then nothing moves and the cross-lane reduction is skipped.
-      if (__any(grow)) {
+        const float mx = rows_max(lmx[rb]);
+        const float mold = mrow[g][rb];
+        const float mnew = mx > mold + kLazyRescale ? mx : mold;
+        const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
+        lrow[g][rb] *= alpha;  // alpha is exactly 1 for a row that kept its maximum
 #pragma unroll
+        for (int c = 0; c < 4; ++c) acc[g][rb][c] *= alpha;
+        mrow[g][rb] = mnew;
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
+      v8h pv[NB];
+      float psum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(zs[q][g][rb][k], scale, nmuse));
+          psum += e;
+          pv[q][k] = (_Float16)e;
+        }
+      lrow[g][rb] += psum;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int q = 0; q < NB; ++q)
+          acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vas[q][g][c], pv[q], acc[g][rb][c], 0, 0, 0);
+    }
+  };
+  using One = std::integral_constant<int, 1>;
+  using Two = std::integral_constant<int, 2>;
+
+  // One block on its own: its scores, running max, P and PV.
+  auto one_block = [&](KvBlock<NG>& buf, const int kb) {
+    substitute(buf, kb);
+    float z[1][NG][NRB][8];
+    qk(buf, z[0]);
+    v8h va[1][NG][4];
+    v_operand(buf, va[0]);
+    mask(kb, z[0]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) softmax_pv(g, z, va, One{});
+  };
+
+  if (kLateB && nb <= 2) {
+    // A short chunk (at most one pair per wave): block A is processed while
+    // block B's rows are still arriving.
+    const int kb0 = start + kw * kKeyBlock;
+    if (nb > 0) one_block(bufA, kb0);
+    if (nb > 1) one_block(bufB, kb0 + KW * kKeyBlock);
+  } else {
+    // Blocks are taken in pairs: the scores and V^T operands of both, then the
+    // next pair's loads are issued, then per KV head one running-max decision for
+    // the pair and P / PV for both.  Scores stay raw (q.k): the scale (> 0) goes
+    // into the exponent's fma, so the maximum is taken on raw scores.
+    for (int bi = 0; bi < nb; bi += 2) {
+      const bool has_b = bi + 1 < nb;
+      // An absent second block sits past the chunk: every key masked, no codes substituted.
+      const int kb0 = start + (kw + KW * bi) * kKeyBlock;
+      const int kb1 = has_b ? kb0 + KW * kKeyBlock : end;
+      substitute(bufA, kb0);
+      if (has_b) substitute(bufB, kb1);
+      float z0[NG][NRB][8], z1[NG][NRB][8];
+      qk(bufA, z0);
+      qk(bufB, z1);
+      v8h va0[NG][4], va1[NG][4];
+      v_operand(bufA, va0);
+      v_operand(bufB, va1);
+      // The next pair's loads (wave-uniform branch): a wave's last pair issues
+      // none, which spares a short chunk (a decode window: one pair per wave)
+      // re-reading its blocks behind the softmax in issue order.
+      if (bi + 2 < nb) {
+        bufA = load_block(pa, bi + 2);
+        bufB = load_block(pb, bi + 3);
+        pa = load_pte(bi + 4);
+        pb = load_pte(bi + 5);
+      }
+      mask(kb0, z0);
+      mask(kb1, z1);
+  #pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        float lmx[NRB];     // this lane's scaled maximum over its 16 keys of the pair
+        bool grow = false;  // some lane's maximum passes its row's lazy bound
+  #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-          const float mx = rows_max(lmx[rb]);
-          const float mold = mrow[g][rb];
-          const float mnew = mx > mold + kLazyRescale ? mx : mold;
-          const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
-          lrow[g][rb] *= alpha;  // alpha is exactly 1 for a row that kept its maximum
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[g][rb][c] *= alpha;
-          mrow[g][rb] = mnew;
+          const float* u = z0[g][rb];
+          const float* v = z1[g][rb];
+          float m = fmax3(fmax3(u[0], u[1], u[2]), fmax3(u[3], u[4], u[5]), fmax3(u[6], u[7], v[0]));
+          m = fmax3(m, fmax3(v[1], v[2], v[3]), fmax3(v[4], v[5], v[6]));
+          lmx[rb] = fmax3(m, v[7], -INFINITY) * scale;
+          grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
         }
-      }
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) {
-        const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
-        v8h p0v, p1v;
-        float psum = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z0[g][rb][k], scale, nmuse));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z1[g][rb][k], scale, nmuse));
-          psum += e0 + e1;
-          p0v[k] = (_Float16)e0;
-          p1v[k] = (_Float16)e1;
+        // A row's maximum moves only when its full maximum (over the four lane
+        // groups) passes the bound, which no lane's own maximum does in the common
+        // case: then nothing moves and the cross-lane reduction is skipped.
+        if (__any(grow)) {
+  #pragma unroll
+          for (int rb = 0; rb < NRB; ++rb) {
+            const float mx = rows_max(lmx[rb]);
+            const float mold = mrow[g][rb];
+            const float mnew = mx > mold + kLazyRescale ? mx : mold;
+            const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
+            lrow[g][rb] *= alpha;  // alpha is exactly 1 for a row that kept its maximum
+  #pragma unroll
+            for (int c = 0; c < 4; ++c) acc[g][rb][c] *= alpha;
+            mrow[g][rb] = mnew;
+          }
         }
-        lrow[g][rb] += psum;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0[g][c], p0v, acc[g][rb][c], 0, 0, 0);
-          acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1[g][c], p1v, acc[g][rb][c], 0, 0, 0);
+  #pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
+          v8h p0v, p1v;
+          float psum = 0.0f;
+  #pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z0[g][rb][k], scale, nmuse));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z1[g][rb][k], scale, nmuse));
+            psum += e0 + e1;
+            p0v[k] = (_Float16)e0;
+            p1v[k] = (_Float16)e1;
+          }
+          lrow[g][rb] += psum;
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0[g][c], p0v, acc[g][rb][c], 0, 0, 0);
+            acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va1[g][c], p1v, acc[g][rb][c], 0, 0, 0);
+          }
         }
       }
     }
