@@ -77,6 +77,12 @@ def lib():
                                ctypes.c_float, P, P, P]
         for f in ("orc_prologue", "orc_attention", "orc_epilogue", "orc_step"):
             getattr(L, f).restype = ctypes.c_int
+        L.orc_fp16_to_double.restype = ctypes.c_double
+        L.orc_fp16_to_double.argtypes = [ctypes.c_uint16]
+        L.orc_fp16_round.restype = ctypes.c_uint16
+        L.orc_fp16_round.argtypes = [ctypes.c_double]
+        L.orc_qk_norm.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_float, ctypes.c_float, P]
         _lib = L
     return _lib
 
@@ -224,3 +230,30 @@ def step(cfg: Config, qkv, positions, cache_loc, cache_seqlens, page_table, k_ca
                           float(k_scale), float(v_scale), _p(q), _p(o), _p(out)), "step")
     return (q, out.reshape(cfg.batch, cfg.q_len, cfg.num_q_heads * cfg.head_dim),
             o.reshape(T, cfg.num_q_heads, cfg.head_dim))
+
+
+# Page "qk_norm" (vLLM's CuTeDSL fused QK-norm): the plain definition, see
+# orc_qk_norm in oracle.c.
+QK_BF16, QK_FP16 = 0, 1
+
+
+def fp16_round(x: float) -> int:
+    """Binary16 bit pattern of x rounded to nearest, ties to even."""
+    return int(lib().orc_fp16_round(float(x)))
+
+
+def fp16_to_float(h: int) -> float:
+    return float(lib().orc_fp16_to_double(int(h)))
+
+
+def qk_norm(x: np.ndarray, num_heads: int, head_dim: int, dtype: int, eps: float = 1e-5,
+            scale: float = 1.0) -> np.ndarray:
+    """x: uint16 bit patterns [M, row_stride] (bf16 or fp16 per dtype); the
+    first num_heads * head_dim columns of each row are normed.  Returns the
+    uint16 bit patterns of the [M, num_heads * head_dim] output."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    M, stride = x.shape
+    out = np.zeros((M, num_heads * head_dim), np.uint16)
+    _check(lib().orc_qk_norm(_p(x), M, num_heads, head_dim, stride, dtype, ctypes.c_float(eps),
+                             ctypes.c_float(scale), _p(out)), "orc_qk_norm")
+    return out

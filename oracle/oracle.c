@@ -500,3 +500,83 @@ int orc_step_meta(const orc_config* cfg, const int32_t* seq_lens, const int32_t*
   }
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Page "qk_norm" (vLLM's CuTeDSL fused QK-norm for MuseSpark1x attention):  */
+/* the `qk_norm` function and the kernel of its `QKNormDirectKernel` class.  */
+/* Each head_dim-wide group of a row of x [M, heads * head_dim] (rows        */
+/* `row_stride` elements apart, the last dimension contiguous) is normed     */
+/* without a weight: rstd = rsqrt(sum of squares / head_dim + eps); the      */
+/* kernel keeps x * rstd in fp32, multiplies by the output scale when one is */
+/* given, and rounds once, on the store, to the input's 16-bit type.         */
+/* READING: the page's fp32 sum and fastmath rsqrt are taken exactly: the    */
+/* sum of squares (each square exact in fp32) is formed in double and        */
+/* rounded once to fp32, and rsqrt is correctly rounded; the divide by       */
+/* head_dim and the + eps are fp32 operations.  The scale multiplies only    */
+/* when it is not 1 (the page compiles the product out otherwise; a product  */
+/* by 1 changes nothing either way).                                         */
+/* ------------------------------------------------------------------------ */
+
+/* IEEE binary16 bit pattern -> value (exact). */
+double orc_fp16_to_double(uint16_t h) {
+  const int s = h >> 15, e = (h >> 10) & 0x1F, m = h & 0x3FF;
+  double v;
+  if (e == 0x1F) v = m ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)m, -24); /* subnormal: quantum 2^-24 */
+  else v = ldexp(1024.0 + (double)m, e - 25);
+  return s ? -v : v;
+}
+
+/* Round a real number to binary16, to nearest with ties to even.  Written
+ * from the format: 11 significant bits, normal exponents down to 2^-14,
+ * subnormal quantum 2^-24, largest finite 65504; from the halfway point
+ * 65520 up the result is infinity. */
+uint16_t orc_fp16_round(double x) {
+  if (isnan(x)) return 0x7E00;
+  const uint16_t sign = signbit(x) ? 0x8000 : 0;
+  const double ax = fabs(x);
+  if (ax >= 65520.0) return sign | 0x7C00;
+  if (ax == 0.0) return sign;
+  int e;
+  frexp(ax, &e); /* leading bit 2^(e-1) */
+  int lead = e - 1;
+  if (lead < -14) lead = -14;
+  const double quantum = ldexp(1.0, lead - 10);
+  const double q = nearbyint(ax / quantum); /* ties to even */
+  const double r = q * quantum;
+  if (r < ldexp(1.0, -14)) return sign | (uint16_t)q; /* subnormal (q < 1024) */
+  int re;
+  frexp(r, &re);
+  const int rl = re - 1; /* rounding may carry into the next binade */
+  const double mant = r / ldexp(1.0, rl) - 1.0;
+  return sign | (uint16_t)(((rl + 15) << 10) | (int)nearbyint(mant * 1024.0));
+}
+
+/* dtype 0: bfloat16, 1: binary16. */
+int orc_qk_norm(const uint16_t* x, int64_t M, int32_t num_heads, int32_t head_dim,
+                int64_t row_stride, int32_t dtype, float eps, float scale, uint16_t* out) {
+  if (M < 0 || num_heads < 1 || head_dim < 1 || (dtype != 0 && dtype != 1) ||
+      row_stride < (int64_t)num_heads * head_dim)
+    return ORC_BAD_ARG;
+  const int64_t n = (int64_t)num_heads * head_dim;
+  for (int64_t r = 0; r < M; ++r) {
+    for (int32_t h = 0; h < num_heads; ++h) {
+      const uint16_t* xs = x + r * row_stride + (int64_t)h * head_dim;
+      uint16_t* os = out + r * n + (int64_t)h * head_dim;
+      double ss = 0.0;
+      for (int32_t c = 0; c < head_dim; ++c) {
+        const float v = dtype ? (float)orc_fp16_to_double(xs[c]) : orc_bf16_to_float(xs[c]);
+        ss += (double)(v * v);
+      }
+      const float ms = (float)ss / (float)head_dim;
+      const float rstd = orc_rsqrt_cr(ms + eps);
+      for (int32_t c = 0; c < head_dim; ++c) {
+        const float v = dtype ? (float)orc_fp16_to_double(xs[c]) : orc_bf16_to_float(xs[c]);
+        float y = v * rstd;
+        if (scale != 1.0f) y = y * scale;
+        os[c] = dtype ? orc_fp16_round((double)y) : orc_bf16_round((double)y);
+      }
+    }
+  }
+  return ORC_OK;
+}
