@@ -24,7 +24,11 @@ MI355X_GA_HIP_ERROR = 4
 EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_gated_attn_plan",
             "mi355x_gated_attn_workspace_init", "mi355x_gated_attn_step", "mi355x_gated_attn_destroy",
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
-            "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta"]
+            "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta",
+            "mi355x_qk_norm_supports", "mi355x_qk_norm"]
+
+MI355X_QKN_BF16 = 0
+MI355X_QKN_FP16 = 1
 
 
 class GatedAttnError(RuntimeError):
@@ -71,6 +75,9 @@ def lib() -> ctypes.CDLL:
         L.mi355x_gated_attn_timing.argtypes = [P, ctypes.c_int]
         L.mi355x_gated_attn_timing_read.argtypes = [P, ctypes.POINTER(ctypes.c_double),
                                                     ctypes.POINTER(ctypes.c_int64)]
+        L.mi355x_qk_norm_supports.argtypes = [ctypes.c_int32, ctypes.c_int32]
+        L.mi355x_qk_norm.argtypes = [P, P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_float, P]
         for name in EXPORTED:
             if name not in ("mi355x_gated_attn_destroy", "mi355x_gated_attn_last_error"):
                 getattr(L, name).restype = ctypes.c_int
@@ -234,3 +241,57 @@ class GatedAttnStep:
             self.close()
         except Exception:
             pass
+
+
+# ---- per-head QK-norm with an output scale (page "qk_norm") ----------------
+
+def mi355x_qk_norm_supports(dtype: int, head_dim: int) -> bool:
+    return bool(lib().mi355x_qk_norm_supports(int(dtype), int(head_dim)))
+
+
+def mi355x_qk_norm(x, out, M: int, num_heads: int, head_dim: int, x_row_stride: int, dtype: int,
+                   eps: float = 1e-5, scale: float = 1.0, stream=None):
+    """Raw entry point: x and out are device pointers (ints) or None."""
+    _check(lib().mi355x_qk_norm(x, out, int(M), int(num_heads), int(head_dim), int(x_row_stride),
+                                int(dtype), ctypes.c_float(eps), ctypes.c_float(scale), stream))
+
+
+def _qk_dtype(dtype) -> int:
+    import torch
+    if dtype == torch.bfloat16:
+        return MI355X_QKN_BF16
+    if dtype == torch.float16:
+        return MI355X_QKN_FP16
+    return -1
+
+
+def supports_qk_norm(dtype, head_dim: int) -> bool:
+    """Whether qk_norm serves a torch dtype and head_dim (the page's
+    supports_qk_norm)."""
+    d = _qk_dtype(dtype)
+    return d >= 0 and mi355x_qk_norm_supports(d, head_dim)
+
+
+def qk_norm(x, head_dim: int, eps: float = 1e-5, scale: float = 1.0, out=None, stream=None):
+    """The page's qk_norm(x, head_dim, eps, scale): x is [num_tokens,
+    num_heads * head_dim] (bf16 or fp16, last dimension contiguous, rows may be
+    strided); returns a new contiguous tensor of the same shape and type."""
+    import torch
+    if x.dim() != 2:
+        raise ValueError("x must be [num_tokens, num_heads * head_dim]")
+    if x.stride(1) != 1:
+        raise ValueError("x must be contiguous along its last dim")
+    M, N = x.shape
+    if N % head_dim:
+        raise ValueError(f"{N} is not a multiple of head_dim={head_dim}")
+    d = _qk_dtype(x.dtype)
+    if d < 0 or not mi355x_qk_norm_supports(d, head_dim):
+        raise GatedAttnError(MI355X_GA_UNSUPPORTED, f"qk_norm does not serve {x.dtype} with head_dim {head_dim}")
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    if M == 0:
+        return out
+    s = stream if stream is not None else torch.cuda.current_stream(x.device).cuda_stream
+    mi355x_qk_norm(x.data_ptr(), out.data_ptr(), M, N // head_dim, head_dim, x.stride(0), d, eps,
+                   scale, s)
+    return out

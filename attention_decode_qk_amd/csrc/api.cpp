@@ -369,3 +369,42 @@ int mi355x_gated_attn_timing_read(mi355x_gated_attn_ctx* ctx, double* kernel_ms,
 }
 
 }  // extern "C"
+
+extern "C" int mi355x_qk_norm_supports(int32_t dtype, int32_t head_dim) {
+  // The page's launch-shape table gives 8, 16 or 32 threads of eight 16-bit
+  // values per head for head_dim up to 64, 128 and 3072, and more threads
+  // (never matching) beyond: with no tail path, 64, 128 and 256 are served.
+  if (dtype != MI355X_QKN_BF16 && dtype != MI355X_QKN_FP16) return 0;
+  return head_dim == 64 || head_dim == 128 || head_dim == 256;
+}
+
+extern "C" int mi355x_qk_norm(const void* x, void* out, int64_t M, int32_t num_heads,
+                              int32_t head_dim, int64_t x_row_stride, int32_t dtype, float eps,
+                              float scale, void* stream) {
+  if (!mi355x_qk_norm_supports(dtype, head_dim))
+    return fail(MI355X_GA_UNSUPPORTED, "qk_norm serves bf16/fp16 with head_dim 64, 128 or 256 (got dtype %d, head_dim %d)",
+                dtype, head_dim);
+  if (M < 0) return fail(MI355X_GA_INVALID_ARGUMENT, "M = %lld < 0", (long long)M);
+  if (num_heads < 1) return fail(MI355X_GA_INVALID_ARGUMENT, "num_heads = %d < 1", num_heads);
+  const int64_t n = (int64_t)num_heads * head_dim;
+  if (x_row_stride < n || x_row_stride % 8)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "x_row_stride %lld: must be a multiple of 8 and >= %lld",
+                (long long)x_row_stride, (long long)n);
+  if (M == 0) return ok();
+  if (!x || !out) return fail(MI355X_GA_INVALID_ARGUMENT, "x or out is NULL");
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "x and out must be 16-byte aligned");
+  QkNormParams p;
+  p.x = static_cast<const uint16_t*>(x);
+  p.out = static_cast<uint16_t*>(out);
+  p.rows = M;
+  p.row_stride = x_row_stride;
+  p.heads = num_heads;
+  p.head_dim = head_dim;
+  p.fp16 = dtype == MI355X_QKN_FP16;
+  p.eps = eps;
+  p.scale = scale;
+  const hipError_t e = launch_qk_norm(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "qk_norm launch: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -75,6 +75,21 @@ struct StepParams {
 
 hipError_t launch_step(const StepParams& p, hipStream_t stream);
 
+// Per-head RMSNorm with an output scale (qk_norm_kernel.hip).
+struct QkNormParams {
+  const uint16_t* x;   // bf16 or fp16 [rows, row_stride], 16-byte aligned rows
+  uint16_t* out;       // same type [rows, heads * head_dim]
+  int64_t rows;
+  int64_t row_stride;  // elements between rows of x (a multiple of 8)
+  int32_t heads;
+  int32_t head_dim;    // 64, 128 or 256
+  int32_t fp16;        // 1: binary16, 0: bfloat16
+  float eps;
+  float scale;         // the product is skipped when 1
+};
+
+hipError_t launch_qk_norm(const QkNormParams& p, hipStream_t stream);
+
 // Per-step metadata shared by every layer (meta_kernel.hip).
 struct MetaParams {
   const int32_t* seq_lens;       // [B]

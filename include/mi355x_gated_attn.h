@@ -204,6 +204,52 @@ int mi355x_gated_attn_timing(mi355x_gated_attn_ctx* ctx, int enable);
 int mi355x_gated_attn_timing_read(mi355x_gated_attn_ctx* ctx, double* kernel_ms,
                                   int64_t* steps);
 
+/* ---- Per-head QK-norm with an output scale --------------------------------
+ * The operation of the page "qk_norm" (vLLM's CuTeDSL fused QK-norm for
+ * MuseSpark1x attention: the qk_norm function, QKNormDirectKernel's kernel and
+ * supports_qk_norm).  Independent of any ctx. */
+
+/* Element types of the QK-norm input and output. */
+enum { MI355X_QKN_BF16 = 0, MI355X_QKN_FP16 = 1 };
+
+/*
+ * Whether mi355x_qk_norm serves (dtype, head_dim): 1 if it does, 0 if not.
+ * On the page a head is covered by a fixed number of threads per row (chosen
+ * from head_dim by the launch-shape table of _DirectConfig) holding eight
+ * 16-bit values each, with no tail path; for 16-bit types that leaves
+ * head_dim 64, 128 and 256.  This build serves the same set, for bfloat16 and
+ * binary16.
+ */
+int mi355x_qk_norm_supports(int32_t dtype, int32_t head_dim);
+
+/*
+ * Unweighted RMSNorm of every head_dim-wide group plus an output scale.  For
+ * row r < M and head h < num_heads, with v[c] = x[r * x_row_stride +
+ * h * head_dim + c], c < head_dim:
+ *   rstd = 1 / sqrt(sum_c v[c]^2 / head_dim + eps)
+ *   out[r * num_heads * head_dim + h * head_dim + c] = round(v[c] * rstd * scale)
+ * rstd is fp32 (the sum of squares formed exactly and rounded once, the
+ * quotient and + eps in fp32, rsqrt correctly rounded); the products are fp32,
+ * the one by scale only when scale != 1; round is to nearest even in dtype and
+ * is the only rounding.
+ *   x             device, dtype [M, x_row_stride]: only the first
+ *                 num_heads * head_dim columns of each row are read; 16-byte
+ *                 aligned, x_row_stride (elements) a multiple of 8 and
+ *                 >= num_heads * head_dim (a strided view of a wider row, such
+ *                 as the q columns of a fused projection, is served as is)
+ *   out           device, dtype [M, num_heads * head_dim], 16-byte aligned;
+ *                 must not overlap x
+ *   M             rows >= 0; M == 0 returns MI355X_GA_OK with no launch
+ *   stream        hipStream_t (NULL: the null stream); the call is asynchronous
+ *                 on it and allocates nothing
+ * Caller-owned memory throughout.  Returns MI355X_GA_UNSUPPORTED when
+ * mi355x_qk_norm_supports(dtype, head_dim) is 0; MI355X_GA_INVALID_ARGUMENT
+ * for M < 0, num_heads < 1, a short or unaligned row stride, or (M > 0) a NULL
+ * or misaligned pointer; MI355X_GA_HIP_ERROR when the launch fails.
+ */
+int mi355x_qk_norm(const void* x, void* out, int64_t M, int32_t num_heads, int32_t head_dim,
+                   int64_t x_row_stride, int32_t dtype, float eps, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

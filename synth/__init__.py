@@ -177,3 +177,46 @@ def small(name: str = "small", batch: int = 3, q_len: int = 1, seq_lo: int = 40,
 def with_seed(w: Workload, seed: int) -> Workload:
     return replace(w, seed=seed)
 
+
+
+# ---- inputs of the per-head QK-norm (page "qk_norm") --------------------------
+
+def to_fp16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> binary16 bit patterns via torch's cast (round to nearest even)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+@dataclass(frozen=True)
+class QkNormWorkload:
+    name: str
+    rows: int          # tokens
+    num_heads: int
+    head_dim: int
+    row_stride: int    # elements between rows of x (>= num_heads * head_dim)
+    dtype: str         # "bf16" or "fp16"
+    scale: float       # the output scale
+    std: float = 1.0   # x ~ N(0, std^2), cast once
+    eps: float = 1e-5
+    seed: int = 0
+
+
+# The page's qk_norm reads a strided view such as the q columns of the fused
+# projection row (2304 wide per GPU on page "012-attention-local-splits.py",
+# q first); the q scale 5.473 is that page's query factor, folded into q.
+QK_NORM_WORKLOADS = {
+    "qk_norm_q_prefill": QkNormWorkload("qk_norm_q_prefill", 16384, 16, 64, 2304, "bf16", 5.473,
+                                        seed=2001),
+    "qk_norm_q_decode": QkNormWorkload("qk_norm_q_decode", 32, 16, 64, 2304, "bf16", 5.473,
+                                       seed=2002),
+    "qk_norm_fp16_d256": QkNormWorkload("qk_norm_fp16_d256", 8192, 8, 256, 2048, "fp16", 1.0,
+                                        seed=2003),
+}
+
+
+def make_qk_norm_input(w: QkNormWorkload, rows: int | None = None) -> np.ndarray:
+    """uint16 bit patterns [rows, row_stride] of N(0, std^2) values in w.dtype."""
+    rng = np.random.default_rng(w.seed)
+    n = w.rows if rows is None else rows
+    x = rng.standard_normal((n, w.row_stride), dtype=np.float32) * np.float32(w.std)
+    return to_bf16_bits(x) if w.dtype == "bf16" else to_fp16_bits(x)

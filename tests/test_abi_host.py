@@ -27,7 +27,7 @@ def _declared_symbols():
         if f.endswith(".h"):
             text = open(os.path.join(inc, f)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names |= set(re.findall(r"\b(mi355x_gated_attn_\w+)\s*\(", text))
+            names |= set(re.findall(r"\b(mi355x_(?:gated_attn|qk_norm)\w*)\s*\(", text))
     return names
 
 
@@ -255,3 +255,50 @@ def test_step_meta_validates_before_launch(L):
         assert L.mi355x_gated_attn_step_meta(ctx, None, None, None, None, None, None) == ga.MI355X_GA_OK
     finally:
         ga.mi355x_gated_attn_destroy(ctx)
+
+
+# ---- per-head QK-norm (page "qk_norm") ---------------------------------------
+
+def test_qk_norm_serves_the_pages_head_dims(L):
+    """The page's launch-shape table covers a head with 8, 16 or 32 threads of
+    eight 16-bit values (no tail path): head_dim 64, 128, 256 for bf16/fp16."""
+    served = {(d, h) for d in (0, 1, 2, -1) for h in range(1, 600)
+              if ga.mi355x_qk_norm_supports(d, h)}
+    assert served == {(d, h) for d in (0, 1) for h in (64, 128, 256)}
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), 1), (dict(dtype=2), 1),
+    (dict(M=-1), 2), (dict(num_heads=0), 2),
+    (dict(x_row_stride=1000), 2),                 # shorter than 16 * 64
+    (dict(x_row_stride=1028), 2),                 # not a multiple of 8
+    (dict(x=None), 2), (dict(out=None), 2),       # NULL with M > 0
+    (dict(x=0x1008), 2), (dict(out=0x2004), 2),   # not 16-byte aligned
+])
+def test_qk_norm_rejects_bad_arguments_before_any_launch(L, kw, status):
+    args = dict(x=0x1000, out=0x2000, M=4, num_heads=16, head_dim=64, x_row_stride=2304, dtype=0,
+                eps=1e-5, scale=1.0, stream=None)
+    args.update(kw)
+    rc = L.mi355x_qk_norm(args["x"], args["out"], args["M"], args["num_heads"], args["head_dim"],
+                          args["x_row_stride"], args["dtype"], ctypes.c_float(args["eps"]),
+                          ctypes.c_float(args["scale"]), args["stream"])
+    assert rc == status
+    assert ga.mi355x_gated_attn_last_error() != ""
+
+
+def test_qk_norm_of_no_rows_is_a_no_op(L):
+    assert L.mi355x_qk_norm(None, None, 0, 16, 64, 1024, 0, ctypes.c_float(1e-5),
+                            ctypes.c_float(5.473), None) == 0
+
+
+def test_qk_norm_binding_checks_shapes_like_the_page():
+    import torch
+    x = torch.zeros((4, 100), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        ga.qk_norm(x, 64)  # 100 is not a multiple of 64
+    with pytest.raises(ValueError):
+        ga.qk_norm(torch.zeros((4, 64, 2), dtype=torch.bfloat16), 64)
+    with pytest.raises(ga.GatedAttnError):
+        ga.qk_norm(torch.zeros((4, 128), dtype=torch.float32), 64)
+    assert ga.qk_norm(torch.zeros((0, 128), dtype=torch.bfloat16), 64).shape == (0, 128)
+    assert ga.supports_qk_norm(torch.float16, 256) and not ga.supports_qk_norm(torch.float32, 64)
