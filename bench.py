@@ -40,17 +40,28 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
+def _kernel_prefix(workload: str) -> str:
+    return "qk_norm" if workload.startswith("qk_norm") else "fused_step"
+
+
 def counters_file(workload: str) -> str:
     """The committed rocprofv3 counter summary of one workload."""
-    return os.path.join(ROOT, "profiles", f"fused_step_{workload}_counters.md")
-KERNEL_SOURCES = [os.path.join(ROOT, "attention_decode_qk_amd", "csrc", f)
-                  for f in ("step_kernel.hip", "kernels.h", "numerics.h")] + \
-                 [os.path.join(ROOT, "attention_decode_qk_amd", "build.py")]  # compiler flags
+    return os.path.join(ROOT, "profiles", f"{_kernel_prefix(workload)}_{workload}_counters.md")
 
 
-def kernel_source_hash() -> str:
+def _sources(kernel_file: str):
+    return [os.path.join(ROOT, "attention_decode_qk_amd", "csrc", f)
+            for f in (kernel_file, "kernels.h", "numerics.h")] + \
+           [os.path.join(ROOT, "attention_decode_qk_amd", "build.py")]  # compiler flags
+
+
+KERNEL_SOURCES = _sources("step_kernel.hip")
+QK_NORM_SOURCES = _sources("qk_norm_kernel.hip")
+
+
+def kernel_source_hash(files=None) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in files or KERNEL_SOURCES:
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -106,7 +117,8 @@ def load_traffic(workload: str):
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("kernel_source_sha256") != kernel_source_hash():
+    files = QK_NORM_SOURCES if workload.startswith("qk_norm") else KERNEL_SOURCES
+    if d.get("kernel_source_sha256") != kernel_source_hash(files):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -133,6 +145,110 @@ def cpu_baseline(x, budget_s: float):
     dt = time.perf_counter() - t0
     del np
     return n, dt
+
+
+def qk_norm_bytes(w) -> int:
+    """Algorithmic HBM bytes of one call: the normed columns read once, the
+    output written once."""
+    return 2 * w.rows * w.num_heads * w.head_dim * 2
+
+
+def run_qk_norm(args, w, dev):
+    """The per-head QK-norm (page "qk_norm") on its own: K calls round-robin
+    over enough input/output buffer pairs that one round touches the cold
+    bytes, graph-captured, one replay timed."""
+    import numpy as np
+    import torch
+
+    import attention_decode_qk_amd as ga
+    import synth
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    x0 = synth.make_qk_norm_input(w)
+    call_bytes = qk_norm_bytes(w)
+    pool_bytes = x0.nbytes + call_bytes // 2
+    n_pools = layer_pool_count(call_bytes, pool_bytes, args.cold_bytes * (1 << 30))
+    print(f"[bench] {w.name}: {w.rows} x {w.num_heads} x {w.head_dim} {w.dtype}, stride "
+          f"{w.row_stride}; {n_pools} buffer pairs", file=sys.stderr, flush=True)
+    base = torch.from_numpy(x0.view(np.int16)).to(dev).view(tdt)
+    xs, outs = [], []
+    for i in range(n_pools):
+        x = base if i == 0 else torch.roll(base, shifts=i, dims=0).contiguous()
+        xs.append(x[:, :w.num_heads * w.head_dim])
+        outs.append(torch.empty((w.rows, w.num_heads * w.head_dim), dtype=tdt, device=dev))
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+
+    def call(i, stream):
+        ga.qk_norm(xs[i], w.head_dim, eps=w.eps, scale=w.scale, out=outs[i], stream=stream.cuda_stream)
+
+    with torch.cuda.stream(cap):
+        for i in range(n_pools):
+            call(i, cap)
+    torch.cuda.synchronize()
+
+    def capture(n, rotate):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for k in range(n):
+                    call(k % n_pools if rotate else 0, cap)
+        return g
+
+    g_warm, g_cold, g_hot = capture(max(1, args.warmup), True), capture(args.steps, True), \
+        capture(args.steps, False)
+    torch.cuda.synchronize()
+
+    def timed(g):
+        g_warm.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    t0 = time.perf_counter()
+    us = 1000.0 * timed(g_cold) / args.steps
+    wall_s = time.perf_counter() - t0
+    us_warm = 1000.0 * timed(g_hot) / args.steps
+    achieved = call_bytes / (us * 1e-6) / 1e9
+    result = {
+        "metric": f"µs per call and HBM GB/s (% of peak), per-head QK-norm {w.name}",
+        "value": round(achieved, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(us / 1000.0, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "rows": w.rows, "num_heads": w.num_heads,
+                   "head_dim": w.head_dim, "row_stride": w.row_stride, "scale": w.scale,
+                   "buffer_pairs": n_pools, "touched_bytes_per_round": n_pools * call_bytes},
+        "us_per_call": round(us, 3),
+        "warm_single_buffer": {"us_per_call": round(us_warm, 3),
+                               "gbs": round(call_bytes / (us_warm * 1e-6) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(w.name), "algorithmic_bytes": call_bytes,
+                     "kernel": "qk_norm_kernel", "kernel_source": kernel_source_hash(QK_NORM_SOURCES)},
+        "timed_wall_s": round(wall_s, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        dt_code = oracle.QK_BF16 if w.dtype == "bf16" else oracle.QK_FP16
+        rows = max(1, min(w.rows, 4096))
+        sample = np.ascontiguousarray(x0[:rows])
+        n, t1 = 0, time.perf_counter()
+        while True:
+            oracle.qk_norm(sample, w.num_heads, w.head_dim, dt_code, eps=w.eps, scale=w.scale)
+            n += 1
+            if time.perf_counter() - t1 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t1
+        per = 2 * rows * w.num_heads * w.head_dim * 2
+        result["cpu_baseline"] = {"value": round(n * per / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": f"{n} calls on the first {rows} rows, single-threaded, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
 
 
 def main():
@@ -169,6 +285,10 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     dev = torch.device("cuda:0")
+
+    if args.workload in synth.QK_NORM_WORKLOADS:
+        run_qk_norm(args, synth.QK_NORM_WORKLOADS[args.workload], dev)
+        return
 
     if args.calibrate_copy:
         n = 1 << 30
