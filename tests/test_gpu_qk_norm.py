@@ -56,6 +56,11 @@ CASES = [
     ("fp16", 128, 4, 61, 512, 1.0, 2.0),
     ("fp16", 256, 2, 40, 520, 1.0, 1e-3),
     ("fp16", 256, 7, 9, 1792, 2.0, 0.5),
+    # more groups than one pass of the capped grid covers (the grid strides),
+    # one group per thread and four
+    ("bf16", 64, 16, 10000, 2304, 5.473, 1.0),
+    ("bf16", 64, 16, 20000, 1024, 1.0, 1.0),
+    ("fp16", 256, 8, 9000, 2048, 5.473, 1.0),
 ]
 
 
