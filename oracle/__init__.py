@@ -41,7 +41,8 @@ class _Cfg(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_pages", ctypes.c_int64), ("rope_theta", ctypes.c_float),
-                ("sm_scale", ctypes.c_float), ("kv_scale", ctypes.c_float)]
+                ("sm_scale", ctypes.c_float), ("kv_scale", ctypes.c_float),
+                ("q_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -103,11 +104,12 @@ class Config:
     rope_theta: float = 0.0
     sm_scale: float = 0.125
     kv_scale: float = 1.0
+    q_scale: float = 1.0  # q's norm output scale (page "qk_norm"); 1 = page 1
 
     def c(self) -> _Cfg:
         return _Cfg(self.batch, self.q_len, self.num_q_heads, self.num_kv_heads, self.head_dim,
                     self.page_size, self.window, self.max_pages, self.num_pages,
-                    self.rope_theta, self.sm_scale, self.kv_scale)
+                    self.rope_theta, self.sm_scale, self.kv_scale, self.q_scale)
 
 
 def _p(a: np.ndarray | None):

@@ -49,6 +49,8 @@ typedef struct {
   float rope_theta;     /* 0 = no RoPE                                         */
   float sm_scale;       /* applied softmax scale                               */
   float kv_scale;       /* != 1 selects the divided store / descaled read     */
+  float q_scale;        /* q's norm output scale before its one bf16 rounding */
+                        /*    (page "qk_norm"); 1 = page 1's prologue         */
 } orc_config;
 
 /* ------------------------------------------------------------------------ */
@@ -194,14 +196,16 @@ static int cfg_ok(const orc_config* c) {
   if (c->head_dim != 64) return 0;
   if (c->num_q_heads % c->num_kv_heads) return 0;
   if (c->page_size < 1 || c->window < 0 || c->max_pages < 0 || c->num_pages < 0) return 0;
+  if (!(c->q_scale > 0.0f) || isinf(c->q_scale)) return 0;
   return 1;
 }
 
 /* Per-head unweighted RMSNorm of one 64-wide bf16 row, page order:
  * fp32 sum of squares (each square is exact in fp32; the sum is formed exactly
  * in double and rounded once), /D, + 1e-5 in fp32, rsqrt, fp32 product,
- * bf16 rounding. */
-static void norm_row(const uint16_t* xin, int d, float* y_out, float* inv_out) {
+ * bf16 rounding.  With scale != 1 the fp32 product is multiplied by it before
+ * that one rounding (page "qk_norm": QKNormDirectKernel's output scale). */
+static void norm_row(const uint16_t* xin, int d, float scale, float* y_out, float* inv_out) {
   double ss = 0.0;
   for (int c = 0; c < d; ++c) {
     float x = orc_bf16_to_float(xin[c]);
@@ -213,6 +217,7 @@ static void norm_row(const uint16_t* xin, int d, float* y_out, float* inv_out) {
   for (int c = 0; c < d; ++c) {
     float x = orc_bf16_to_float(xin[c]);
     float prod = x * inv;
+    if (scale != 1.0f) prod = prod * scale;
     y_out[c] = bf16r(prod);
   }
   if (inv_out) *inv_out = inv;
@@ -241,7 +246,7 @@ static void rope_row(float* y, int d, int64_t pos, const float* inv_freq) {
  * y receives the bf16-valued results (exposed for the tests' pins). */
 void orc_norm_rope_row(const uint16_t* x, int d, int64_t pos, float theta, float* y) {
   float inv_freq[128];
-  norm_row(x, d, y, NULL);
+  norm_row(x, d, 1.0f, y, NULL);
   if (theta != 0.0f) {
     orc_inv_freq(theta, d, inv_freq);
     rope_row(y, d, pos, inv_freq);
@@ -276,7 +281,10 @@ int orc_prologue(const orc_config* cfg, const uint16_t* qkv, const int64_t* posi
      * request slot) stores nothing; its q is still produced. */
     const int store = slot >= 0 && slot < rows;
     for (int h = 0; h < hq + hkv; ++h) { /* q heads then k heads */
-      norm_row(row + (int64_t)h * d, d, y, NULL);
+      /* READING: the q scale (page "qk_norm", folding the query factor into q
+       * before its e4m3 cast) applies to the q heads' norm only; RoPE follows
+       * on the scaled, rounded values as on page 1. */
+      norm_row(row + (int64_t)h * d, d, h < hq ? cfg->q_scale : 1.0f, y, NULL);
       if (cfg->rope_theta != 0.0f) rope_row(y, d, positions[t], inv_freq);
       if (h < hq) {
         for (int c = 0; c < d; ++c) q_out[(t * hq + h) * d + c] = orc_e4m3_encode(y[c]);

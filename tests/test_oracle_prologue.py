@@ -159,3 +159,54 @@ def test_q_and_key_codes_match_torch_composition(orc, theta, kv_scale):
         # mismatches are one code apart
         assert np.all(np.abs(got.astype(int) - ref.astype(int))[neq] == 1)
         assert torch.all(torch.sign(vg) * torch.sign(vr) >= 0)
+
+
+# ---- q scale before the bf16 rounding (page "qk_norm": the output scale) ----
+
+def _q_codes(orc, w, q_scale, sm_scale=None):
+    x = synth.make_inputs(w)
+    cfg = orc.Config(batch=w.batch, q_len=w.q_len, page_size=w.page_size, window=w.window,
+                     max_pages=x.max_pages, num_pages=x.num_pages, rope_theta=w.rope_theta,
+                     sm_scale=w.sm_scale if sm_scale is None else sm_scale, kv_scale=w.kv_scale,
+                     q_scale=q_scale)
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    q = orc.prologue(cfg, x.qkv, x.positions, x.cache_loc, kc, vc, x.k_scale, x.v_scale)
+    return x, cfg, q, kc, vc
+
+
+@pytest.mark.parametrize("q_scale", [5.473, 0.37])
+def test_q_scale_without_rope_is_the_pages_qk_norm(orc, q_scale):
+    """Without RoPE, q's bf16 values are exactly the page's qk_norm of the q
+    columns with that output scale (the independently pinned function), and K
+    and V do not depend on the q scale."""
+    w = synth.small(batch=3, q_len=2, rope_theta=0.0, qkv_std=1.4)
+    x, cfg, q, kc, vc = _q_codes(orc, w, q_scale)
+    T = w.batch * w.q_len
+    rows = x.qkv.reshape(T, -1)
+    normed = orc.qk_norm(rows, 16, 64, orc.QK_BF16, eps=1e-5, scale=q_scale)
+    want = synth.to_e4m3_codes(_bits_to_f32(normed)).reshape(T, 16, 64)
+    assert np.array_equal(q, want)
+    _, _, q1, kc1, vc1 = _q_codes(orc, w, 1.0)
+    assert np.array_equal(kc, kc1) and np.array_equal(vc, vc1)
+    assert not np.array_equal(q, q1)
+
+
+def test_q_scale_moved_out_of_the_softmax_scale_keeps_the_output(orc):
+    """Scaling q by 2 and halving the softmax scale gives the same attention up to
+    e4m3's rounding of the doubled values (exact but in its subnormal band): the
+    unrounded attention outputs agree to 1e-3 (observed 1e-4), while a scale
+    applied twice moves them by more than 0.1 (observed 1.5)."""
+    w = synth.small(batch=2, q_len=3, rope_theta=500000.0, window=64, qkv_std=1.2)
+    outs = []
+    for qs, sm in ((1.0, w.sm_scale), (2.0, w.sm_scale / 2), (2.0, w.sm_scale)):
+        x = synth.make_inputs(w)
+        cfg = orc.Config(batch=w.batch, q_len=w.q_len, page_size=w.page_size, window=w.window,
+                         max_pages=x.max_pages, num_pages=x.num_pages, rope_theta=w.rope_theta,
+                         sm_scale=sm, kv_scale=w.kv_scale, q_scale=qs)
+        kc, vc = x.k_cache.copy(), x.v_cache.copy()
+        _, _, o = orc.step(cfg, x.qkv, x.positions, x.cache_loc, x.cache_seqlens, x.page_table,
+                           kc, vc, x.k_scale, x.v_scale)
+        outs.append(o)
+    ref, moved, doubled = outs
+    assert np.max(np.abs(moved - ref)) <= 1e-3
+    assert np.max(np.abs(doubled - ref)) > 0.1
