@@ -44,7 +44,8 @@ class Config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("page_size", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_pages", ctypes.c_int64), ("rope_theta", ctypes.c_float),
-                ("sm_scale", ctypes.c_float), ("kv_scale", ctypes.c_float)]
+                ("sm_scale", ctypes.c_float), ("kv_scale", ctypes.c_float),
+                ("q_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -96,9 +97,9 @@ def _check(rc: int):
 
 def make_config(batch, q_len, page_size, window, max_pages, num_pages, rope_theta=0.0,
                 sm_scale=0.125, kv_scale=1.0, num_q_heads=16, num_kv_heads=2,
-                head_dim=64) -> Config:
+                head_dim=64, q_scale=1.0) -> Config:
     return Config(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, window,
-                  max_pages, num_pages, rope_theta, sm_scale, kv_scale)
+                  max_pages, num_pages, rope_theta, sm_scale, kv_scale, q_scale)
 
 
 def mi355x_gated_attn_supports(cfg: Config) -> int:

@@ -113,6 +113,8 @@ int mi355x_gated_attn_supports(const mi355x_gated_attn_config* c) {
     return fail(MI355X_GA_INVALID_ARGUMENT, "sm_scale must be finite and positive");
   if (!(c->kv_scale > 0.0f) || std::isinf(c->kv_scale))
     return fail(MI355X_GA_INVALID_ARGUMENT, "kv_scale must be finite and positive");
+  if (!(c->q_scale > 0.0f) || std::isinf(c->q_scale))
+    return fail(MI355X_GA_INVALID_ARGUMENT, "q_scale must be finite and positive (1: none)");
   if (c->num_q_heads % c->num_kv_heads)
     return fail(MI355X_GA_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 c->num_q_heads, c->num_kv_heads);
@@ -313,6 +315,7 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   sp.scaled = scaled ? 1 : 0;
   sp.rope = rope ? 1 : 0;
   sp.sm_scale_log2 = c.sm_scale * 1.4426950408889634f;
+  sp.q_scale = c.q_scale;
   std::memcpy(sp.inv_freq, ctx->inv_freq, sizeof sp.inv_freq);
 
   hipEvent_t* ev = nullptr;

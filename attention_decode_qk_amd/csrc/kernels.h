@@ -70,6 +70,7 @@ struct StepParams {
   int32_t scaled;                // 1 iff kv_scale != 1
   int32_t rope;                  // 1 iff rope_theta != 0
   float sm_scale_log2;           // sm_scale * log2(e)
+  float q_scale;                 // q's norm output scale before its bf16 rounding (1: none)
   float inv_freq[kHeadDim / 2];
 };
 

@@ -214,10 +214,10 @@ __device__ inline KvBlock<NG> load_kv(const StepParams& p, int2 entry, int kk, i
 
 // Norm (+ RoPE) of one 8-column slice of a head row, page order, every fp32 step
 // rounded once (no contraction): fp64-exact sum of squares over the 8 lanes of
-// the row, exact rsqrt, fp32 product, bf16; RoPE pairs (2i, 2i+1) with fp32
-// products and sum, bf16.
+// the row, exact rsqrt, fp32 product (times `scale`, exact when 1), bf16; RoPE
+// pairs (2i, 2i+1) with fp32 products and sum, bf16.
 __device__ inline void norm_rope8(const float (&x)[8], bool rope, const float (*cs)[2], int c8,
-                                  float (&y)[8]) {
+                                  float scale, float (&y)[8]) {
 #pragma clang fp contract(off)
   double ss = 0.0;
 #pragma unroll
@@ -226,7 +226,13 @@ __device__ inline void norm_rope8(const float (&x)[8], bool rope, const float (*
   const float ms = (float)ss / 64.0f;
   const float inv = rsqrt_exact(ms + 1.0e-5f);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = round_bf16(x[k] * inv);
+  for (int k = 0; k < 8; ++k) y[k] = x[k] * inv;
+  if (scale != 1.0f) {  // page 1's norm (scale 1) skips the product
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = y[k] * scale;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k]);
   if (rope) {
 #pragma unroll
     for (int pr = 0; pr < 4; ++pr) {
@@ -416,7 +422,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       x[2 * k + 1] = bf16_value(w[k] >> 16);
     }
     if (hr < kQHeads + kKvHeads) {
-      norm_rope8(x, p.rope != 0, s_cs[i], c8, y);
+      norm_rope8(x, p.rope != 0, s_cs[i], c8, is_q ? p.q_scale : 1.0f, y);
       if (hr >= kQHeads && p.scaled) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k] / ks);

@@ -128,7 +128,7 @@ def cpu_baseline(x, budget_s: float):
     layer pool 0's inputs until the time budget is used (at least one step)."""
     import numpy as np
     import oracle
-    cfg = oracle.Config(batch=x.w.batch, q_len=x.w.q_len, num_q_heads=x.w.num_q_heads,
+    cfg = oracle.Config(q_scale=x.w.q_scale, batch=x.w.batch, q_len=x.w.q_len, num_q_heads=x.w.num_q_heads,
                         num_kv_heads=x.w.num_kv_heads, head_dim=x.w.head_dim,
                         page_size=x.w.page_size, window=x.w.window, max_pages=x.max_pages,
                         num_pages=x.num_pages, rope_theta=x.w.rope_theta,
@@ -312,7 +312,7 @@ def main():
           f"touched per step", file=sys.stderr, flush=True)
 
     cfg = ga.make_config(w.batch, w.q_len, w.page_size, w.window, x0.max_pages, x0.num_pages,
-                         w.rope_theta, w.sm_scale, w.kv_scale)
+                         w.rope_theta, w.sm_scale, w.kv_scale, q_scale=w.q_scale)
     step = ga.GatedAttnStep(cfg, int(w.seq_hi + w.q_len), args.splits)
 
     # Layer pools: pool 0 is the tests' seeded input; the others are drawn on

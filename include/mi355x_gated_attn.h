@@ -48,7 +48,8 @@ enum {
 /*
  * Step configuration: the page's Config (batch, q_len, num_q_heads,
  * num_kv_heads, head_dim, page_size, window, rope_theta, sm_scale, kv_scale)
- * plus the two bounds the library needs to keep every access in range.
+ * plus the two bounds the library needs to keep every access in range, and
+ * q_scale, the output scale of page "qk_norm" applied to q's norm.
  */
 typedef struct mi355x_gated_attn_config {
   int32_t batch;        /* B >= 0 requests; B == 0 makes every step a no-op     */
@@ -65,6 +66,10 @@ typedef struct mi355x_gated_attn_config {
                         /* query factor in: sm_scale * qk_scale_factor)        */
   float kv_scale;       /* != 1 selects the scaled store (divide by k_scale /   */
                         /* v_scale) and the descaled read; == 1 ignores them    */
+  float q_scale;        /* > 0: q's normed fp32 product is multiplied by it     */
+                        /* before its one bf16 rounding (page "qk_norm",        */
+                        /* QKNormDirectKernel's output scale: a query factor    */
+                        /* carried by q, not by sm_scale); 1 = page 1's norm    */
 } mi355x_gated_attn_config;
 
 /* Opaque per-configuration context (host memory only). */

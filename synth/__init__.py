@@ -32,6 +32,7 @@ class Workload:
     page_size: int = 1
     kv_scale: float = 1.0
     qkv_std: float = 1.0
+    q_scale: float = 1.0   # q's norm output scale (page "qk_norm"); 1 = page 1's prologue
     table: str = "perm"    # "identity": page j of request b is page b*max + j; "perm": shuffled
     num_q_heads: int = 16
     num_kv_heads: int = 2
@@ -166,12 +167,12 @@ def small(name: str = "small", batch: int = 3, q_len: int = 1, seq_lo: int = 40,
           window: int = 0, rope_theta: float = 0.0, page_size: int = 1, kv_scale: float = 1.0,
           qkv_std: float = 1.0, table: str = "perm", sm_scale: float = 0.125,
           num_q_heads: int = 16, num_kv_heads: int = 2, spare_pages: int = 3,
-          seed: int = 7) -> Workload:
+          seed: int = 7, q_scale: float = 1.0) -> Workload:
     """A workload small enough for the oracle to finish in well under a second."""
     return Workload(name, batch, q_len, seq_lo, seq_hi, window, rope_theta, page_size=page_size,
                     kv_scale=kv_scale, qkv_std=qkv_std, table=table, sm_scale=sm_scale,
                     num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
-                    spare_pages=spare_pages, seed=seed)
+                    spare_pages=spare_pages, seed=seed, q_scale=q_scale)
 
 
 def with_seed(w: Workload, seed: int) -> Workload:

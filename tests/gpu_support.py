@@ -20,14 +20,15 @@ def oracle_config(x: synth.Inputs) -> oracle.Config:
     return oracle.Config(batch=w.batch, q_len=w.q_len, num_q_heads=w.num_q_heads,
                          num_kv_heads=w.num_kv_heads, head_dim=w.head_dim, page_size=w.page_size,
                          window=w.window, max_pages=x.max_pages, num_pages=x.num_pages,
-                         rope_theta=w.rope_theta, sm_scale=w.sm_scale, kv_scale=w.kv_scale)
+                         rope_theta=w.rope_theta, sm_scale=w.sm_scale, kv_scale=w.kv_scale,
+                         q_scale=w.q_scale)
 
 
 def abi_config(x: synth.Inputs) -> ga.Config:
     w = x.w
     return ga.make_config(w.batch, w.q_len, w.page_size, w.window, x.max_pages, x.num_pages,
                           w.rope_theta, w.sm_scale, w.kv_scale, w.num_q_heads, w.num_kv_heads,
-                          w.head_dim)
+                          w.head_dim, w.q_scale)
 
 
 def max_context(x: synth.Inputs) -> int:

@@ -70,6 +70,8 @@ def test_supports_accepts_the_served_shapes(L):
     (dict(sm_scale=0.0), ga.MI355X_GA_INVALID_ARGUMENT),
     (dict(sm_scale=float("nan")), ga.MI355X_GA_INVALID_ARGUMENT),
     (dict(kv_scale=-0.5), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(q_scale=0.0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(q_scale=float("inf")), ga.MI355X_GA_INVALID_ARGUMENT),
 ])
 def test_supports_rejects(L, kw, status):
     assert ga.mi355x_gated_attn_supports(cfg(**kw)) == status

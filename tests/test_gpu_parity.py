@@ -34,6 +34,9 @@ SMALL = {
     "verify8_scaled_page64": dict(batch=2, q_len=8, window=0, page_size=64, kv_scale=0.5,
                                   qkv_std=1.4142135),
     "decode_qk_factor": dict(batch=2, q_len=1, window=0, sm_scale=5.473 / 8),
+    # the query factor carried by q (page "qk_norm"'s output scale), not sm_scale
+    "decode_q_scaled": dict(batch=3, q_len=1, window=0, q_scale=5.473),
+    "verify3_swa_q_scaled": dict(batch=2, q_len=3, window=40, rope_theta=500000.0, q_scale=5.473),
     "decode_b1_identity": dict(batch=1, q_len=1, window=0, table="identity"),
     "verify8_window1": dict(batch=2, q_len=8, window=1),
 }
@@ -161,6 +164,25 @@ def test_full_size_workload(name):
     out_ref = ref.outputs(st, sh)
     got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
     assert_outputs_close(got, out_ref, name + " out")
+
+
+def test_full_size_decode_with_the_query_factor_in_q():
+    """The headline decode with page "qk_norm"'s output scale carrying the
+    query factor (q_scale 5.473, sm_scale 1/8): every q and cache byte, sampled
+    output rows."""
+    import dataclasses
+    w = dataclasses.replace(synth.WORKLOADS["swa_decode"], name="swa_decode_q_scaled", q_scale=5.473)
+    _say("[gpu] full-size swa_decode with q_scale 5.473")
+    x = synth.make_inputs(w)
+    res = run_gpu(x)
+    ref = Reference(x)
+    written = x.tokens * w.num_kv_heads * w.head_dim
+    assert_codes_match(res.q, ref.q, ref.q.size, "q_scaled q")
+    assert_codes_match(res.k_cache, ref.k_cache, written, "q_scaled k_cache")
+    rng = np.random.default_rng(8)
+    st, sh = _sample_rows(x.tokens, w.num_q_heads, rng)
+    got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
+    assert_outputs_close(got, ref.outputs(st, sh), "q_scaled out")
 
 
 def test_graph_replay_matches_eager():
