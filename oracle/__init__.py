@@ -82,6 +82,10 @@ def lib():
         L.orc_fp16_to_double.argtypes = [ctypes.c_uint16]
         L.orc_fp16_round.restype = ctypes.c_uint16
         L.orc_fp16_round.argtypes = [ctypes.c_double]
+        L.orc_sparse_attention.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, ctypes.c_int32,
+                                           ctypes.c_int32, ctypes.c_float, ctypes.c_float, P]
+        L.orc_sparse_step.argtypes = [ctypes.POINTER(_Cfg), P, P, P, P, P, P, ctypes.c_int32,
+                                      ctypes.c_int32, P, P, ctypes.c_float, ctypes.c_float, P, P, P]
         L.orc_qk_norm.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_float, ctypes.c_float, P]
         _lib = L
@@ -259,3 +263,38 @@ def qk_norm(x: np.ndarray, num_heads: int, head_dim: int, dtype: int, eps: float
     _check(lib().orc_qk_norm(_p(x), M, num_heads, head_dim, stride, dtype, ctypes.c_float(eps),
                              ctypes.c_float(scale), _p(out)), "orc_qk_norm")
     return out
+
+
+# Page "msa.py": page-list-driven (top-k block-sparse) decode, see
+# orc_sparse_attention in oracle.c.
+
+def sparse_attention(cfg: Config, q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray,
+                     page_table: np.ndarray, cache_seqlens: np.ndarray, block_idx: np.ndarray,
+                     block_size: int, k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+    """Unrounded attention output double [B, Hq, D]; block_idx int32 [Hkv, B, topk]."""
+    bi = np.ascontiguousarray(block_idx, np.int32)
+    o = np.zeros((cfg.batch, cfg.num_q_heads, cfg.head_dim), np.float64)
+    _check(lib().orc_sparse_attention(ctypes.byref(cfg.c()), _p(np.ascontiguousarray(q)),
+                                      _p(k_cache), _p(v_cache),
+                                      _p(np.ascontiguousarray(page_table, np.int32)),
+                                      _p(np.ascontiguousarray(cache_seqlens, np.int32)), _p(bi),
+                                      int(block_size), int(bi.shape[-1]), float(k_scale),
+                                      float(v_scale), _p(o)), "sparse_attention")
+    return o
+
+
+def sparse_step(cfg: Config, qkv, positions, cache_loc, cache_seqlens, page_table, block_idx,
+                block_size: int, k_cache, v_cache, k_scale: float, v_scale: float):
+    """Whole sparse decode step; caches updated in place.  Returns (q codes, out
+    bf16 bits [B, 1, Hq*D], unrounded attention output double [B, Hq, D])."""
+    T = cfg.batch * cfg.q_len
+    bi = np.ascontiguousarray(block_idx, np.int32)
+    q = np.zeros((T, cfg.num_q_heads, cfg.head_dim), np.uint8)
+    o = np.zeros((T * cfg.num_q_heads, cfg.head_dim), np.float64)
+    out = np.zeros((T * cfg.num_q_heads, cfg.head_dim), np.uint16)
+    _check(lib().orc_sparse_step(ctypes.byref(cfg.c()), _p(qkv), _p(positions), _p(cache_loc),
+                                 _p(cache_seqlens), _p(page_table), _p(bi), int(block_size),
+                                 int(bi.shape[-1]), _p(k_cache), _p(v_cache), float(k_scale),
+                                 float(v_scale), _p(q), _p(o), _p(out)), "sparse_step")
+    return (q, out.reshape(cfg.batch, cfg.q_len, cfg.num_q_heads * cfg.head_dim),
+            o.reshape(T, cfg.num_q_heads, cfg.head_dim))

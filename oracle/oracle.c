@@ -412,6 +412,90 @@ int orc_attention(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cach
 }
 
 /* ------------------------------------------------------------------------ */
+/* Page-list-driven (top-k block-sparse) decode (page "msa.py":              */
+/* msa_sparse_decode_main and build_msa_decode_meta): each request is one    */
+/* decode query at position cache_seqlens[b] - 1 attending to its cached     */
+/* keys through the blocks a per-KV-head top-k list selects.                 */
+/* block_idx int32 [Hkv, B, topk]: logical block indices, -1 padding; block  */
+/* j holds keys j*BS .. (j+1)*BS - 1 of the request, those below             */
+/* cache_seqlens[b] being visible (READING: the plan's qo_offset places the  */
+/* query at the last cached position, and non-causal decode sees every      */
+/* cached key of a selected block).  Query head h reads the list of KV head  */
+/* h / (Hq/Hkv).  The key set is the union of the selected blocks (a         */
+/* repeated index adds nothing); no window applies.  Scores, weights,        */
+/* descales and the empty-set output 0 are as in orc_attention.              */
+/* ------------------------------------------------------------------------ */
+int orc_sparse_attention(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cache,
+                         const uint8_t* v_cache, const int32_t* page_table,
+                         const int32_t* cache_seqlens, const int32_t* block_idx,
+                         int32_t block_size, int32_t topk, float k_scale, float v_scale,
+                         double* o_out) {
+  if (!cfg_ok(cfg) || cfg->q_len != 1 || block_size < 1 || topk < 1) return ORC_BAD_ARG;
+  const int hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
+  const int grp = hq / hkv;
+  const int64_t B = cfg->batch;
+  const int scaled = cfg->kv_scale != 1.0f;
+  const double kd = scaled ? (double)k_scale : 1.0, vd = scaled ? (double)v_scale : 1.0;
+  double qv[256];
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t cs = cache_seqlens[b];
+    /* visible keys per KV head: the union of its selected blocks, below cs */
+    unsigned char* vis = (unsigned char*)calloc((size_t)(cs > 0 ? cs : 1), 1);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)(cs > 0 ? cs : 1));
+    if (!vis || !sc) {
+      free(vis);
+      free(sc);
+      return ORC_BAD_ARG;
+    }
+    for (int g = 0; g < hkv; ++g) {
+      memset(vis, 0, (size_t)(cs > 0 ? cs : 1));
+      for (int i = 0; i < topk; ++i) {
+        const int64_t j = block_idx[((int64_t)g * B + b) * topk + i];
+        if (j < 0) continue;
+        for (int64_t key = j * block_size; key < (j + 1) * block_size && key < cs; ++key) vis[key] = 1;
+      }
+      for (int hh = 0; hh < grp; ++hh) {
+        const int h = g * grp + hh;
+        double* o = o_out + (b * hq + h) * d;
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        for (int c = 0; c < d; ++c) qv[c] = orc_e4m3_decode(q[(b * hq + h) * d + c]);
+        double mx = -INFINITY;
+        int64_t cnt = 0;
+        for (int64_t key = 0; key < cs; ++key) {
+          if (!vis[key]) continue;
+          const int64_t r = key_row(cfg, page_table, b, key);
+          if (r < 0) {
+            free(vis);
+            free(sc);
+            return ORC_BAD_ROW;
+          }
+          const uint8_t* kr = k_cache + (r * hkv + g) * d;
+          double dot = 0.0;
+          for (int c = 0; c < d; ++c) dot += qv[c] * orc_e4m3_decode(kr[c]);
+          sc[key] = dot * kd * (double)cfg->sm_scale;
+          if (sc[key] > mx) mx = sc[key];
+          ++cnt;
+        }
+        if (cnt == 0) continue;
+        double wsum = 0.0;
+        for (int64_t key = 0; key < cs; ++key) {
+          if (!vis[key]) continue;
+          const double w = exp(sc[key] - mx);
+          wsum += w;
+          const int64_t r = key_row(cfg, page_table, b, key);
+          const uint8_t* vr = v_cache + (r * hkv + g) * d;
+          for (int c = 0; c < d; ++c) o[c] += w * orc_e4m3_decode(vr[c]);
+        }
+        for (int c = 0; c < d; ++c) o[c] = vd * o[c] / wsum;
+      }
+    }
+    free(vis);
+    free(sc);
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Step 6: the gated epilogue (page: rms_norm_gate on the bf16 attention     */
 /* output, weight None, eps 1e-5).                                          */
 /* ------------------------------------------------------------------------ */
@@ -449,6 +533,21 @@ int orc_epilogue(const orc_config* cfg, const double* o_in, const uint16_t* qkv,
     }
   }
   return ORC_OK;
+}
+
+/* The sparse decode step: the same prologue and epilogue around the         */
+/* block-sparse attention (every cache store before any attention read).     */
+int orc_sparse_step(const orc_config* cfg, const uint16_t* qkv, const int64_t* positions,
+                    const int64_t* cache_loc, const int32_t* cache_seqlens,
+                    const int32_t* page_table, const int32_t* block_idx, int32_t block_size,
+                    int32_t topk, uint8_t* k_cache, uint8_t* v_cache, float k_scale,
+                    float v_scale, uint8_t* q_out, double* o_scratch, uint16_t* out) {
+  int rc = orc_prologue(cfg, qkv, positions, cache_loc, k_cache, v_cache, k_scale, v_scale, q_out);
+  if (rc) return rc;
+  rc = orc_sparse_attention(cfg, q_out, k_cache, v_cache, page_table, cache_seqlens, block_idx,
+                            block_size, topk, k_scale, v_scale, o_scratch);
+  if (rc) return rc;
+  return orc_epilogue(cfg, o_scratch, qkv, 0, NULL, NULL, out);
 }
 
 /* ------------------------------------------------------------------------ */

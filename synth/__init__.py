@@ -33,6 +33,8 @@ class Workload:
     kv_scale: float = 1.0
     qkv_std: float = 1.0
     q_scale: float = 1.0   # q's norm output scale (page "qk_norm"); 1 = page 1's prologue
+    sparse_block: int = 0  # > 0: block-sparse decode (page "msa.py") over blocks of this many keys
+    sparse_topk: int = 0   # blocks each KV head's list selects
     table: str = "perm"    # "identity": page j of request b is page b*max + j; "perm": shuffled
     num_q_heads: int = 16
     num_kv_heads: int = 2
@@ -71,6 +73,17 @@ SUPPLEMENTARY = {
     "full_decode_16k": Workload("full_decode_16k", 32, 1, 16384, 16384, 0, 500000.0, seed=1007),
 }
 WORKLOADS.update(SUPPLEMENTARY)
+
+# Page-list-driven (top-k block-sparse) decode, page "msa.py": blocks of 128
+# keys, one page each (the page's block_size_k == page_size == 128), 16
+# selected per KV head (2,048 keys, the headline's window), 8k-32k cached, no
+# window, no RoPE.  Synthetic block lists (the real ones come from a trained
+# indexer): see make_block_lists.
+SPARSE = {
+    "sparse_decode": Workload("sparse_decode", 32, 1, 8192, 32768, 0, 0.0, page_size=128,
+                              sparse_block=128, sparse_topk=16, seed=1008),
+}
+WORKLOADS.update(SPARSE)
 
 
 @dataclass
@@ -156,11 +169,35 @@ def make_inputs(w: Workload, seed: int | None = None, seq_lens: np.ndarray | Non
     v_cache = _normal_e4m3(rng, (rows_total, w.num_kv_heads, w.head_dim))
     qkv = to_bf16_bits(rng.standard_normal((B, L, w.width), dtype=np.float32) * np.float32(w.qkv_std))
     cu = (np.arange(B + 1, dtype=np.int32) * L).astype(np.int32)
+    extra = {}
+    if w.sparse_block > 0:
+        extra["block_idx"] = make_block_lists(rng, cache_seqlens, w.sparse_block, w.sparse_topk,
+                                              w.num_kv_heads)
     return Inputs(w=w, qkv=qkv, positions=positions.reshape(-1).copy(),
                   cache_loc=rows.reshape(-1).copy(), cache_seqlens=cache_seqlens,
                   cu_seqlens_q=cu, page_table=page_table, seq_lens=seq_lens,
                   k_cache=k_cache, v_cache=v_cache, k_scale=float(w.kv_scale),
-                  v_scale=float(w.kv_scale), max_pages=int(max_pages), num_pages=num_pages)
+                  v_scale=float(w.kv_scale), max_pages=int(max_pages), num_pages=num_pages,
+                  extra=extra)
+
+
+def make_block_lists(rng: np.random.Generator, cache_seqlens: np.ndarray, block_size: int,
+                     topk: int, num_kv_heads: int) -> np.ndarray:
+    """int32 [Hkv, B, topk] top-k block lists: per (KV head, request) the
+    block holding the query's own position (cache_seqlens - 1) and distinct
+    other blocks of the request drawn uniformly, min(topk, blocks) in all, in
+    random order, padded with -1."""
+    B = len(cache_seqlens)
+    out = np.full((num_kv_heads, B, topk), -1, np.int32)
+    for g in range(num_kv_heads):
+        for b in range(B):
+            n = int(-(-int(cache_seqlens[b]) // block_size))
+            if n <= 0:
+                continue
+            others = rng.choice(n - 1, size=min(topk, n) - 1, replace=False) if n > 1 else []
+            sel = np.concatenate([[n - 1], np.asarray(others, np.int64)])
+            out[g, b, :len(sel)] = rng.permutation(sel)
+    return out
 
 
 def small(name: str = "small", batch: int = 3, q_len: int = 1, seq_lo: int = 40, seq_hi: int = 300,
