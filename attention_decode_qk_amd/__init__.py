@@ -25,7 +25,7 @@ EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_g
             "mi355x_gated_attn_workspace_init", "mi355x_gated_attn_step", "mi355x_gated_attn_destroy",
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
             "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta",
-            "mi355x_qk_norm_supports", "mi355x_qk_norm"]
+            "mi355x_qk_norm_supports", "mi355x_qk_norm", "mi355x_gated_attn_sparse_step"]
 
 MI355X_QKN_BF16 = 0
 MI355X_QKN_FP16 = 1
@@ -45,7 +45,8 @@ class Config(ctypes.Structure):
                 ("window", ctypes.c_int32), ("max_pages", ctypes.c_int32),
                 ("num_pages", ctypes.c_int64), ("rope_theta", ctypes.c_float),
                 ("sm_scale", ctypes.c_float), ("kv_scale", ctypes.c_float),
-                ("q_scale", ctypes.c_float)]
+                ("q_scale", ctypes.c_float), ("sparse_block", ctypes.c_int32),
+                ("sparse_topk", ctypes.c_int32)]
 
 
 _lib = None
@@ -69,6 +70,7 @@ def lib() -> ctypes.CDLL:
         L.mi355x_gated_attn_workspace_init.argtypes = [P, P, ctypes.c_size_t, P]
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_step_meta.argtypes = [P] * 7
+        L.mi355x_gated_attn_sparse_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_destroy.argtypes = [P]
         L.mi355x_gated_attn_destroy.restype = None
         L.mi355x_gated_attn_last_error.argtypes = []
@@ -97,9 +99,10 @@ def _check(rc: int):
 
 def make_config(batch, q_len, page_size, window, max_pages, num_pages, rope_theta=0.0,
                 sm_scale=0.125, kv_scale=1.0, num_q_heads=16, num_kv_heads=2,
-                head_dim=64, q_scale=1.0) -> Config:
+                head_dim=64, q_scale=1.0, sparse_block=0, sparse_topk=0) -> Config:
     return Config(batch, q_len, num_q_heads, num_kv_heads, head_dim, page_size, window,
-                  max_pages, num_pages, rope_theta, sm_scale, kv_scale, q_scale)
+                  max_pages, num_pages, rope_theta, sm_scale, kv_scale, q_scale, sparse_block,
+                  sparse_topk)
 
 
 def mi355x_gated_attn_supports(cfg: Config) -> int:
@@ -154,6 +157,27 @@ def mi355x_gated_attn_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_t
     _check(lib().mi355x_gated_attn_step(
         ctx, _ptr(qkv), _ptr(positions), _ptr(cache_loc), _ptr(cache_seqlens), _ptr(page_table),
         _ptr(seq_lens), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+        _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
+
+
+def mi355x_gated_attn_sparse_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table,
+                                  block_idx, k_cache, v_cache, k_scale, v_scale, out, workspace,
+                                  stream=None):
+    """Launch one page-list-driven decode step (block_idx: contiguous int32
+    device tensor [Hkv, B, topk], -1 padded); otherwise as mi355x_gated_attn_step."""
+    import torch
+    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, cache_seqlens=cache_seqlens,
+                   page_table=page_table, block_idx=block_idx, k_cache=k_cache, v_cache=v_cache,
+                   out=out, workspace=workspace)
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_sparse_step(
+        ctx, _ptr(qkv), _ptr(positions), _ptr(cache_loc), _ptr(cache_seqlens), _ptr(page_table),
+        _ptr(block_idx), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
         _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
 
 
@@ -225,6 +249,14 @@ class GatedAttnStep:
         mi355x_gated_attn_step(self.ctx, qkv, positions, cache_loc, cache_seqlens, page_table,
                                seq_lens, k_cache, v_cache, k_scale, v_scale, out, self.workspace,
                                stream)
+        return out
+
+    def sparse(self, qkv, positions, cache_loc, cache_seqlens, page_table, block_idx, k_cache,
+               v_cache, k_scale, v_scale, out, stream=None):
+        """One page-list-driven decode step (a config with sparse_block > 0)."""
+        mi355x_gated_attn_sparse_step(self.ctx, qkv, positions, cache_loc, cache_seqlens,
+                                      page_table, block_idx, k_cache, v_cache, k_scale, v_scale,
+                                      out, self.workspace, stream)
         return out
 
     def meta(self, seq_lens, page_table, positions, cache_loc, cache_seqlens, stream=None):

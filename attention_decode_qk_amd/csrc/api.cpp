@@ -115,6 +115,21 @@ int mi355x_gated_attn_supports(const mi355x_gated_attn_config* c) {
     return fail(MI355X_GA_INVALID_ARGUMENT, "kv_scale must be finite and positive");
   if (!(c->q_scale > 0.0f) || std::isinf(c->q_scale))
     return fail(MI355X_GA_INVALID_ARGUMENT, "q_scale must be finite and positive (1: none)");
+  if (c->sparse_block < 0 || c->sparse_topk < 0)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "sparse_block and sparse_topk must be >= 0");
+  if (c->sparse_block > 0) {
+    if (c->sparse_topk < 1) return fail(MI355X_GA_INVALID_ARGUMENT, "sparse_topk must be >= 1");
+    if (c->sparse_block % kKeyBlock)
+      return fail(MI355X_GA_UNSUPPORTED, "sparse_block %d: this build serves multiples of %d",
+                  c->sparse_block, kKeyBlock);
+    if (c->sparse_topk > kMaxSparseTopk)
+      return fail(MI355X_GA_UNSUPPORTED, "sparse_topk %d: this build serves up to %d", c->sparse_topk,
+                  kMaxSparseTopk);
+    if (c->q_len != 1 || c->window != 0)
+      return fail(MI355X_GA_UNSUPPORTED, "page-list-driven decode serves q_len 1 without a window");
+    if ((int64_t)c->sparse_block * c->sparse_topk > (int64_t)1 << 30)
+      return fail(MI355X_GA_UNSUPPORTED, "sparse_block * sparse_topk exceeds 2^30 keys");
+  }
   if (c->num_q_heads % c->num_kv_heads)
     return fail(MI355X_GA_UNSUPPORTED, "num_q_heads %d is not a multiple of num_kv_heads %d",
                 c->num_q_heads, c->num_kv_heads);
@@ -164,8 +179,11 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(MI355X_GA_INVALID_ARGUMENT, "num_splits %d outside 0..%d", num_splits, kMaxSplits);
   const auto& c = ctx->cfg;
+  const bool sparse = c.sparse_block > 0;
   int64_t keys = max_context;  // union of a request's visible keys
   if (c.window > 0) keys = std::min<int64_t>(keys, (int64_t)c.window + c.q_len - 1);
+  // Page-list-driven decode walks topk * block_size list positions per KV head.
+  if (sparse) keys = (int64_t)c.sparse_topk * c.sparse_block;
   // Token groups: for short key ranges (a sliding window) the step is bound by
   // its fixed latencies, and groups of two tokens shorten the per-unit prologue
   // and the combine; long ranges are bound by the key loop, where groups of four
@@ -179,12 +197,13 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   // of a cache row, fetched by different waves, cost HBM efficiency (B = 64,
   // L = 1, 32k keys: 160 against 113 us; B = 32, L = 1, W = 2048: 13.0 against
   // 12.5 us), so four waves keep both heads.
-  const bool head_split = keys <= kShortKeys && c.q_len > 1;
+  // (Page-list-driven decode: each KV head has its own list, so one head per wave.)
+  const bool head_split = sparse || (keys <= kShortKeys && c.q_len > 1);
   // Decode over long key ranges keeps more K/V blocks in flight with eight
   // waves per unit, both heads each (B = 64, 32k keys: 106 against 113 us); over
   // a window the extra merge and barrier cost more (B = 32, W = 2048: 15.7
   // against 12.5 us).
-  const int key_waves = (c.q_len == 1 && keys > kShortKeys) ? 2 * kAttnWaves : kAttnWaves;
+  const int key_waves = (!sparse && c.q_len == 1 && keys > kShortKeys) ? 2 * kAttnWaves : kAttnWaves;
   int32_t s = num_splits;
   if (s == 0) {
     const int64_t min_keys_per_split = (int64_t)key_waves * kKeyBlock;  // a block per wave
@@ -256,15 +275,22 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
   return ok();
 }
 
-int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
-                           const int64_t* cache_loc, const int32_t* cache_seqlens,
-                           const int32_t* page_table, const int32_t* seq_lens, void* k_cache,
-                           void* v_cache, const float* k_scale, const float* v_scale, void* out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
-  (void)seq_lens;  // the page's attention call takes cache_seqlens only
+}  // extern "C"
+
+namespace {
+
+int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
+             const int64_t* cache_loc, const int32_t* cache_seqlens, const int32_t* page_table,
+             const int32_t* block_idx, void* k_cache, void* v_cache, const float* k_scale,
+             const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
   if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
   const auto& c = ctx->cfg;
+  if (c.batch == 0) return ok();
+  if ((c.sparse_block > 0) != (block_idx != nullptr))
+    return fail(MI355X_GA_INVALID_ARGUMENT,
+                c.sparse_block > 0 ? "a page-list-driven config needs block_idx (sparse_step)"
+                                   : "block_idx given for a dense config (use step)");
   if (c.batch == 0) return ok();
   const bool scaled = c.kv_scale != 1.0f;
   const bool rope = c.rope_theta != 0.0f;
@@ -316,6 +342,9 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   sp.rope = rope ? 1 : 0;
   sp.sm_scale_log2 = c.sm_scale * 1.4426950408889634f;
   sp.q_scale = c.q_scale;
+  sp.block_idx = block_idx;
+  sp.sparse_block = c.sparse_block;
+  sp.sparse_topk = c.sparse_topk;
   std::memcpy(sp.inv_freq, ctx->inv_freq, sizeof sp.inv_freq);
 
   hipEvent_t* ev = nullptr;
@@ -336,6 +365,34 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
+                           const int64_t* cache_loc, const int32_t* cache_seqlens,
+                           const int32_t* page_table, const int32_t* seq_lens, void* k_cache,
+                           void* v_cache, const float* k_scale, const float* v_scale, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  (void)seq_lens;  // the page's attention call takes cache_seqlens only
+  return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, nullptr, k_cache,
+                  v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream);
+}
+
+int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                  const int64_t* positions, const int64_t* cache_loc,
+                                  const int32_t* cache_seqlens, const int32_t* page_table,
+                                  const int32_t* block_idx, void* k_cache, void* v_cache,
+                                  const float* k_scale, const float* v_scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (ctx && ctx->cfg.batch > 0 && !block_idx)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "block_idx is NULL");
+  if (ctx && ctx->cfg.sparse_block == 0)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "sparse_step on a dense config (sparse_block 0)");
+  return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, block_idx, k_cache,
+                  v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream);
 }
 
 void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx) {

@@ -27,6 +27,7 @@ constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
 constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
 constexpr int kMaxTokensPerUnit = 4;
+constexpr int kMaxSparseTopk = 256;  // list slots per (KV head, request) of page-list-driven decode
 constexpr int token_groups(int q_len, bool short_keys) {
   return short_keys ? (q_len + 1) / 2 : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit;
 }
@@ -71,6 +72,9 @@ struct StepParams {
   int32_t rope;                  // 1 iff rope_theta != 0
   float sm_scale_log2;           // sm_scale * log2(e)
   float q_scale;                 // q's norm output scale before its bf16 rounding (1: none)
+  const int32_t* block_idx;      // page-list-driven decode: int32 [Hkv, B, topk] block lists (-1 pad)
+  int32_t sparse_block;          // keys per listed block (a multiple of 32); 0: dense step
+  int32_t sparse_topk;           // list slots per (KV head, request), <= kMaxSparseTopk
   float inv_freq[kHeadDim / 2];
 };
 

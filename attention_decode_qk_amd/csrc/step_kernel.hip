@@ -251,7 +251,7 @@ __device__ inline uint2 pack_e4m3x8(const float (&y)[8]) {
   return make_uint2(lo, hi);
 }
 
-template <int LU, bool HS, int KW>
+template <int LU, bool HS, int KW, bool SP>
 __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(StepParams p) {
   // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
   // LU consecutive tokens; the unit (request b, token group tg, key chunk kc)
@@ -266,6 +266,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   constexpr int kQItems = LU * kQHeads * 8;     // (token, q head, 8-column slice)
   constexpr int kMaxL = max_q_len_for(LU);
   static_assert(kMaxL >= LU, "no q_len is served by this unit size");
+  static_assert(!SP || (HS && LU == 1), "page-list-driven decode: q_len 1, one KV head per wave");
   constexpr int kMaxItems = kQItems + kMaxL * 2 * kKvHeads * 8;  // + K/V rows of every token
   constexpr int kItemIters = (kMaxItems + kThreads - 1) / kThreads;
   constexpr int kRows = LU * kQHeads;           // partial rows of a unit
@@ -276,6 +277,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   __shared__ __align__(16) float s_mo[KW][kRows][kHeadDim];
   __shared__ __align__(16) float s_ml[KW][kRows][2];
   __shared__ int s_last;
+  // SP (page-list-driven decode): the request's block lists, one per KV head.
+  __shared__ int s_blk[SP ? kKvHeads : 1][SP ? kMaxSparseTopk : 1];
 
   // A unit size that serves a single q_len (LU = 1: q_len 1) serves it as one group.
   constexpr bool kOneGroup = kMaxL == LU;
@@ -307,15 +310,24 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // that every path reaches the page-table wait with the same loads in flight.
   const float ks = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
+  if constexpr (SP) {  // both KV heads' lists of request b into LDS (2 * topk <= threads)
+    if (tid < kKvHeads * p.sparse_topk) {
+      const int g = tid / p.sparse_topk, s = tid - g * p.sparse_topk;
+      s_blk[g][s] = p.block_idx[((int64_t)g * p.batch + b) * p.sparse_topk + s];
+    }
+    lds_barrier();
+  }
   asm volatile("" ::: "memory");
   const int p0 = cs - L;  // key index (position) of the request's first new token
   const int last = cs - 1;
-  const int first = p.window > 0 ? max(0, p0 - p.window + 1) : 0;
-  const int n = max(0, last - first + 1);
+  // SP: the unit's chunk is a range of virtual key indices v in [0, topk * BS):
+  // list slot v / BS, offset v % BS within that block.
+  const int first = SP ? 0 : (p.window > 0 ? max(0, p0 - p.window + 1) : 0);
+  const int n = SP ? p.sparse_topk * p.sparse_block : max(0, last - first + 1);
   int chunk = (n + p.splits - 1) / p.splits;
   chunk = (chunk + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
   const int start = first + kc * chunk;
-  const int end = min(start + chunk, last + 1);
+  const int end = min(start + chunk, SP ? n : last + 1);
   const int nblk = end > start ? (end - start + kKeyBlock - 1) / kKeyBlock : 0;
   const int nb = nblk > kw ? (nblk - kw + KW - 1) / KW : 0;  // this wave's
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
@@ -328,8 +340,28 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     const int blk = min(i, max(nb - 1, 0));
     return max(0, min(start + (kw + KW * blk) * kKeyBlock + off, end - 1));
   };
-  auto k_key = [&](int i) { return block_key(i, lane & 31); };
-  auto v_key = [&](int i) { return block_key(i, voff); };
+  // SP: virtual index -> key of the request; false (and key 0, a row in bounds)
+  // when the slot is empty or the key lies at or past the cached length.
+  auto sp_key = [&](int v, int& key) {
+    if constexpr (SP) {
+      const int slot = v / p.sparse_block;
+      const int bid = s_blk[g0][slot];
+      key = bid * p.sparse_block + (v - slot * p.sparse_block);
+      const bool ok = bid >= 0 && key < cs;
+      key = ok ? key : 0;
+      return ok;
+    } else {
+      key = v;
+      return true;
+    }
+  };
+  auto mapped = [&](int v) {
+    int key;
+    sp_key(v, key);
+    return key;
+  };
+  auto k_key = [&](int i) { return SP ? mapped(block_key(i, lane & 31)) : block_key(i, lane & 31); };
+  auto v_key = [&](int i) { return SP ? mapped(block_key(i, voff)) : block_key(i, voff); };
   auto load_pte = [&](int i) { return make_int2(page_entry(p, pt, k_key(i)), page_entry(p, pt, v_key(i))); };
   auto load_block = [&](int2 e, int i) { return load_kv<NG>(p, e, k_key(i), v_key(i), g0, j, q4); };
 
@@ -392,6 +424,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // (one per token group); the group-0 one stores them.  A key with no place in
   // any chunk (a padded slot) goes to chunk 0.
   auto chunk_has = [&](int i) {
+    if constexpr (SP) return true;  // the new key may sit in any chunk's blocks
     const int key = p0 + i;
     return (key >= start && key < end) || (key < first && kc == 0);
   };
@@ -444,7 +477,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   }
   lds_barrier();
 
-  if (tid < L && tg == 0 && chunk_has(tid) && my_slot >= 0 && my_slot < p.num_rows) {
+  if (tid < L && tg == 0 && (SP ? kc == 0 : chunk_has(tid)) && my_slot >= 0 && my_slot < p.num_rows) {
     const uint4* kk = reinterpret_cast<const uint4*>(s_newk[tid]);
     const uint4* vv = reinterpret_cast<const uint4*>(s_newv[tid]);
     uint4* kd = reinterpret_cast<uint4*>(p.k_cache + my_slot * kRowBytes);
@@ -496,6 +529,31 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // ---------------- B. key loop ----------------
   // New keys' codes replace the cache bytes of a block that holds them.
   auto substitute = [&](KvBlock<NG>& d, const int kbase) {
+    if constexpr (SP) {
+      // q_len 1: the new key p0, wherever this block's list slot holds it (a
+      // 32-key block lies in one slot: BS and the chunks are multiples of 32).
+      if (kbase >= end) return;
+      const int slot = kbase / p.sparse_block;
+      const int bid = s_blk[g0][slot];
+      const int k0 = bid * p.sparse_block + (kbase - slot * p.sparse_block);
+      if (bid < 0 || p0 < k0 || p0 >= k0 + kKeyBlock) return;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bool nk = k0 + 16 * t + j == p0;
+        const uint4 nv = *reinterpret_cast<const uint4*>(&s_newk[0][g0 * kHeadDim + 16 * q4]);
+        d.k[t][0].x = nk ? nv.x : d.k[t][0].x;
+        d.k[t][0].y = nk ? nv.y : d.k[t][0].y;
+        d.k[t][0].z = nk ? nv.z : d.k[t][0].z;
+        d.k[t][0].w = nk ? nv.w : d.k[t][0].w;
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const bool nk = k0 + 16 * (r >> 2) + 4 * q4 + (r & 3) == p0;
+        const uint32_t nv = *reinterpret_cast<const uint32_t*>(&s_newv[0][g0 * kHeadDim + 4 * j]);
+        d.v[0][r] = nk ? nv : d.v[0][r];
+      }
+      return;
+    }
     if (kbase + kKeyBlock - 1 < p0) return;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -570,6 +628,23 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 
   // Invisible keys (outside the chunk or a row's window) get a -inf score.
   auto mask = [&](const int kbase, float (&z)[NG][NRB][8]) {
+    if constexpr (SP) {
+      // A block past the chunk is invisible; otherwise its keys are visible when
+      // their slot is used and they lie below the cached length (q_len 1).
+      const int slot = min(kbase, end - 1) / p.sparse_block;
+      const int bid = kbase < end ? s_blk[g0][slot] : -1;
+      const int k0 = bid * p.sparse_block + (kbase - slot * p.sparse_block);
+      if (bid >= 0 && k0 + kKeyBlock - 1 < cs) return;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool vis = bid >= 0 && k0 + 16 * (k >> 2) + 4 * q4 + (k & 3) < cs;
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+          for (int g = 0; g < NG; ++g) z[g][rb][k] = vis ? z[g][rb][k] : -INFINITY;
+      }
+      return;
+    }
     if (kbase >= lo_all && kbase + kKeyBlock - 1 <= hi_all) return;  // visible to every row
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -948,10 +1023,10 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   if (tid == 0 && p.splits > 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int LU, bool HS, int KW>
+template <int LU, bool HS, int KW, bool SP = false>
 hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
-  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
+  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW, SP>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -976,6 +1051,15 @@ __global__ void zero_counters_kernel(int32_t* c, int n) {
 
 hipError_t launch_step(const StepParams& p, hipStream_t stream) {
   if (p.batch == 0) return hipSuccess;
+  if (p.sparse_block > 0) {
+    // Page-list-driven decode: q_len 1, one KV head per wave (each head has its
+    // own list), blocks of a multiple of 32 keys, at most kMaxSparseTopk slots.
+    if (p.q_len != 1 || p.tgroups != 1 || !p.head_split || p.key_waves != kAttnWaves ||
+        p.sparse_block % kKeyBlock || p.sparse_topk < 1 || p.sparse_topk > kMaxSparseTopk ||
+        !p.block_idx)
+      return hipErrorInvalidValue;
+    return launch_lu<1, true, kAttnWaves, true>(p, stream);
+  }
   if (p.q_len < 1 || p.q_len > kMaxQLen ||
       (p.tgroups != token_groups(p.q_len, false) && p.tgroups != token_groups(p.q_len, true)))
     return hipErrorInvalidValue;

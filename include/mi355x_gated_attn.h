@@ -70,6 +70,10 @@ typedef struct mi355x_gated_attn_config {
                         /* before its one bf16 rounding (page "qk_norm",        */
                         /* QKNormDirectKernel's output scale: a query factor    */
                         /* carried by q, not by sm_scale); 1 = page 1's norm    */
+  int32_t sparse_block; /* 0: dense (window) step.  > 0: page-list-driven decode */
+                        /* (mi355x_gated_attn_sparse_step) over blocks of this   */
+                        /* many keys, a multiple of 32; needs q_len 1, window 0 */
+  int32_t sparse_topk;  /* list slots per (KV head, request), 1..256 when sparse */
 } mi355x_gated_attn_config;
 
 /* Opaque per-configuration context (host memory only). */
@@ -192,6 +196,32 @@ void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx);
 
 /* The calling thread's last error message ("" if none). */
 const char* mi355x_gated_attn_last_error(void);
+
+/*
+ * Page-list-driven (top-k block-sparse) decode step: page "msa.py"
+ * (msa_sparse_decode_main; build_msa_decode_meta places each request's one
+ * query at its last cached position).  The same prologue, combine and gated
+ * epilogue as mi355x_gated_attn_step, with attention restricted per KV head to
+ * the keys of the blocks its list selects: for KV head g and request b,
+ *   keys = union over i < sparse_topk with j = block_idx[(g * B + b) *
+ *          sparse_topk + i] >= 0 of  j*sparse_block .. (j+1)*sparse_block - 1,
+ *          those below cache_seqlens[b] (the new token's key included when its
+ *          block is listed; no window);
+ * query head h uses KV head h / (Hq/Hkv).  An empty set gives output 0.
+ *   block_idx  device int32 [Hkv, B, sparse_topk], -1 for unused slots; block
+ *              indices are logical (key / sparse_block) and distinct within a
+ *              list (a repeated index is a caller error)
+ * Other arguments as mi355x_gated_attn_step (seq_lens is not taken).  The
+ * config must have sparse_block > 0 (INVALID_ARGUMENT otherwise, and
+ * mi355x_gated_attn_step rejects such a config); the plan sizes splits for
+ * sparse_topk * sparse_block keys per head.
+ */
+int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                  const int64_t* positions, const int64_t* cache_loc,
+                                  const int32_t* cache_seqlens, const int32_t* page_table,
+                                  const int32_t* block_idx, void* k_cache, void* v_cache,
+                                  const float* k_scale, const float* v_scale, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Measurement hook (not part of the page's interface): while enabled, each

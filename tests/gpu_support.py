@@ -28,7 +28,7 @@ def abi_config(x: synth.Inputs) -> ga.Config:
     w = x.w
     return ga.make_config(w.batch, w.q_len, w.page_size, w.window, x.max_pages, x.num_pages,
                           w.rope_theta, w.sm_scale, w.kv_scale, w.num_q_heads, w.num_kv_heads,
-                          w.head_dim, w.q_scale)
+                          w.head_dim, w.q_scale, w.sparse_block, w.sparse_topk)
 
 
 def max_context(x: synth.Inputs) -> int:
@@ -53,8 +53,14 @@ class Device:
         self.v_scale = torch.tensor([x.v_scale], dtype=torch.float32, device=dev)
         self.out = torch.zeros((x.w.batch, x.w.q_len, x.w.num_q_heads * x.w.head_dim),
                                dtype=torch.int16, device=dev)
+        self.block_idx = t(x.extra["block_idx"]) if "block_idx" in x.extra else None
 
     def run(self, step: ga.GatedAttnStep, stream=None):
+        if self.block_idx is not None:  # page-list-driven decode
+            step.sparse(self.qkv, self.positions, self.cache_loc, self.cache_seqlens,
+                        self.page_table, self.block_idx, self.k_cache, self.v_cache, self.k_scale,
+                        self.v_scale, self.out, stream)
+            return
         step(self.qkv, self.positions, self.cache_loc, self.cache_seqlens, self.page_table,
              self.seq_lens, self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.out,
              stream)
@@ -90,6 +96,14 @@ class Reference:
 
     def outputs(self, sel_t=None, sel_h=None):
         x = self.x
+        if "block_idx" in x.extra:  # page-list-driven decode: all rows, then the selection
+            o = oracle.sparse_attention(self.cfg, self.q, self.k_cache, self.v_cache,
+                                        x.page_table, x.cache_seqlens, x.extra["block_idx"],
+                                        x.w.sparse_block, x.k_scale, x.v_scale)
+            o = o.reshape(-1, x.w.head_dim)
+            if sel_t is not None:
+                o = o[np.asarray(sel_t) * x.w.num_q_heads + np.asarray(sel_h)]
+            return oracle.epilogue(self.cfg, np.ascontiguousarray(o), x.qkv, sel_t, sel_h)
         o = oracle.attention(self.cfg, self.q, self.k_cache, self.v_cache, x.page_table,
                              x.cache_seqlens, x.k_scale, x.v_scale, sel_t, sel_h)
         return oracle.epilogue(self.cfg, o, x.qkv, sel_t, sel_h)

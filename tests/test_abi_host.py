@@ -304,3 +304,51 @@ def test_qk_norm_binding_checks_shapes_like_the_page():
         ga.qk_norm(torch.zeros((4, 128), dtype=torch.float32), 64)
     assert ga.qk_norm(torch.zeros((0, 128), dtype=torch.bfloat16), 64).shape == (0, 128)
     assert ga.supports_qk_norm(torch.float16, 256) and not ga.supports_qk_norm(torch.float32, 64)
+
+
+# ---- page-list-driven (top-k block-sparse) decode (page "msa.py") -------------
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(sparse_block=128, sparse_topk=16, window=0), ga.MI355X_GA_OK),
+    (dict(sparse_block=32, sparse_topk=256, window=0), ga.MI355X_GA_OK),
+    (dict(sparse_block=128, sparse_topk=16), ga.MI355X_GA_UNSUPPORTED),            # a window
+    (dict(sparse_block=128, sparse_topk=16, window=0, q_len=2), ga.MI355X_GA_UNSUPPORTED),
+    (dict(sparse_block=48, sparse_topk=16, window=0), ga.MI355X_GA_UNSUPPORTED),    # not x32
+    (dict(sparse_block=128, sparse_topk=257, window=0), ga.MI355X_GA_UNSUPPORTED),
+    (dict(sparse_block=128, sparse_topk=0, window=0), ga.MI355X_GA_INVALID_ARGUMENT),
+    (dict(sparse_block=-32, sparse_topk=4, window=0), ga.MI355X_GA_INVALID_ARGUMENT),
+])
+def test_sparse_configs(L, kw, status):
+    assert ga.mi355x_gated_attn_supports(cfg(**kw)) == status
+
+
+def test_sparse_plan_sizes_splits_for_the_listed_keys(L):
+    """topk * block keys per KV head, one KV head per wave: B = 32 with 16
+    blocks of 128 gives 2,048 keys, eight splits (one unit per CU)."""
+    ctx = ga.mi355x_gated_attn_prepare(cfg(sparse_block=128, sparse_topk=16, window=0))
+    try:
+        _, s = ga.mi355x_gated_attn_plan(ctx, 1 << 20, 0)
+        assert s == 8
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_dense_and_sparse_steps_refuse_each_others_configs(L):
+    P = ctypes.c_void_p
+    sparse = ga.mi355x_gated_attn_prepare(cfg(sparse_block=128, sparse_topk=16, window=0))
+    dense = ga.mi355x_gated_attn_prepare(cfg())
+    try:
+        ga.mi355x_gated_attn_plan(sparse, 1 << 20, 0)
+        ga.mi355x_gated_attn_plan(dense, 16385, 0)
+        assert _raw_step(L, sparse) == ga.MI355X_GA_INVALID_ARGUMENT  # dense step, sparse config
+        args = [P(0x1000), P(0x2000), P(0x3000), P(0x4000), P(0x5000), P(0x6000), P(0x10000),
+                P(0x20000), P(0x7000), P(0x8000), P(0x9000), P(0x100000)]
+        assert L.mi355x_gated_attn_sparse_step(dense, *args, 1 << 30, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+        no_list = list(args)
+        no_list[5] = None
+        assert L.mi355x_gated_attn_sparse_step(sparse, *no_list, 1 << 30, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+    finally:
+        ga.mi355x_gated_attn_destroy(sparse)
+        ga.mi355x_gated_attn_destroy(dense)
