@@ -78,11 +78,37 @@ def attended_keys(w, cache_seqlens) -> int:
     return total
 
 
+def sparse_keys(w, x):
+    """Page-list-driven decode: per (KV head, request) the keys of its listed
+    blocks below the cached length (the union), and the listed blocks' pages."""
+    keys = pages = 0
+    bi = x.extra["block_idx"]
+    for g in range(w.num_kv_heads):
+        for b, cs in enumerate(x.cache_seqlens.tolist()):
+            seen, pg = set(), set()
+            for j in bi[g, b].tolist():
+                if j >= 0:
+                    ks = range(j * w.sparse_block, min((j + 1) * w.sparse_block, cs))
+                    seen.update(ks)
+                    pg.update(k // w.page_size for k in ks)
+            keys += len(seen)
+            pages += len(pg)
+    return keys, pages
+
+
 def algorithmic_bytes(w, x):
     """Per step: KV bytes (the metric's numerator), and the step kernel's
     algorithmic bytes: KV rows and page-table entries of the attended keys, plus
     per token the projection row, its two K/V row stores, its output row and its
-    position and cache row."""
+    position and cache row.  Page-list-driven decode reads one KV head's half of
+    a row per (head, listed key), and its block lists."""
+    per_token = (w.width * 2 + 2 * w.num_kv_heads * w.head_dim
+                 + w.num_q_heads * w.head_dim * 2 + 16)
+    if w.sparse_block > 0:
+        keys, pages = sparse_keys(w, x)
+        kv = keys * w.head_dim * 2
+        lists = 4 * w.num_kv_heads * w.batch * w.sparse_topk
+        return kv, kv + 4 * pages + lists + x.tokens * per_token
     keys = attended_keys(w, x.cache_seqlens)
     kv = keys * w.num_kv_heads * w.head_dim * 2
     pages = 0
@@ -90,8 +116,6 @@ def algorithmic_bytes(w, x):
         first = cs - w.q_len - (w.window - 1 if w.window > 0 else cs)
         first = max(first, 0)
         pages += (cs - 1) // w.page_size - first // w.page_size + 1
-    per_token = (w.width * 2 + 2 * w.num_kv_heads * w.head_dim
-                 + w.num_q_heads * w.head_dim * 2 + 16)
     return kv, kv + 4 * pages + x.tokens * per_token
 
 
@@ -128,7 +152,8 @@ def cpu_baseline(x, budget_s: float):
     layer pool 0's inputs until the time budget is used (at least one step)."""
     import numpy as np
     import oracle
-    cfg = oracle.Config(q_scale=x.w.q_scale, batch=x.w.batch, q_len=x.w.q_len, num_q_heads=x.w.num_q_heads,
+    cfg = oracle.Config(q_scale=x.w.q_scale, batch=x.w.batch, q_len=x.w.q_len,
+                        num_q_heads=x.w.num_q_heads,
                         num_kv_heads=x.w.num_kv_heads, head_dim=x.w.head_dim,
                         page_size=x.w.page_size, window=x.w.window, max_pages=x.max_pages,
                         num_pages=x.num_pages, rope_theta=x.w.rope_theta,
@@ -137,8 +162,13 @@ def cpu_baseline(x, budget_s: float):
     n = 0
     t0 = time.perf_counter()
     while True:
-        oracle.step(cfg, x.qkv, x.positions, x.cache_loc, x.cache_seqlens, x.page_table, kc, vc,
-                    x.k_scale, x.v_scale)
+        if x.w.sparse_block > 0:
+            oracle.sparse_step(cfg, x.qkv, x.positions, x.cache_loc, x.cache_seqlens,
+                               x.page_table, x.extra["block_idx"], x.w.sparse_block, kc, vc,
+                               x.k_scale, x.v_scale)
+        else:
+            oracle.step(cfg, x.qkv, x.positions, x.cache_loc, x.cache_seqlens, x.page_table, kc,
+                        vc, x.k_scale, x.v_scale)
         n += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -312,7 +342,8 @@ def main():
           f"touched per step", file=sys.stderr, flush=True)
 
     cfg = ga.make_config(w.batch, w.q_len, w.page_size, w.window, x0.max_pages, x0.num_pages,
-                         w.rope_theta, w.sm_scale, w.kv_scale, q_scale=w.q_scale)
+                         w.rope_theta, w.sm_scale, w.kv_scale, q_scale=w.q_scale,
+                         sparse_block=w.sparse_block, sparse_topk=w.sparse_topk)
     step = ga.GatedAttnStep(cfg, int(w.seq_hi + w.q_len), args.splits)
 
     # Layer pools: pool 0 is the tests' seeded input; the others are drawn on
@@ -357,8 +388,16 @@ def main():
         layers.append(dict(qkv=qkv, cache_loc=cl, page_table=pt, k_cache=kc, v_cache=vc, out=out))
     torch.cuda.synchronize()
 
+    # Page-list-driven decode: pool 0's block lists serve every layer (each
+    # layer's own page table and caches still make its rows its own).
+    block_idx = (torch.from_numpy(x0.extra["block_idx"]).to(dev) if w.sparse_block > 0 else None)
+
     def run(li, stream=None):
         L_ = layers[li]
+        if block_idx is not None:
+            step.sparse(L_["qkv"], positions, L_["cache_loc"], cache_seqlens, L_["page_table"],
+                        block_idx, L_["k_cache"], L_["v_cache"], k_scale, v_scale, L_["out"], stream)
+            return
         step(L_["qkv"], positions, L_["cache_loc"], cache_seqlens, L_["page_table"], seq,
              L_["k_cache"], L_["v_cache"], k_scale, v_scale, L_["out"], stream)
 

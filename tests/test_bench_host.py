@@ -65,3 +65,21 @@ def test_traffic_comes_only_from_the_workloads_own_counters():
     if os.path.exists(bench.counters_file("swa_decode")):
         t = bench.load_traffic("swa_decode")
         assert t is None or t > 0
+
+
+def test_sparse_bytes_count_each_heads_listed_keys_once():
+    import dataclasses
+    w = dataclasses.replace(synth.small(batch=3, q_len=1, page_size=8, seq_lo=100, seq_hi=400),
+                            sparse_block=32, sparse_topk=4)
+    x = synth.make_inputs(w)
+    kv, total = bench.algorithmic_bytes(w, x)
+    brute = 0
+    for g in range(2):
+        for b, cs in enumerate(x.cache_seqlens.tolist()):
+            keys = set()
+            for j in x.extra["block_idx"][g, b].tolist():
+                if j >= 0:
+                    keys.update(k for k in range(j * 32, (j + 1) * 32) if k < cs)
+            brute += len(keys)
+    assert kv == brute * 64 * 2
+    assert total > kv
