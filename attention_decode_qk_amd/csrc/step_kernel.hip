@@ -212,6 +212,38 @@ __device__ inline KvBlock<NG> load_kv(const StepParams& p, int2 entry, int kk, i
   return d;
 }
 
+// The norm alone (norm_rope8 without its RoPE) and the RoPE alone, for a
+// prologue that computes the sincos table while the norms run.
+__device__ inline void norm8(const float (&x)[8], float scale, float (&y)[8]) {
+#pragma clang fp contract(off)
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) ss += (double)(x[k] * x[k]);
+  ss = sum8(ss);
+  const float ms = (float)ss / 64.0f;
+  const float inv = rsqrt_exact(ms + 1.0e-5f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = x[k] * inv;
+  if (scale != 1.0f) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = y[k] * scale;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k]);
+}
+
+__device__ inline void rope8(const float (*cs)[2], int c8, float (&y)[8]) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int pr = 0; pr < 4; ++pr) {
+    const float c = cs[c8 * 4 + pr][0], s = cs[c8 * 4 + pr][1];
+    const float e = y[2 * pr], o = y[2 * pr + 1];
+    const float ec = e * c, os = o * s, oc = o * c, es = e * s;
+    y[2 * pr] = round_bf16(ec - os);
+    y[2 * pr + 1] = round_bf16(oc + es);
+  }
+}
+
 // Norm (+ RoPE) of one 8-column slice of a head row, page order, every fp32 step
 // rounded once (no contraction): fp64-exact sum of squares over the 8 lanes of
 // the row, exact rsqrt, fp32 product (times `scale`, exact when 1), bf16; RoPE
@@ -389,13 +421,20 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     xv[it] = *reinterpret_cast<const uint4*>(qkv_b + min(item_token(item), L - 1) * kWidth +
                                               item_row(item) * kHeadDim + (item & 7) * 8);
   }
-  const bool cs_thread = p.rope && tid < 32 * L;
+  // The sincos table's (token, frequency) threads: the first 32 L, or, when a
+  // one-token unit leaves threads without an item, the last 32, which then
+  // compute it while the item threads compute their norms.
+  constexpr bool kIdleCs = kOneGroup && kMaxItems + 32 * LU <= kThreads;
+  constexpr int kCsBase = kIdleCs ? kThreads - 32 * LU : 0;
+  const bool cs_thread = kIdleCs ? p.rope && tid >= kCsBase && tid < kCsBase + 32 * L
+                                 : p.rope && tid < 32 * L;
   int64_t my_slot = p.cache_loc[tok0 + min(tid, L - 1)];
   // Raw position and frequency now; the angle (which waits for them) after the
   // K/V loads.  Without RoPE, positions may be absent: read a cache row index
   // instead (same type, always present) and ignore it.
   const int64_t* pos_src = p.rope ? p.positions : p.cache_loc;
-  int64_t my_pos = pos_src[tok0 + min(tid >> 5, L - 1)];
+  int64_t my_pos = kIdleCs ? pos_src[tok0 + min(max((tid - kCsBase) >> 5, 0), L - 1)]
+                           : pos_src[tok0 + min(tid >> 5, L - 1)];
   float my_freq = p.inv_freq[tid & 31];
   asm volatile("" ::: "memory");  // ... and ahead of the K/V loads, so waiting for them never waits for K/V
 
@@ -430,6 +469,61 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   };
 
   // RoPE table for the request's tokens: (token, frequency) per thread.
+  auto sincos_table = [&]() {  // (one-token units with idle threads)
+    if (cs_thread) {
+      const float my_ang = (float)my_pos * my_freq;
+      double sd, cd;
+      sincos((double)my_ang, &sd, &cd);
+      s_cs[(tid - kCsBase) >> 5][tid & 31][0] = (float)cd;
+      s_cs[(tid - kCsBase) >> 5][tid & 31][1] = (float)sd;
+    }
+  };
+  if constexpr (kIdleCs) {
+    // One item per thread: its norm, then (after the table) RoPE and the codes.
+    static_assert(kItemIters == 1, "one item per thread");
+    const int item = tid;
+    const int i = min(item_token(item), L - 1);
+    const int hr = item_row(item), c8 = item & 7;
+    const bool is_q = item < kQItems;
+    const bool active = !(item >= kItems || item_token(item) >= L || (!is_q && !chunk_has(i)));
+    float y[8];
+    if (active) {
+      float x[8];
+      const uint32_t w[4] = {xv[0].x, xv[0].y, xv[0].z, xv[0].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_value(w[k] & 0xffffu);
+        x[2 * k + 1] = bf16_value(w[k] >> 16);
+      }
+      if (hr < kQHeads + kKvHeads) {
+        norm8(x, is_q ? p.q_scale : 1.0f, y);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[k] = p.scaled ? round_bf16(x[k] / vs) : x[k];  // raw value
+      }
+    }
+    sincos_table();
+    lds_barrier();
+    if (active) {
+      if (hr < kQHeads + kKvHeads) {
+        if (p.rope) rope8(s_cs[i], c8, y);
+        if (hr >= kQHeads && p.scaled) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k] / ks);
+        }
+      }
+      const uint2 codes = pack_e4m3x8(y);
+      if (is_q) {
+        *reinterpret_cast<uint2*>(&s_q[i - t_lo][hr][c8 * 8]) = codes;
+        if (kc == 0)
+          *reinterpret_cast<uint2*>(p.q_out + ((tok0 + i) * kQHeads + hr) * kHeadDim + c8 * 8) = codes;
+      } else if (hr < kQHeads + kKvHeads) {
+        *reinterpret_cast<uint2*>(&s_newk[i][(hr - kQHeads) * kHeadDim + c8 * 8]) = codes;
+      } else {
+        *reinterpret_cast<uint2*>(&s_newv[i][(hr - kQHeads - kKvHeads) * kHeadDim + c8 * 8]) = codes;
+      }
+    }
+  } else {
   if (cs_thread) {
     const float my_ang = (float)my_pos * my_freq;
     double sd, cd;
@@ -475,6 +569,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       *reinterpret_cast<uint2*>(&s_newv[i][(hr - kQHeads - kKvHeads) * kHeadDim + c8 * 8]) = codes;
     }
   }
+  }  // kIdleCs
   lds_barrier();
 
   if (tid < L && tg == 0 && (SP ? kc == 0 : chunk_has(tid)) && my_slot >= 0 && my_slot < p.num_rows) {
