@@ -44,6 +44,9 @@ CASES = [
     dict(batch=2, q_len=1, window=1),
     dict(batch=2, q_len=3, window=0, num_q_heads=4, num_kv_heads=2),
     dict(batch=1, q_len=1, window=0, sm_scale=5.473 / 8),
+    # extend / prefill (q_len >> 8): causal inside the block, per-query windows
+    dict(batch=2, q_len=40, window=0, page_size=8),
+    dict(batch=1, q_len=67, window=24, rope_theta=500000.0, page_size=1),
 ]
 
 
