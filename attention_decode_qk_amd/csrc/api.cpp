@@ -138,8 +138,10 @@ int mi355x_gated_attn_supports(const mi355x_gated_attn_config* c) {
   if (c->num_q_heads != kQHeads || c->num_kv_heads != kKvHeads)
     return fail(MI355X_GA_UNSUPPORTED, "heads %d/%d: this build serves %d query / %d KV heads",
                 c->num_q_heads, c->num_kv_heads, kQHeads, kKvHeads);
-  if (c->q_len > kMaxQLen)
-    return fail(MI355X_GA_UNSUPPORTED, "q_len %d: this build serves 1..%d", c->q_len, kMaxQLen);
+  if (c->q_len > kMaxExtendLen)
+    return fail(MI355X_GA_UNSUPPORTED, "q_len %d: this build serves 1..%d", c->q_len, kMaxExtendLen);
+  if (c->q_len > kMaxQLen && (int64_t)c->batch * c->q_len > (int64_t)INT32_MAX)
+    return fail(MI355X_GA_UNSUPPORTED, "extend: batch * q_len exceeds one launch's 2^31 - 1 workgroups");
   if ((int64_t)c->max_pages * c->page_size > (int64_t)1 << 30)
     return fail(MI355X_GA_UNSUPPORTED, "max_pages * page_size exceeds 2^30 keys per request");
   if (c->num_pages * (int64_t)c->page_size >= (int64_t)1 << 31)
@@ -179,6 +181,27 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (num_splits < 0 || num_splits > kMaxSplits)
     return fail(MI355X_GA_INVALID_ARGUMENT, "num_splits %d outside 0..%d", num_splits, kMaxSplits);
   const auto& c = ctx->cfg;
+  const size_t T = (size_t)c.batch * c.q_len;
+  if (c.q_len > kMaxQLen) {
+    // Extend / prefill: one unit per (request, 16-token tile, KV head) walks its
+    // whole key range, so there are no partials: the workspace holds q only
+    // (and the per-request counters that workspace_init clears).
+    if (num_splits > 1)
+      return fail(MI355X_GA_UNSUPPORTED, "q_len %d > %d runs without a key split (num_splits %d)",
+                  c.q_len, kMaxQLen, num_splits);
+    ctx->q_bytes = T * kQHeads * kHeadDim;
+    ctx->po_off = ctx->pml_off = ctx->cnt_off = align_up(ctx->q_bytes, 256);
+    ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)c.batch * sizeof(int32_t), 256);
+    if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
+    ctx->splits = 1;
+    ctx->groups = 1;
+    ctx->head_split = false;
+    ctx->key_waves = kAttnWaves;
+    ctx->planned = true;
+    if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
+    if (num_splits_out) *num_splits_out = 1;
+    return ok();
+  }
   const bool sparse = c.sparse_block > 0;
   int64_t keys = max_context;  // union of a request's visible keys
   if (c.window > 0) keys = std::min<int64_t>(keys, (int64_t)c.window + c.q_len - 1);
@@ -215,7 +238,6 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   }
   if ((int64_t)c.batch * groups * s > (int64_t)INT32_MAX)
     return fail(MI355X_GA_UNSUPPORTED, "batch %d x %d splits exceeds one launch's workgroups", c.batch, s);
-  const size_t T = (size_t)c.batch * c.q_len;
   const size_t rows = T * kQHeads;  // (token, q head) rows
   ctx->q_bytes = T * kQHeads * kHeadDim;
   ctx->po_off = align_up(ctx->q_bytes, 256);

@@ -28,6 +28,7 @@ constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
 constexpr int kMaxTokensPerUnit = 4;
 constexpr int kMaxSparseTopk = 256;  // list slots per (KV head, request) of page-list-driven decode
+constexpr int kMaxExtendLen = 65536;  // longest extend / prefill block (q_len > kMaxQLen) served
 constexpr int token_groups(int q_len, bool short_keys) {
   return short_keys ? (q_len + 1) / 2 : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit;
 }

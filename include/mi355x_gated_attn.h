@@ -1,8 +1,9 @@
 /*
  * mi355x_gated_attn.h -- C ABI of the MI355X (gfx950) gated-attention step.
  *
- * One decoder layer's attention step for a decode (q_len 1) or speculative
- * verify (q_len up to 8) batch, at one GPU's head share, as defined on the
+ * One decoder layer's attention step for a decode (q_len 1), speculative
+ * verify (q_len up to 8) or extend / prefill (a block of up to 65536 new
+ * tokens per request) batch, at one GPU's head share, as defined on the
  * page "012-attention-local-splits.py" (SGLang's Muse Spark Open gated
  * attention, FP8 e4m3 KV cache).  In the page's order (module docstring):
  *
@@ -53,7 +54,7 @@ enum {
  */
 typedef struct mi355x_gated_attn_config {
   int32_t batch;        /* B >= 0 requests; B == 0 makes every step a no-op     */
-  int32_t q_len;        /* L new tokens per request, 1..8 (causal in the block) */
+  int32_t q_len;        /* L new tokens per request, 1..65536 (causal in the block) */
   int32_t num_q_heads;  /* Hq; this build serves 16 (one GPU's share under TP8) */
   int32_t num_kv_heads; /* Hkv; this build serves 2; q head h reads h/(Hq/Hkv)  */
   int32_t head_dim;     /* D; 64                                                */
@@ -81,7 +82,8 @@ typedef struct mi355x_gated_attn_ctx mi355x_gated_attn_ctx;
 
 /*
  * Whether this build serves cfg: returns MI355X_GA_OK, MI355X_GA_UNSUPPORTED
- * (head_dim != 64, Hq != 16, Hkv != 2, q_len outside 1..8) or
+ * (head_dim != 64, Hq != 16, Hkv != 2, q_len outside 1..65536, B * q_len
+ * beyond 2^31 - 1 for q_len > 8) or
  * MI355X_GA_INVALID_ARGUMENT (negative or zero sizes, window < 0,
  * rope_theta < 0, non-finite or non-positive scales).  Pure host code.
  */
@@ -107,6 +109,10 @@ int mi355x_gated_attn_prepare(const mi355x_gated_attn_config* cfg, int device,
  * unit per (request, group, split): G = ceil(L/2) when the key range (the
  * window + L - 1, or max_context) is at most 4096 keys, else ceil(L/4).  A step
  * launches B * G * splits workgroups (UNSUPPORTED beyond 2^31-1).
+ * q_len > 8 (extend / prefill; page "msa.py", msa_sparse_prefill_main: causal
+ * attention with the query offset = the prefix length, here dense) is planned
+ * without a key split: num_splits must be 0 or 1 (UNSUPPORTED otherwise) and
+ * the chosen count is 1.
  * Outputs (either may be NULL): *workspace_bytes = the workspace a step needs,
  * *num_splits_out = the chosen split count.  Host-only.
  */
@@ -153,7 +159,9 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
  * One layer-step, asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream); the calling thread's current device must be the ctx's device.
  * No host synchronisation, allocation or device-value read: capturable.
- * The whole step is one kernel launch.
+ * The whole step is one kernel launch for q_len <= 8; for q_len > 8 it is two
+ * (the prologue of every new token, then attention and epilogue, which reads
+ * the new keys back from the cache rows the first launch stored).
  *
  *   qkv            bf16 [B, L, (2Hq + 2Hkv) * D], rows contiguous: q heads |
  *                  k heads | v heads | gate logits (Hq*D); 16-byte aligned
@@ -181,7 +189,8 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
  *                  aligned, initialised once by mi355x_gated_attn_workspace_init.
  *                  Layout after a step: bytes [0, B*L*Hq*D) hold q as e4m3
  *                  [B*L, Hq, D]; then split partials and B*G int32
- *                  counters (G token groups per request, from the plan).
+ *                  counters (G token groups per request, from the plan; for
+ *                  q_len > 8 no partials and B counters).
  * Calls that share a workspace, or write the same cache rows, must be ordered
  * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
  */

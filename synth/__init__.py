@@ -85,6 +85,16 @@ SPARSE = {
 }
 WORKLOADS.update(SPARSE)
 
+# Extend / prefill blocks (q_len >> 8) through the same step: a 1,024-token
+# chunk per request over an 8k-16k prefix with page 1's window and RoPE, and
+# page 2's prefill shape (blocks of 128 keys, one page each, causal from the
+# prefix length) as 2,048 new tokens over a 4k-8k prefix, full attention.
+EXTEND = {
+    "swa_extend": Workload("swa_extend", 4, 1024, 8192, 16384, 2048, 500000.0, seed=1009),
+    "full_extend": Workload("full_extend", 2, 2048, 4096, 8192, 0, 0.0, page_size=128, seed=1010),
+}
+WORKLOADS.update(EXTEND)
+
 
 @dataclass
 class Inputs:

@@ -47,7 +47,7 @@ def cfg(**kw):
 
 
 def test_supports_accepts_the_served_shapes(L):
-    for q_len in range(1, 9):
+    for q_len in list(range(1, 9)) + [9, 16, 67, 4096, 65536]:
         assert ga.mi355x_gated_attn_supports(cfg(q_len=q_len)) == ga.MI355X_GA_OK
     assert ga.mi355x_gated_attn_supports(cfg(batch=0)) == ga.MI355X_GA_OK
     assert ga.mi355x_gated_attn_supports(cfg(page_size=64, window=0, rope_theta=0.0,
@@ -58,7 +58,8 @@ def test_supports_accepts_the_served_shapes(L):
     (dict(head_dim=128), ga.MI355X_GA_UNSUPPORTED),
     (dict(num_q_heads=15), ga.MI355X_GA_UNSUPPORTED),
     (dict(num_q_heads=8, num_kv_heads=1), ga.MI355X_GA_UNSUPPORTED),
-    (dict(q_len=9), ga.MI355X_GA_UNSUPPORTED),
+    (dict(q_len=65537), ga.MI355X_GA_UNSUPPORTED),
+    (dict(batch=65536, q_len=65536), ga.MI355X_GA_UNSUPPORTED),
     (dict(q_len=0), ga.MI355X_GA_INVALID_ARGUMENT),
     (dict(batch=-1), ga.MI355X_GA_INVALID_ARGUMENT),
     (dict(page_size=0), ga.MI355X_GA_INVALID_ARGUMENT),
@@ -352,3 +353,27 @@ def test_dense_and_sparse_steps_refuse_each_others_configs(L):
     finally:
         ga.mi355x_gated_attn_destroy(sparse)
         ga.mi355x_gated_attn_destroy(dense)
+
+
+@pytest.mark.parametrize("q_len", [9, 100, 4096])
+def test_extend_plan_holds_q_only_and_runs_without_a_split(L, q_len):
+    """q_len > 8 (extend / prefill) walks each tile's whole key range: one split,
+    no partials, the workspace = the q codes + the per-request counters."""
+    B = 5
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=B, q_len=q_len), 0)
+    try:
+        nbytes, splits = ga.mi355x_gated_attn_plan(ctx, 200000, 0)
+        assert splits == 1
+        q = B * q_len * 16 * 64
+        assert nbytes == -(-(-(-q // 256) * 256 + 4 * B) // 256) * 256
+        assert ga.mi355x_gated_attn_plan(ctx, 200000, 1) == (nbytes, 1)
+        with pytest.raises(ga.GatedAttnError) as e:
+            ga.mi355x_gated_attn_plan(ctx, 200000, 2)
+        assert e.value.status == ga.MI355X_GA_UNSUPPORTED
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_extend_refuses_page_list_driven_configs(L):
+    assert ga.mi355x_gated_attn_supports(
+        cfg(q_len=16, window=0, sparse_block=32, sparse_topk=4)) == ga.MI355X_GA_UNSUPPORTED

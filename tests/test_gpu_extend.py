@@ -1,0 +1,139 @@
+"""GPU parity of the step at extend / prefill sizes (q_len > 8: a block of new
+tokens per request, causal inside the block from the prefix length on, page 1's
+window per query; page 2's prefill calls the same attention with the query
+offset = prefix length) against the oracle, through the C ABI.  Bar: q and cache
+bytes exact (one e4m3 code on at most 0.1% of written elements allowed); bf16
+outputs within 2e-2 absolute + 2e-2 relative."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_support import (Device, Reference, abi_config, assert_codes_match, assert_outputs_close,
+                         check_full, max_context, run_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+# 16-token tiles: 9 (one ragged tile), 16 (one whole tile), 17, 33 (a one-token
+# tail), 40, 64 and 200 (many tiles, ragged); windows shorter than a tile, than
+# the block and longer; pages of 1, 3, 16, 64 rows.
+SMALL = {
+    "ext9_full": dict(batch=3, q_len=9, window=0),
+    "ext16_swa_rope": dict(batch=2, q_len=16, window=24, rope_theta=500000.0),
+    "ext17_page16": dict(batch=3, q_len=17, window=0, page_size=16),
+    "ext33_scaled_page64": dict(batch=2, q_len=33, window=0, page_size=64, kv_scale=0.5,
+                                qkv_std=1.4142135),
+    "ext40_window1": dict(batch=2, q_len=40, window=1),
+    "ext40_window5_page4": dict(batch=2, q_len=40, window=5, page_size=4),
+    "ext64_swa_rope_q_scaled": dict(batch=2, q_len=64, window=100, rope_theta=500000.0,
+                                    q_scale=5.473),
+    "ext100_window50": dict(batch=2, q_len=100, window=50, rope_theta=500000.0, page_size=16),
+    "ext200_page3": dict(batch=2, q_len=200, window=0, page_size=3),
+    "ext67_b5_swa": dict(batch=5, q_len=67, window=300, rope_theta=500000.0, page_size=8),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_extend_small_case_matches_oracle(name):
+    w = synth.small(name=name, seq_lo=20, seq_hi=700, **SMALL[name])
+    x = synth.make_inputs(w, seed=300 + len(name))
+    _say(f"[gpu] extend {name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}")
+    res = run_gpu(x)
+    assert res.splits == 1
+    check_full(x, res, Reference(x), name)
+
+
+def test_extend_fresh_prefill_whole_context_in_the_block():
+    """Prefixes of 1-3 tokens: the block is (nearly) the whole context, so each
+    row's keys are mostly its own block's new keys, read back from the cache."""
+    w = synth.small(name="fresh", batch=3, q_len=130, window=0, seq_lo=1, seq_hi=3, page_size=16)
+    x = synth.make_inputs(w, seed=9)
+    _say("[gpu] extend fresh prefill L=130")
+    res = run_gpu(x)
+    check_full(x, res, Reference(x), "fresh")
+
+
+def test_extend_padded_slot_stores_nothing_and_outputs_zero():
+    """A slot with cache_seqlens 0 and cache_loc -1 for all its tokens (a padded
+    batch slot) writes no cache row and outputs zeros; the others are unaffected."""
+    w = synth.small(name="pad", batch=3, q_len=20, window=0, seq_lo=50, seq_hi=200)
+    x = synth.make_inputs(w, seed=8)
+    L = w.q_len
+    x.cache_seqlens[1] = 0
+    x.cache_loc[L:2 * L] = -1
+    _say("[gpu] extend padded slot")
+    res = run_gpu(x)
+    ref = Reference(x)
+    np.testing.assert_array_equal(res.k_cache, ref.k_cache)
+    np.testing.assert_array_equal(res.v_cache, ref.v_cache)
+    assert np.all(res.out[1] == 0)
+    assert_outputs_close(res.out, ref.outputs().reshape(res.out.shape), "extend pad")
+
+
+def test_extend_graph_replay_matches_eager():
+    """The two launches captured in a HIP graph and replayed several times, with
+    eager work and synchronisation between replays: every replay equals eager."""
+    import attention_decode_qk_amd as ga
+    w = synth.small(name="graph", batch=2, q_len=48, window=40, rope_theta=500000.0,
+                    seq_lo=100, seq_hi=400, page_size=4)
+    x = synth.make_inputs(w, seed=22)
+    _say("[gpu] extend graph replay")
+    step = ga.GatedAttnStep(abi_config(x), max_context(x))
+    d = Device(x)
+    d.run(step)
+    torch.cuda.synchronize()
+    eager_out = d.out.clone()
+    eager_k, eager_v = d.k_cache.clone(), d.v_cache.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.run(step, stream=s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            d.run(step, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        d.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, eager_out), f"replay {rep}"
+        assert torch.equal(d.k_cache, eager_k) and torch.equal(d.v_cache, eager_v)
+    step.close()
+
+
+def _sample_rows(T, hq, rng, n=96):
+    t = [0] * hq + [T - 1] * hq + list(rng.integers(0, T, n))
+    h = list(range(hq)) * 2 + list(rng.integers(0, hq, n))
+    return np.array(t, np.int64), np.array(h, np.int32)
+
+
+@pytest.mark.parametrize("name", list(synth.EXTEND))
+def test_extend_full_size_workload(name):
+    """Every q and cache byte and sampled output rows of one full-size extend."""
+    w = synth.WORKLOADS[name]
+    _say(f"[gpu] full-size {name}: generating inputs")
+    x = synth.make_inputs(w)
+    _say(f"[gpu] full-size {name}: running step (B={w.batch} L={w.q_len})")
+    res = run_gpu(x)
+    _say(f"[gpu] full-size {name}: oracle prologue")
+    ref = Reference(x)
+    written = x.tokens * w.num_kv_heads * w.head_dim
+    assert_codes_match(res.q, ref.q, ref.q.size, name + " q")
+    assert_codes_match(res.k_cache, ref.k_cache, written, name + " k_cache")
+    assert_codes_match(res.v_cache, ref.v_cache, written, name + " v_cache")
+    rng = np.random.default_rng(11)
+    st, sh = _sample_rows(x.tokens, w.num_q_heads, rng)
+    _say(f"[gpu] full-size {name}: oracle attention on {len(st)} rows")
+    out_ref = ref.outputs(st, sh)
+    got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
+    assert_outputs_close(got, out_ref, name + " out")
