@@ -382,8 +382,11 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
     ctx->events_used += 2;
   }
   hipError_t e = hipSuccess;
-  if (ev) e = hipEventRecord(ev[0], st);
-  if (e == hipSuccess) e = launch_step(sp, st);
+  // The hook times the attention kernel: the whole step for q_len <= 8, the
+  // second launch of an extend step.
+  const bool extend = c.q_len > kMaxQLen;
+  if (ev && !extend) e = hipEventRecord(ev[0], st);
+  if (e == hipSuccess) e = launch_step(sp, st, ev && extend ? ev[0] : nullptr);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();

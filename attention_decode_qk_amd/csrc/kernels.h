@@ -79,7 +79,9 @@ struct StepParams {
   float inv_freq[kHeadDim / 2];
 };
 
-hipError_t launch_step(const StepParams& p, hipStream_t stream);
+// attn_start (may be null): for q_len > kMaxQLen, an event recorded between
+// the prologue launch and the attention launch.
+hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_start = nullptr);
 
 // Per-head RMSNorm with an output scale (qk_norm_kernel.hip).
 struct QkNormParams {

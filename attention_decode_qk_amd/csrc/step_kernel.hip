@@ -1131,6 +1131,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 constexpr int kExtTile = 16;                 // new tokens per attention unit
 constexpr int kExtRows = kExtTile * kGroup;  // 128 query rows
 constexpr int kExtStride = kHeadDim + 16;    // LDS bytes per staged key row (bank spread)
+constexpr int kXcds = 8;                     // MI355X: accelerator complex dies, one L2 each
 
 // One workgroup per new token: 160 items (16 q, 2 k, 2 v head rows x 8
 // column slices), the sincos table on 32 threads that hold no item.
@@ -1196,9 +1197,16 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
   __shared__ __align__(16) float s_o[kExtRows][kHeadDim + 4];
   const int L = p.q_len;
   const int n_tiles = (L + kExtTile - 1) / kExtTile;
-  const int tile = blockIdx.x % n_tiles;
-  const int bg = blockIdx.x / n_tiles;
-  const int g = bg % kKvHeads, b = bg / kKvHeads;
+  // Units in (request, tile, KV head) order, a contiguous range of them per
+  // XCD (workgroups reach the XCDs round-robin): one L2 then holds a request's
+  // keys for its neighbouring tiles and both KV heads, which share each cache
+  // row.  The grid is padded to a multiple of kXcds; the padding exits.
+  const int n_units = p.batch * n_tiles * kKvHeads;
+  const int per_xcd = (n_units + kXcds - 1) / kXcds;
+  const int unit = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (unit >= n_units) return;
+  const int g = unit % kKvHeads;
+  const int tile = (unit / kKvHeads) % n_tiles, b = unit / (kKvHeads * n_tiles);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 15, q4 = lane >> 4;
   const int cs = p.cache_seqlens[b];
@@ -1233,7 +1241,9 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
 
   // Staging: thread -> (K or V, key of the block, 16-byte quarter of the row).
   const int st_v = tid >> 7, st_key = (tid >> 2) & 31, st_c = tid & 3;
-  auto st_keyof = [&](int blk) { return min(lo + blk * kKeyBlock + st_key, hi); };
+  // Keys past hi reload key hi (masked); with no key at all (hi < lo, hi maybe
+  // negative) key 0, in bounds and unused.
+  auto st_keyof = [&](int blk) { return max(min(lo + blk * kKeyBlock + st_key, hi), 0); };
   auto st_entry = [&](int blk) { return page_entry(p, pt, st_keyof(blk)); };
   auto st_load = [&](int entry, int blk) {
     const int row = key_row(p, entry, st_keyof(blk));
@@ -1248,21 +1258,32 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  uint4 data = make_uint4(0, 0, 0, 0);
-  int e_next = 0;
-  if (nblk > 0) {
-    data = st_load(st_entry(0), 0);
-    e_next = st_entry(min(1, nblk - 1));
-  }
-  for (int blk = 0; blk < nblk; ++blk) {
+  // Loads run two blocks ahead of the compute (a gather's latency exceeds one
+  // block's compute), page-table entries two blocks ahead of the loads; the
+  // two register sets alternate, so each wait is for the oldest load only.
+  // Primed unconditionally and in the loop's own issue order (data, entry,
+  // data, entry), so the compiler's wait counts at the loop head stay exact.
+  const int last = max(nblk - 1, 0);
+  const int e0 = st_entry(0), e1 = st_entry(min(1, last));
+  uint4 dA = st_load(e0, 0);
+  int eA = st_entry(min(2, last));
+  uint4 dB = st_load(e1, min(1, last));
+  int eB = st_entry(min(3, last));
+  // The q operands are taken here, once (issued first, they are in by now):
+  // a first use inside the loop would make every iteration wait for all loads.
+  asm volatile("" ::"v"(qop[0][0]), "v"(qop[0][1]), "v"(qop[1][0]), "v"(qop[1][1]));
+  auto block_step = [&](const int blk, uint4& data, int& e_next) {
     const int buf = blk & 1;
     *reinterpret_cast<uint4*>(st_v ? &s_v[buf][st_key][st_c * 16] : &s_k[buf][st_key][st_c * 16]) = data;
     lds_barrier();  // block blk staged; block blk-2's reads of this buffer are behind every wave
-    if (blk + 1 < nblk) {
-      data = st_load(e_next, blk + 1);
-      e_next = st_entry(min(blk + 2, nblk - 1));
-    }
+    // Unconditional (the last blocks reload block nblk - 1, in bounds and
+    // unused), so the loop has no branch around its loads.
+    data = st_load(e_next, min(blk + 2, last));
+    e_next = st_entry(min(blk + 4, last));
     const int kbase = lo + blk * kKeyBlock;
+    // Interior: every key <= the first row's position (so <= hi) and inside the
+    // last real row's window.
+    const bool edge = !(kbase + kKeyBlock - 1 <= p_first && (p.window == 0 || kbase >= hi - p.window + 1));
     // V^T operand of the block (keys 16(r/4) + 4 q4 + r % 4, columns 4j..4j+3).
     uint32_t vr[8];
 #pragma unroll
@@ -1301,11 +1322,14 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) z[t * 4 + ii] = c[ii];
       }
-      // Causal and window mask of the row (every key of the block is <= hi).
+      // Causal and window mask of the row, on edge blocks only (an interior
+      // block is visible to every real row; padding rows are never stored).
+      if (edge) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
-        z[k] = (key <= prow[rb] && key >= plo[rb]) ? z[k] : -INFINITY;
+        for (int k = 0; k < 8; ++k) {
+          const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
+          z[k] = (key <= prow[rb] && key >= plo[rb]) ? z[k] : -INFINITY;
+        }
       }
       float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], -INFINITY));
       const float lmx = m * scale;
@@ -1333,7 +1357,15 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
       for (int c = 0; c < 4; ++c)
         acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[c], pv, acc[rb][c], 0, 0, 0);
     }
+  };
+  // Whole pairs in the loop (its back edge always follows the second half, so
+  // the loads are always in the same order there), an odd last block after it.
+  int blk = 0;
+  for (; blk + 1 < nblk; blk += 2) {
+    block_step(blk, dA, eA);
+    block_step(blk + 1, dB, eB);
   }
+  if (blk < nblk) block_step(blk, dA, eA);
 
   // o / l of every row to LDS (column 16 q4 + 4 ii + c of row 32 wave + 16 rb + j).
 #pragma unroll
@@ -1398,16 +1430,18 @@ __global__ void zero_counters_kernel(int32_t* c, int n) {
 
 }  // namespace
 
-hipError_t launch_step(const StepParams& p, hipStream_t stream) {
+hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_start) {
   if (p.batch == 0) return hipSuccess;
   if (p.q_len > kMaxQLen) {  // extend / prefill: prologue, then attention + epilogue
     if (p.sparse_block > 0 || p.q_len > kMaxExtendLen) return hipErrorInvalidValue;
     const unsigned tokens = (unsigned)p.batch * (unsigned)p.q_len;
     hipLaunchKernelGGL(extend_prologue_kernel, dim3(tokens), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && attn_start) e = hipEventRecord(attn_start, stream);
     if (e != hipSuccess) return e;
     const unsigned units = (unsigned)p.batch * kKvHeads * (unsigned)((p.q_len + kExtTile - 1) / kExtTile);
-    hipLaunchKernelGGL(extend_attn_kernel, dim3(units), dim3(256), 0, stream, p);
+    const unsigned grid = (units + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD-aware unit order
+    hipLaunchKernelGGL(extend_attn_kernel, dim3(grid), dim3(256), 0, stream, p);
     return hipGetLastError();
   }
   if (p.sparse_block > 0) {

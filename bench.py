@@ -19,9 +19,12 @@ would (measured within noise of the default).  The layer-
 steps are captured in HIP graphs outside the timed region (one graph of W
 warm-up steps, one of exactly K timed steps) and the timed region is one
 replay of the K-step graph, bracketed by synchronisation and HIP events on the
-replay stream.  The step is a single kernel, so the time per step is also the
-kernel's average duration (the roofline figure); a second, eager pass with the
-library's event hook is reported as well (it includes event overhead).
+replay stream.  For q_len <= 8 the step is a single kernel, so the time per
+step is also the kernel's average duration (the roofline figure); a second,
+eager pass with the library's event hook is reported as well (it includes
+event overhead).  An extend workload (q_len > 8: swa_extend, full_extend) is
+two launches, and its roofline (matrix cores) takes the attention launch's
+duration from that event hook, which then brackets that launch alone.
 
 Prints one JSON line (see the design doc for every field).
 """
@@ -40,8 +43,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
 METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
+
+
 def _kernel_prefix(workload: str) -> str:
-    return "qk_norm" if workload.startswith("qk_norm") else "fused_step"
+    if workload.startswith("qk_norm"):
+        return "qk_norm"
+    return "extend_attn" if workload.endswith("_extend") else "fused_step"
 
 
 def counters_file(workload: str) -> str:
@@ -76,6 +84,28 @@ def attended_keys(w, cache_seqlens) -> int:
         first = max(cs - w.q_len - w.window + 1, 0) if w.window > 0 else 0
         total += max(0, last - first + 1)
     return total
+
+
+def extend_flops(w, cache_seqlens):
+    """Extend / prefill: the attention's algorithmic flops per step, QK^T (fp8
+    operands) and PV (f16 operands) separately: 2*D each per (query row,
+    visible key), query i of request b at p = cache_seqlens[b] - L + i seeing
+    max(0, p-W+1)..p."""
+    import numpy as np
+    rows = 0
+    for cs in cache_seqlens.tolist():
+        p = np.arange(cs - w.q_len, cs, dtype=np.int64)
+        vis = np.minimum(p + 1, w.window) if w.window > 0 else p + 1
+        rows += int(np.maximum(vis, 0).sum())
+    f = 2 * w.head_dim * rows * w.num_q_heads
+    return f, f
+
+
+def mfma_peak(f_fp8: float, f_f16: float) -> float:
+    """The matrix cores' peak for this mix: both products at their own dtype's
+    dense peak, back to back (TFLOP/s)."""
+    t = f_fp8 / MFMA_PEAK_TFLOPS["fp8"] + f_f16 / MFMA_PEAK_TFLOPS["f16"]
+    return (f_fp8 + f_f16) / t
 
 
 def sparse_keys(w, x):
@@ -175,6 +205,42 @@ def cpu_baseline(x, budget_s: float):
     dt = time.perf_counter() - t0
     del np
     return n, dt
+
+
+def cpu_baseline_extend(x, budget_s: float):
+    """Extend / prefill: a whole step of the oracle takes minutes, so it is timed
+    on a sample: the prologue of every token once, then attention + epilogue on
+    random (token, head) rows in chunks until the budget is used.  Returns the
+    estimated seconds per whole step and the sample's description."""
+    import numpy as np
+    import oracle
+    w = x.w
+    cfg = oracle.Config(q_scale=w.q_scale, batch=w.batch, q_len=w.q_len,
+                        num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads,
+                        head_dim=w.head_dim, page_size=w.page_size, window=w.window,
+                        max_pages=x.max_pages, num_pages=x.num_pages, rope_theta=w.rope_theta,
+                        sm_scale=w.sm_scale, kv_scale=w.kv_scale)
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    t0 = time.perf_counter()
+    q = oracle.prologue(cfg, x.qkv, x.positions, x.cache_loc, kc, vc, x.k_scale, x.v_scale)
+    t_pro = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+    n_rows, t_rows = 0, 0.0
+    while t_rows < budget_s:
+        st = rng.integers(0, x.tokens, 64).astype(np.int64)
+        sh = rng.integers(0, w.num_q_heads, 64).astype(np.int32)
+        t1 = time.perf_counter()
+        o = oracle.attention(cfg, q, kc, vc, x.page_table, x.cache_seqlens, x.k_scale, x.v_scale,
+                             st, sh)
+        oracle.epilogue(cfg, o, x.qkv, st, sh)
+        t_rows += time.perf_counter() - t1
+        n_rows += 64
+    total_rows = x.tokens * w.num_q_heads
+    est = t_pro + t_rows / n_rows * total_rows
+    sample = (f"prologue of all {x.tokens} tokens ({t_pro:.1f} s) + attention and epilogue of "
+              f"{n_rows} random (token, head) rows of {total_rows} ({t_rows:.1f} s), scaled to "
+              f"the whole step: {est:.0f} s per step; single-threaded")
+    return est, sample
 
 
 def qk_norm_bytes(w) -> int:
@@ -473,8 +539,27 @@ def main():
 
     # The step is one kernel, so the graph-timed time per step is that kernel's
     # average duration over the timed region (rocprofv3's kernel trace agrees).
+    # An extend step is two launches: its roofline takes the attention kernel's
+    # event-timed duration (the hook brackets that launch alone).
+    extend = w.q_len > 8
     achieved = step_bytes / (us_step * 1e-6) / 1e9
     traffic = load_traffic(w.name)
+    if extend:
+        f8, f16 = extend_flops(w, x0.cache_seqlens)
+        peak = mfma_peak(f8, f16)
+        achieved_tf = (f8 + f16) / (kernel_us * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": round(peak, 1),
+                    "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 4), "traffic": traffic,
+                    "algorithmic_flops": {"qk_fp8": f8, "pv_f16": f16},
+                    "peak_rule": "QK^T at the fp8 dense peak (5.0 PFLOP/s) and PV at the f16 "
+                                 "one (2.5), back to back",
+                    "kernel": "extend_attn_kernel", "kernel_us": round(kernel_us, 3),
+                    "kernel_source": kernel_source_hash()}
+    else:
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes": step_bytes,
+                    "kernel": "fused_step_kernel", "kernel_source": kernel_source_hash()}
     result = {
         "metric": METRIC,
         "value": round(kv_bytes / (us_step * 1e-6) / 1e9, 1),
@@ -504,13 +589,17 @@ def main():
         "step_meta_us": round(meta_us, 3),
         "warm_single_pool": {"us_per_layer_step": round(us_warm, 3),
                              "kv_gbs": round(kv_bytes / (us_warm * 1e-6) / 1e9, 1)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes": step_bytes,
-                     "kernel": "fused_step_kernel", "kernel_source": kernel_source_hash()},
+        "roofline": roofline,
         "timed_wall_s": round(wall_s, 3),
     }
-    if not args.no_cpu_baseline:
+    if extend:
+        result["kernel_us"] = round(kernel_us, 3)  # the attention launch; the step has two
+        result["tokens_per_s"] = round(x0.tokens / (us_step * 1e-6), 1)
+    if not args.no_cpu_baseline and extend:
+        est, sample = cpu_baseline_extend(x0, args.cpu_seconds)
+        result["cpu_baseline"] = {"value": round(kv_bytes / est / 1e9, 6), "unit": "GB/s",
+                                  "cores": 1, "kind": "oracle", "sample": sample}
+    elif not args.no_cpu_baseline:
         n, dt = cpu_baseline(x0, args.cpu_seconds)
         result["cpu_baseline"] = {
             "value": round(n * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,

@@ -234,7 +234,9 @@ int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
 
 /*
  * Measurement hook (not part of the page's interface): while enabled, each
- * step records a HIP event pair on its stream around its kernel.  `enable`
+ * step records a HIP event pair on its stream around its attention kernel
+ * (the step's one launch for q_len <= 8; the second of its two, attention and
+ * epilogue, for q_len > 8).  `enable`
  * != 0 starts a fresh accumulation, 0 stops recording.  Not for use under
  * graph capture.
  */

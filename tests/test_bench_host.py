@@ -83,3 +83,31 @@ def test_sparse_bytes_count_each_heads_listed_keys_once():
             brute += len(keys)
     assert kv == brute * 64 * 2
     assert total > kv
+
+
+@pytest.mark.parametrize("kw", [dict(batch=3, q_len=20, window=0), dict(batch=2, q_len=40, window=7),
+                                dict(batch=2, q_len=33, window=100, seq_lo=2, seq_hi=9)])
+def test_extend_flops_count_every_visible_row_key_pair(kw):
+    """2*D flops per (query row, visible key) for each product, by brute force
+    over the rows."""
+    w = synth.small(**kw)
+    x = synth.make_inputs(w)
+    pairs = 0
+    for cs in x.cache_seqlens.tolist():
+        for i in range(w.q_len):
+            p = cs - w.q_len + i
+            lo = max(0, p - w.window + 1) if w.window > 0 else 0
+            pairs += len(range(lo, p + 1))
+    f8, f16 = bench.extend_flops(w, x.cache_seqlens)
+    assert f8 == f16 == 2 * w.head_dim * w.num_q_heads * pairs
+
+
+def test_mfma_peak_of_the_mix():
+    assert bench.mfma_peak(1.0, 0.0) == pytest.approx(5000.0)
+    assert bench.mfma_peak(0.0, 1.0) == pytest.approx(2500.0)
+    assert bench.mfma_peak(1.0, 1.0) == pytest.approx(2.0 / (1 / 5000.0 + 1 / 2500.0))
+
+
+def test_extend_workloads_use_their_own_counter_files():
+    assert bench.counters_file("swa_extend").endswith("extend_attn_swa_extend_counters.md")
+    assert bench.counters_file("swa_decode").endswith("fused_step_swa_decode_counters.md")
