@@ -20,8 +20,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmi355x_gated_attn.so")
-SOURCES = ["step_kernel.hip", "meta_kernel.hip", "qk_norm_kernel.hip", "api.cpp"]
+SOURCES = ["step_kernel.hip", "extend_kernel.hip", "meta_kernel.hip", "qk_norm_kernel.hip", "api.cpp"]
 HEADERS = [os.path.join(CSRC, "kernels.h"), os.path.join(CSRC, "numerics.h"),
+           os.path.join(CSRC, "step_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "mi355x_gated_attn.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -82,6 +82,9 @@ struct StepParams {
 // attn_start (may be null): for q_len > kMaxQLen, an event recorded between
 // the prologue launch and the attention launch.
 hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_start = nullptr);
+// The q_len > kMaxQLen path of launch_step (two launches: prologue, then
+// attention and epilogue; attn_start as above).
+hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t attn_start);
 
 // Per-head RMSNorm with an output scale (qk_norm_kernel.hip).
 struct QkNormParams {

@@ -43,20 +43,12 @@
 
 #include "kernels.h"
 #include "numerics.h"
+#include "step_device.h"
 
 namespace mi355x_ga {
 namespace {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-
 constexpr int kHeadRows = kQHeads + 2 * kKvHeads;  // 20 head rows per token
-constexpr float kLazyRescale = 8.0f;               // log2 units: P stays <= 2^8
-
-__device__ inline long as_long(uint32_t lo, uint32_t hi) {
-  return (long)(((unsigned long)hi << 32) | (unsigned long)lo);
-}
 
 __device__ inline void store_coherent(float* dst, float a, float b) {
   const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
@@ -84,83 +76,6 @@ __device__ inline uint2 load_coherent_h4(const _Float16* src) {
 
 __device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
 __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
-
-// Cross-lane moves on the VALU (DPP and the gfx950 lane swaps) rather than LDS
-// permutes.  DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
-// (lane ^ 2), row_half_mirror (lane i <-> 7 - i in each 8), row_mirror (lane
-// i <-> 15 - i in each 16-lane row), row_newbcast n (lane n of each row to the
-// whole row).
-constexpr int kDppXor1 = 0xB1;
-constexpr int kDppXor2 = 0x4E;
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppMirror = 0x140;
-constexpr int kDppRowBcast = 0x150;
-
-template <int C>
-__device__ inline int dpp(int x) { return __builtin_amdgcn_mov_dpp(x, C, 0xF, 0xF, false); }
-template <int C>
-__device__ inline float dpp(float x) { return __int_as_float(dpp<C>(__float_as_int(x))); }
-template <int C>
-__device__ inline double dpp(double x) {
-  const long v = __double_as_longlong(x);
-  const int lo = dpp<C>((int)v), hi = dpp<C>((int)(v >> 32));
-  return __longlong_as_double((long)(((unsigned long)(unsigned)hi << 32) | (unsigned)lo));
-}
-
-// Sum over each aligned group of 8 (16) lanes.  Every step adds the same two
-// values in every lane of a pair, so all lanes of a group end with one value.
-__device__ inline double sum8(double s) {
-  s += dpp<kDppXor1>(s);
-  s += dpp<kDppXor2>(s);
-  return s + dpp<kDppHalfMirror>(s);
-}
-__device__ inline float sum16(float s) {
-  s += dpp<kDppXor1>(s);
-  s += dpp<kDppXor2>(s);
-  s += dpp<kDppHalfMirror>(s);
-  return s + dpp<kDppMirror>(s);
-}
-
-// Maximum of three values in one v_max3_f32, without the quieting moves the
-// compiler puts before fmaxf on values it cannot prove canonical (MFMA results).
-__device__ inline float fmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-// Maximum / sum of lane j over the four 16-lane rows: the 16-row swap pairs
-// rows (0,1) and (2,3), the 32-row swap then pairs the halves.
-__device__ inline float rows_max(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ inline float rows_sum(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
-// Page-table entry of logical key `key` (the load only; nothing waits on it).
-__device__ inline int page_entry(const StepParams& p, const int32_t* pt, int key) {
-  const int page = p.page_shift >= 0 ? key >> p.page_shift : key / p.page_size;
-  return pt[min(page, p.max_pages - 1)];
-}
-
-// Flat cache row of logical key `key` from its page-table entry.
-__device__ inline int key_row(const StepParams& p, int entry, int key) {
-  const int off = p.page_shift >= 0 ? key & (p.page_size - 1) : key % p.page_size;
-  const int64_t phys = (entry < 0 || entry >= p.num_pages) ? 0 : entry;  // invalid input: stay in bounds
-  return (int)(phys * p.page_size + off);
-}
-
-// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
-// outstanding global load of the wave, which would stall on the K/V blocks
-// kept in flight across the prologue.
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // K/V operands of one 32-key block for NG KV heads starting at head g0.
 template <int NG>
@@ -212,38 +127,6 @@ __device__ inline KvBlock<NG> load_kv(const StepParams& p, int2 entry, int kk, i
   return d;
 }
 
-// The norm alone (norm_rope8 without its RoPE) and the RoPE alone, for a
-// prologue that computes the sincos table while the norms run.
-__device__ inline void norm8(const float (&x)[8], float scale, float (&y)[8]) {
-#pragma clang fp contract(off)
-  double ss = 0.0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) ss += (double)(x[k] * x[k]);
-  ss = sum8(ss);
-  const float ms = (float)ss / 64.0f;
-  const float inv = rsqrt_exact(ms + 1.0e-5f);
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = x[k] * inv;
-  if (scale != 1.0f) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) y[k] = y[k] * scale;
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k]);
-}
-
-__device__ inline void rope8(const float (*cs)[2], int c8, float (&y)[8]) {
-#pragma clang fp contract(off)
-#pragma unroll
-  for (int pr = 0; pr < 4; ++pr) {
-    const float c = cs[c8 * 4 + pr][0], s = cs[c8 * 4 + pr][1];
-    const float e = y[2 * pr], o = y[2 * pr + 1];
-    const float ec = e * c, os = o * s, oc = o * c, es = e * s;
-    y[2 * pr] = round_bf16(ec - os);
-    y[2 * pr + 1] = round_bf16(oc + es);
-  }
-}
-
 // Norm (+ RoPE) of one 8-column slice of a head row, page order, every fp32 step
 // rounded once (no contraction): fp64-exact sum of squares over the 8 lanes of
 // the row, exact rsqrt, fp32 product (times `scale`, exact when 1), bf16; RoPE
@@ -275,12 +158,6 @@ __device__ inline void norm_rope8(const float (&x)[8], bool rope, const float (*
       y[2 * pr + 1] = round_bf16(oc + es);
     }
   }
-}
-
-__device__ inline uint2 pack_e4m3x8(const float (&y)[8]) {
-  const uint32_t lo = e4m3x2(y[0], y[1]) | (e4m3x2(y[2], y[3]) << 16);
-  const uint32_t hi = e4m3x2(y[4], y[5]) | (e4m3x2(y[6], y[7]) << 16);
-  return make_uint2(lo, hi);
 }
 
 template <int LU, bool HS, int KW, bool SP>
@@ -1118,292 +995,6 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   if (tid == 0 && p.splits > 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// ---------------- Extend / prefill: q_len > kMaxQLen ----------------
-// Two launches.  The prologue normalises, rotates and encodes every new token
-// (q to the workspace, K/V rows to the cache); the launch boundary orders all
-// those stores before any attention read, so the attention kernel reads the
-// new keys from the cache like every other key.  The attention unit is
-// (request, tile of kExtTile new tokens, KV head): its 128 query rows (token,
-// q head of the KV head) walk the tile's key range in 32-key blocks staged
-// once in LDS for the four waves (32 rows each), fp8 QK^T and f16 PV on the
-// matrix cores, online softmax in fp32; no split, so the unit ends with the
-// gated epilogue of its rows.
-constexpr int kExtTile = 16;                 // new tokens per attention unit
-constexpr int kExtRows = kExtTile * kGroup;  // 128 query rows
-constexpr int kExtStride = kHeadDim + 16;    // LDS bytes per staged key row (bank spread)
-constexpr int kXcds = 8;                     // MI355X: accelerator complex dies, one L2 each
-
-// One workgroup per new token: 160 items (16 q, 2 k, 2 v head rows x 8
-// column slices), the sincos table on 32 threads that hold no item.
-__global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
-  constexpr int kItems = (kQHeads + 2 * kKvHeads) * 8;
-  __shared__ float s_cs[kHeadDim / 2][2];
-  const int64_t t = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int item = min(tid, kItems - 1);
-  const int hr = item >> 3, c8 = item & 7;
-  const bool active = tid < kItems;
-  const uint4 xv = *reinterpret_cast<const uint4*>(p.qkv + t * kWidth + hr * kHeadDim + c8 * 8);
-  const int64_t slot = p.cache_loc[t];
-  const int64_t pos = (p.rope ? p.positions : p.cache_loc)[t];
-  const float freq = p.inv_freq[tid & 31];
-  const float ks = p.scaled ? *p.k_scale : 1.0f;
-  const float vs = p.scaled ? *p.v_scale : 1.0f;
-  float y[8];
-  if (active) {
-    float x[8];
-    const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = bf16_value(w[k] & 0xffffu);
-      x[2 * k + 1] = bf16_value(w[k] >> 16);
-    }
-    if (hr < kQHeads + kKvHeads) {
-      norm8(x, hr < kQHeads ? p.q_scale : 1.0f, y);
-    } else {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = p.scaled ? round_bf16(x[k] / vs) : x[k];  // raw value
-    }
-  }
-  if (p.rope && tid >= 256 - 32) {
-    const float ang = (float)pos * freq;
-    double sd, cd;
-    sincos((double)ang, &sd, &cd);
-    s_cs[tid & 31][0] = (float)cd;
-    s_cs[tid & 31][1] = (float)sd;
-  }
-  lds_barrier();
-  if (!active) return;
-  if (hr < kQHeads + kKvHeads) {
-    if (p.rope) rope8(s_cs, c8, y);
-    if (hr >= kQHeads && p.scaled) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k] / ks);
-    }
-  }
-  const uint2 codes = pack_e4m3x8(y);
-  if (hr < kQHeads) {
-    *reinterpret_cast<uint2*>(p.q_out + (t * kQHeads + hr) * kHeadDim + c8 * 8) = codes;
-  } else if (slot >= 0 && slot < p.num_rows) {
-    uint8_t* base = hr < kQHeads + kKvHeads ? p.k_cache + (hr - kQHeads) * kHeadDim
-                                            : p.v_cache + (hr - kQHeads - kKvHeads) * kHeadDim;
-    *reinterpret_cast<uint2*>(base + slot * kRowBytes + c8 * 8) = codes;
-  }
-}
-
-__global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
-  __shared__ __align__(16) uint8_t s_k[2][kKeyBlock][kExtStride];
-  __shared__ __align__(16) uint8_t s_v[2][kKeyBlock][kExtStride];
-  __shared__ __align__(16) float s_o[kExtRows][kHeadDim + 4];
-  const int L = p.q_len;
-  const int n_tiles = (L + kExtTile - 1) / kExtTile;
-  // Units in (request, tile, KV head) order, a contiguous range of them per
-  // XCD (workgroups reach the XCDs round-robin): one L2 then holds a request's
-  // keys for its neighbouring tiles and both KV heads, which share each cache
-  // row.  The grid is padded to a multiple of kXcds; the padding exits.
-  const int n_units = p.batch * n_tiles * kKvHeads;
-  const int per_xcd = (n_units + kXcds - 1) / kXcds;
-  const int unit = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (unit >= n_units) return;
-  const int g = unit % kKvHeads;
-  const int tile = (unit / kKvHeads) % n_tiles, b = unit / (kKvHeads * n_tiles);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int j = lane & 15, q4 = lane >> 4;
-  const int cs = p.cache_seqlens[b];
-  const int i_lo = tile * kExtTile;             // the tile's first token (request-local)
-  const int n_tok = min(kExtTile, L - i_lo);
-  const int p_first = cs - L + i_lo;            // its position
-  const int hi = p_first + n_tok - 1;           // keys lo..hi (the last token's position)
-  const int lo = p.window > 0 ? max(0, p_first - p.window + 1) : 0;
-  const int nblk = hi >= lo ? (hi - lo) / kKeyBlock + 1 : 0;
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  const int64_t tok0 = (int64_t)b * L + i_lo;   // the tile's first token (global)
-  const float ks = p.scaled ? *p.k_scale : 1.0f;
-  const float vs = p.scaled ? *p.v_scale : 1.0f;
-  const float scale = p.sm_scale_log2 * ks;
-
-  // q operands of the wave's two 16-row blocks: row r = 32 wave + 16 rb + j is
-  // token r / 8 of the tile, q head 8 g + r % 8.
-  long qop[2][2];
-  int prow[2], plo[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * wave + 16 * rb + j;
-    const int ti = r >> 3;
-    const bool valid = ti < n_tok;
-    const uint4 qv = *reinterpret_cast<const uint4*>(
-        p.q_out + ((tok0 + min(ti, n_tok - 1)) * kQHeads + kGroup * g + (r & 7)) * kHeadDim + 16 * q4);
-    qop[rb][0] = valid ? as_long(qv.x, qv.y) : 0;
-    qop[rb][1] = valid ? as_long(qv.z, qv.w) : 0;
-    prow[rb] = valid ? p_first + ti : -1;  // an invalid row sees no key
-    plo[rb] = p.window > 0 ? p_first + ti - p.window + 1 : 0;
-  }
-
-  // Staging: thread -> (K or V, key of the block, 16-byte quarter of the row).
-  const int st_v = tid >> 7, st_key = (tid >> 2) & 31, st_c = tid & 3;
-  // Keys past hi reload key hi (masked); with no key at all (hi < lo, hi maybe
-  // negative) key 0, in bounds and unused.
-  auto st_keyof = [&](int blk) { return max(min(lo + blk * kKeyBlock + st_key, hi), 0); };
-  auto st_entry = [&](int blk) { return page_entry(p, pt, st_keyof(blk)); };
-  auto st_load = [&](int entry, int blk) {
-    const int row = key_row(p, entry, st_keyof(blk));
-    const uint8_t* src = (st_v ? p.v_cache : p.k_cache) + (int64_t)row * kRowBytes + g * kHeadDim + st_c * 16;
-    return *reinterpret_cast<const uint4*>(src);
-  };
-
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.0f, 0.0f};
-  v4f acc[2][4];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // Loads run two blocks ahead of the compute (a gather's latency exceeds one
-  // block's compute), page-table entries two blocks ahead of the loads; the
-  // two register sets alternate, so each wait is for the oldest load only.
-  // Primed unconditionally and in the loop's own issue order (data, entry,
-  // data, entry), so the compiler's wait counts at the loop head stay exact.
-  const int last = max(nblk - 1, 0);
-  const int e0 = st_entry(0), e1 = st_entry(min(1, last));
-  uint4 dA = st_load(e0, 0);
-  int eA = st_entry(min(2, last));
-  uint4 dB = st_load(e1, min(1, last));
-  int eB = st_entry(min(3, last));
-  // The q operands are taken here, once (issued first, they are in by now):
-  // a first use inside the loop would make every iteration wait for all loads.
-  asm volatile("" ::"v"(qop[0][0]), "v"(qop[0][1]), "v"(qop[1][0]), "v"(qop[1][1]));
-  auto block_step = [&](const int blk, uint4& data, int& e_next) {
-    const int buf = blk & 1;
-    *reinterpret_cast<uint4*>(st_v ? &s_v[buf][st_key][st_c * 16] : &s_k[buf][st_key][st_c * 16]) = data;
-    lds_barrier();  // block blk staged; block blk-2's reads of this buffer are behind every wave
-    // Unconditional (the last blocks reload block nblk - 1, in bounds and
-    // unused), so the loop has no branch around its loads.
-    data = st_load(e_next, min(blk + 2, last));
-    e_next = st_entry(min(blk + 4, last));
-    const int kbase = lo + blk * kKeyBlock;
-    // Interior: every key <= the first row's position (so <= hi) and inside the
-    // last real row's window.
-    const bool edge = !(kbase + kKeyBlock - 1 <= p_first && (p.window == 0 || kbase >= hi - p.window + 1));
-    // V^T operand of the block (keys 16(r/4) + 4 q4 + r % 4, columns 4j..4j+3).
-    uint32_t vr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      vr[r] = *reinterpret_cast<const uint32_t*>(&s_v[buf][16 * (r >> 2) + 4 * q4 + (r & 3)][4 * j]);
-    v8h va[4];
-#pragma unroll
-    for (int rp = 0; rp < 4; ++rp) {
-      const uint32_t l0 = __builtin_amdgcn_perm(vr[2 * rp + 1], vr[2 * rp], 0x05010400u);
-      const uint32_t h0 = __builtin_amdgcn_perm(vr[2 * rp + 1], vr[2 * rp], 0x07030602u);
-      const v2h c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(l0, 1.0f, false);
-      const v2h c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(l0, 1.0f, true);
-      const v2h c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h0, 1.0f, false);
-      const v2h c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h0, 1.0f, true);
-      va[0][2 * rp] = c0[0];
-      va[0][2 * rp + 1] = c0[1];
-      va[1][2 * rp] = c1[0];
-      va[1][2 * rp + 1] = c1[1];
-      va[2][2 * rp] = c2[0];
-      va[2][2 * rp + 1] = c2[1];
-      va[3][2 * rp] = c3[0];
-      va[3][2 * rp + 1] = c3[1];
-    }
-    uint4 kv[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) kv[t] = *reinterpret_cast<const uint4*>(&s_k[buf][16 * t + j][16 * q4]);
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      // Raw q.k: lane (q4, j) gets keys 16t + 4q4 + i (slot 4t + i) of row j.
-      float z[8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        v4f c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(kv[t].x, kv[t].y), qop[rb][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(kv[t].z, kv[t].w), qop[rb][1], c, 0, 0, 0);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) z[t * 4 + ii] = c[ii];
-      }
-      // Causal and window mask of the row, on edge blocks only (an interior
-      // block is visible to every real row; padding rows are never stored).
-      if (edge) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
-          z[k] = (key <= prow[rb] && key >= plo[rb]) ? z[k] : -INFINITY;
-        }
-      }
-      float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], -INFINITY));
-      const float lmx = m * scale;
-      if (__any(lmx > mrow[rb] + kLazyRescale)) {
-        const float mx = rows_max(lmx);
-        const float mold = mrow[rb];
-        const float mnew = mx > mold + kLazyRescale ? mx : mold;
-        const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
-        lrow[rb] *= alpha;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[rb][c] *= alpha;
-        mrow[rb] = mnew;
-      }
-      const float nmuse = mrow[rb] == -INFINITY ? 0.0f : -mrow[rb];
-      v8h pv;
-      float psum = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k], scale, nmuse));
-        psum += e;
-        pv[k] = (_Float16)e;
-      }
-      lrow[rb] += psum;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[c], pv, acc[rb][c], 0, 0, 0);
-    }
-  };
-  // Whole pairs in the loop (its back edge always follows the second half, so
-  // the loads are always in the same order there), an odd last block after it.
-  int blk = 0;
-  for (; blk + 1 < nblk; blk += 2) {
-    block_step(blk, dA, eA);
-    block_step(blk + 1, dB, eB);
-  }
-  if (blk < nblk) block_step(blk, dA, eA);
-
-  // o / l of every row to LDS (column 16 q4 + 4 ii + c of row 32 wave + 16 rb + j).
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float l = rows_sum(lrow[rb]);
-    const float inv = l > 0.0f ? vs * __builtin_amdgcn_rcpf(l) : 0.0f;
-    const int r = 32 * wave + 16 * rb + j;
-#pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      *reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]) =
-          make_float4(acc[rb][0][ii] * inv, acc[rb][1][ii] * inv, acc[rb][2][ii] * inv, acc[rb][3][ii] * inv);
-  }
-  lds_barrier();
-  // Gated epilogue: 16 threads per row, 4 columns each.
-  const int c4 = (tid & 15) * 4;
-#pragma unroll
-  for (int pass = 0; pass < kExtRows / 16; ++pass) {
-    const int r = pass * 16 + (tid >> 4);
-    const int ti = r >> 3, h = kGroup * g + (r & 7);
-    const bool valid = ti < n_tok;
-    const int64_t tok = tok0 + min(ti, n_tok - 1);
-    const uint2 graw = *reinterpret_cast<const uint2*>(p.qkv + tok * kWidth + kGateOffset + h * kHeadDim + c4);
-    const float4 o = *reinterpret_cast<const float4*>(&s_o[r][c4]);
-    float y[4] = {round_bf16(o.x), round_bf16(o.y), round_bf16(o.z), round_bf16(o.w)};
-    float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
-    ss = sum16(ss);
-    const float rr = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + 1.0e-5f);
-    const float gate[4] = {bf16_value(graw.x & 0xffffu), bf16_value(graw.x >> 16),
-                           bf16_value(graw.y & 0xffffu), bf16_value(graw.y >> 16)};
-    uint32_t ob[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * rr * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[c])));
-    if (valid)
-      *reinterpret_cast<uint2*>(p.out + tok * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
-          make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
-  }
-}
-
 template <int LU, bool HS, int KW, bool SP = false>
 hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
@@ -1432,18 +1023,7 @@ __global__ void zero_counters_kernel(int32_t* c, int n) {
 
 hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_start) {
   if (p.batch == 0) return hipSuccess;
-  if (p.q_len > kMaxQLen) {  // extend / prefill: prologue, then attention + epilogue
-    if (p.sparse_block > 0 || p.q_len > kMaxExtendLen) return hipErrorInvalidValue;
-    const unsigned tokens = (unsigned)p.batch * (unsigned)p.q_len;
-    hipLaunchKernelGGL(extend_prologue_kernel, dim3(tokens), dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e == hipSuccess && attn_start) e = hipEventRecord(attn_start, stream);
-    if (e != hipSuccess) return e;
-    const unsigned units = (unsigned)p.batch * kKvHeads * (unsigned)((p.q_len + kExtTile - 1) / kExtTile);
-    const unsigned grid = (units + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD-aware unit order
-    hipLaunchKernelGGL(extend_attn_kernel, dim3(grid), dim3(256), 0, stream, p);
-    return hipGetLastError();
-  }
+  if (p.q_len > kMaxQLen) return launch_extend(p, stream, attn_start);  // extend / prefill
   if (p.sparse_block > 0) {
     // Page-list-driven decode: q_len 1, one KV head per wave (each head has its
     // own list), blocks of a multiple of 32 keys, at most kMaxSparseTopk slots.

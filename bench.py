@@ -57,14 +57,22 @@ def counters_file(workload: str) -> str:
     return os.path.join(ROOT, "profiles", f"{_kernel_prefix(workload)}_{workload}_counters.md")
 
 
-def _sources(kernel_file: str):
+def _sources(*kernel_files: str):
     return [os.path.join(ROOT, "attention_decode_qk_amd", "csrc", f)
-            for f in (kernel_file, "kernels.h", "numerics.h")] + \
+            for f in (*kernel_files, "kernels.h", "numerics.h")] + \
            [os.path.join(ROOT, "attention_decode_qk_amd", "build.py")]  # compiler flags
 
 
-KERNEL_SOURCES = _sources("step_kernel.hip")
+KERNEL_SOURCES = _sources("step_kernel.hip", "step_device.h")
+EXTEND_SOURCES = _sources("extend_kernel.hip", "step_device.h")
 QK_NORM_SOURCES = _sources("qk_norm_kernel.hip")
+
+
+def workload_sources(workload: str):
+    """The sources that build the workload's dominant kernel."""
+    if workload.startswith("qk_norm"):
+        return QK_NORM_SOURCES
+    return EXTEND_SOURCES if workload.endswith("_extend") else KERNEL_SOURCES
 
 
 def kernel_source_hash(files=None) -> str:
@@ -171,8 +179,7 @@ def load_traffic(workload: str):
     if not m:
         return None
     d = json.loads(m.group(1))
-    files = QK_NORM_SOURCES if workload.startswith("qk_norm") else KERNEL_SOURCES
-    if d.get("kernel_source_sha256") != kernel_source_hash(files):
+    if d.get("kernel_source_sha256") != kernel_source_hash(workload_sources(workload)):
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -554,7 +561,7 @@ def main():
                     "peak_rule": "QK^T at the fp8 dense peak (5.0 PFLOP/s) and PV at the f16 "
                                  "one (2.5), back to back",
                     "kernel": "extend_attn_kernel", "kernel_us": round(kernel_us, 3),
-                    "kernel_source": kernel_source_hash()}
+                    "kernel_source": kernel_source_hash(EXTEND_SOURCES)}
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
