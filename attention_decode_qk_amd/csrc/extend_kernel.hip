@@ -18,16 +18,33 @@ namespace {
 // Two launches.  The prologue normalises, rotates and encodes every new token
 // (q to the workspace, K/V rows to the cache); the launch boundary orders all
 // those stores before any attention read, so the attention kernel reads the
-// new keys from the cache like every other key.  The attention unit is
-// (request, tile of kExtTile new tokens, KV head): its 128 query rows (token,
-// q head of the KV head) walk the tile's key range in 32-key blocks staged
-// once in LDS for the four waves (32 rows each), fp8 QK^T and f16 PV on the
-// matrix cores, online softmax in fp32; no split, so the unit ends with the
-// gated epilogue of its rows.
-constexpr int kExtTile = 16;                 // new tokens per attention unit
-constexpr int kExtRows = kExtTile * kGroup;  // 128 query rows
-constexpr int kExtStride = kHeadDim + 16;    // LDS bytes per staged key row (bank spread)
-constexpr int kXcds = 8;                     // MI355X: accelerator complex dies, one L2 each
+// new keys from the cache like every other key.
+//
+// Attention unit = (request, tile of kExtTile new tokens, KV head): 128 query
+// rows (token, q head of the KV head), one workgroup of eight waves in two
+// groups of four.  Each wave holds 32 rows (two 16-row MFMA blocks) and the
+// two groups split the tile's key range: every barrier stages 64 keys (two
+// 32-key blocks) in LDS, group 0 takes the first block and group 1 the
+// second, and at the end group 0 merges group 1's (max, sum, output) through
+// LDS.  Staging is one 16-byte load per thread: waves 0-3 stage K rows as they
+// are (the fp8 QK^T operand), waves 4-7 widen V to f16 exactly and store it
+// transposed ([dim][key]), so the PV operand is two plain LDS loads per MFMA.
+// fp8 QK^T and f16 PV on the matrix cores, base-2 online softmax in fp32 with
+// a lazily moved running max; the unit ends with the gated epilogue of its rows.
+constexpr int kExtTile = 16;                    // new tokens per attention unit
+constexpr int kExtRows = kExtTile * kGroup;     // 128 query rows
+constexpr int kExtWaves = 8;                    // two key groups of four waves
+constexpr int kExtStageKeys = 2 * kKeyBlock;    // keys staged per barrier (one block per group)
+constexpr int kExtKStride = kHeadDim + 16;      // LDS bytes per staged K row (fp8; bank spread)
+constexpr int kExtVStride = 2 * kKeyBlock + 8;  // LDS bytes per staged V^T row (f16 x 32 keys + pad)
+// One block's V^T rows (+ the row-group skew), sized so the second block starts
+// 16 banks after the first (4672 B = 1168 dwords = 16 mod 32).
+constexpr int kExtVBlock = kHeadDim * kExtVStride + 64;
+constexpr int kExtKBytes = 2 * kExtStageKeys * kExtKStride;           // double-buffered K
+constexpr int kExtVBytes = 2 * 2 * kExtVBlock;                        // double-buffered V^T, 2 blocks
+constexpr int kExtOBytes = kExtRows * (kHeadDim + 4) * 4 + kExtRows * 8;  // merge / epilogue rows + (m, l)
+constexpr int kExtSmem = (kExtKBytes + kExtVBytes) > kExtOBytes ? (kExtKBytes + kExtVBytes) : kExtOBytes;
+constexpr int kXcds = 8;                        // MI355X: accelerator complex dies, one L2 each
 
 // One workgroup per new token: 160 items (16 q, 2 k, 2 v head rows x 8
 // column slices), the sincos table on 32 threads that hold no item.
@@ -87,10 +104,14 @@ __global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
   }
 }
 
-__global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
-  __shared__ __align__(16) uint8_t s_k[2][kKeyBlock][kExtStride];
-  __shared__ __align__(16) uint8_t s_v[2][kKeyBlock][kExtStride];
-  __shared__ __align__(16) float s_o[kExtRows][kHeadDim + 4];
+__global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepParams p) {
+  // Staging buffers during the key loop; merge rows and (m, l) after it.
+  __shared__ __align__(16) uint8_t smem[kExtSmem];
+  auto s_k = reinterpret_cast<uint8_t(*)[kExtStageKeys][kExtKStride]>(smem);                  // [2][64][80]
+  auto s_vt = reinterpret_cast<uint8_t(*)[2][kExtVBlock]>(smem + kExtKBytes);                 // [2][2][4736]
+  auto s_o = reinterpret_cast<float(*)[kHeadDim + 4]>(smem);                                  // [128][68]
+  auto s_ml = reinterpret_cast<float2*>(smem + kExtRows * (kHeadDim + 4) * 4);                // [128]
+
   const int L = p.q_len;
   const int n_tiles = (L + kExtTile - 1) / kExtTile;
   // Units in (request, tile, KV head) order, a contiguous range of them per
@@ -103,7 +124,9 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
   if (unit >= n_units) return;
   const int g = unit % kKvHeads;
   const int tile = (unit / kKvHeads) % n_tiles, b = unit / (kKvHeads * n_tiles);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
+  const int kg = wave >> 2, wq = wave & 3;  // key group; the wave's rows within the tile
   const int j = lane & 15, q4 = lane >> 4;
   const int cs = p.cache_seqlens[b];
   const int i_lo = tile * kExtTile;             // the tile's first token (request-local)
@@ -112,19 +135,20 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
   const int hi = p_first + n_tok - 1;           // keys lo..hi (the last token's position)
   const int lo = p.window > 0 ? max(0, p_first - p.window + 1) : 0;
   const int nblk = hi >= lo ? (hi - lo) / kKeyBlock + 1 : 0;
+  const int n_stage = (nblk + 1) / 2;
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
   const int64_t tok0 = (int64_t)b * L + i_lo;   // the tile's first token (global)
   const float ks = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
   const float scale = p.sm_scale_log2 * ks;
 
-  // q operands of the wave's two 16-row blocks: row r = 32 wave + 16 rb + j is
-  // token r / 8 of the tile, q head 8 g + r % 8.
+  // q operands of the wave's two 16-row blocks: row r = 32 wq + 16 rb + j is
+  // token r / 8 of the tile, q head 8 g + r % 8 (both key groups hold the same rows).
   long qop[2][2];
   int prow[2], plo[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * wave + 16 * rb + j;
+    const int r = 32 * wq + 16 * rb + j;
     const int ti = r >> 3;
     const bool valid = ti < n_tok;
     const uint4 qv = *reinterpret_cast<const uint4*>(
@@ -135,16 +159,40 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
     plo[rb] = p.window > 0 ? p_first + ti - p.window + 1 : 0;
   }
 
-  // Staging: thread -> (K or V, key of the block, 16-byte quarter of the row).
-  const int st_v = tid >> 7, st_key = (tid >> 2) & 31, st_c = tid & 3;
+  // Staging: thread -> (K for waves 0-3 / V for waves 4-7, key of the 64-key
+  // stage, 16-byte quarter of the head's row).  A K wave's lanes take 16 keys'
+  // rows, four lanes per key; V wave 4 + c takes quarter c of all 64 keys, one
+  // key per lane, so each transposed store writes one dim row of both blocks.
+  const int st_v = wave >> 2;
+  const int st_key = st_v ? lane : (tid >> 2) & (kExtStageKeys - 1);
+  const int st_c = st_v ? wave & 3 : tid & 3;
+  // V^T row r of a block (72-byte rows, 8 bytes of skew per 16-row group): the
+  // 16 rows 4 j + c an MFMA operand load reads (j = 0..15) then cover all 32
+  // banks with their 8-byte pieces.
+  auto vt_row = [](int r) { return r * kExtVStride + ((r >> 4) & 3) * 8; };
   // Keys past hi reload key hi (masked); with no key at all (hi < lo, hi maybe
   // negative) key 0, in bounds and unused.
-  auto st_keyof = [&](int blk) { return max(min(lo + blk * kKeyBlock + st_key, hi), 0); };
-  auto st_entry = [&](int blk) { return page_entry(p, pt, st_keyof(blk)); };
-  auto st_load = [&](int entry, int blk) {
-    const int row = key_row(p, entry, st_keyof(blk));
+  auto st_keyof = [&](int s) { return max(min(lo + s * kExtStageKeys + st_key, hi), 0); };
+  auto st_entry = [&](int s) { return page_entry(p, pt, st_keyof(s)); };
+  auto st_load = [&](int entry, int s) {
+    const int row = key_row(p, entry, st_keyof(s));
     const uint8_t* src = (st_v ? p.v_cache : p.k_cache) + (int64_t)row * kRowBytes + g * kHeadDim + st_c * 16;
     return *reinterpret_cast<const uint4*>(src);
+  };
+  // V: 16 e4m3 values (dims 16 c .. 16 c + 15 of one key) widened to f16
+  // exactly and stored down the key's column of the transposed block.
+  auto stage_v = [&](const int buf, const uint4 d) {
+    uint8_t* col = &s_vt[buf][st_key >> 5][vt_row(16 * st_c) + 2 * (st_key & (kKeyBlock - 1))];
+    const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const v2h lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, false);
+      const v2h hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, true);
+      *reinterpret_cast<_Float16*>(col + (4 * k + 0) * kExtVStride) = lo2[0];
+      *reinterpret_cast<_Float16*>(col + (4 * k + 1) * kExtVStride) = lo2[1];
+      *reinterpret_cast<_Float16*>(col + (4 * k + 2) * kExtVStride) = hi2[0];
+      *reinterpret_cast<_Float16*>(col + (4 * k + 3) * kExtVStride) = hi2[1];
+    }
   };
 
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.0f, 0.0f};
@@ -154,58 +202,26 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Loads run two blocks ahead of the compute (a gather's latency exceeds one
-  // block's compute), page-table entries two blocks ahead of the loads; the
-  // two register sets alternate, so each wait is for the oldest load only.
-  // Primed unconditionally and in the loop's own issue order (data, entry,
-  // data, entry), so the compiler's wait counts at the loop head stay exact.
-  const int last = max(nblk - 1, 0);
-  const int e0 = st_entry(0), e1 = st_entry(min(1, last));
-  uint4 dA = st_load(e0, 0);
-  int eA = st_entry(min(2, last));
-  uint4 dB = st_load(e1, min(1, last));
-  int eB = st_entry(min(3, last));
-  // The q operands are taken here, once (issued first, they are in by now):
-  // a first use inside the loop would make every iteration wait for all loads.
-  asm volatile("" ::"v"(qop[0][0]), "v"(qop[0][1]), "v"(qop[1][0]), "v"(qop[1][1]));
-  auto block_step = [&](const int blk, uint4& data, int& e_next) {
-    const int buf = blk & 1;
-    *reinterpret_cast<uint4*>(st_v ? &s_v[buf][st_key][st_c * 16] : &s_k[buf][st_key][st_c * 16]) = data;
-    lds_barrier();  // block blk staged; block blk-2's reads of this buffer are behind every wave
-    // Unconditional (the last blocks reload block nblk - 1, in bounds and
-    // unused), so the loop has no branch around its loads.
-    data = st_load(e_next, min(blk + 2, last));
-    e_next = st_entry(min(blk + 4, last));
+  // One 32-key block of the wave's key group from stage buffer buf.
+  auto compute = [&](const int buf, const int blk) {
     const int kbase = lo + blk * kKeyBlock;
     // Interior: every key <= the first row's position (so <= hi) and inside the
     // last real row's window.
     const bool edge = !(kbase + kKeyBlock - 1 <= p_first && (p.window == 0 || kbase >= hi - p.window + 1));
-    // V^T operand of the block (keys 16(r/4) + 4 q4 + r % 4, columns 4j..4j+3).
-    uint32_t vr[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r)
-      vr[r] = *reinterpret_cast<const uint32_t*>(&s_v[buf][16 * (r >> 2) + 4 * q4 + (r & 3)][4 * j]);
+    // V^T operand: column c of the lane's four is dim 4 j + c; slots 0-3 are
+    // keys 4 q4 .. 4 q4 + 3 and slots 4-7 keys 16 + 4 q4 .., as in P below.
     v8h va[4];
 #pragma unroll
-    for (int rp = 0; rp < 4; ++rp) {
-      const uint32_t l0 = __builtin_amdgcn_perm(vr[2 * rp + 1], vr[2 * rp], 0x05010400u);
-      const uint32_t h0 = __builtin_amdgcn_perm(vr[2 * rp + 1], vr[2 * rp], 0x07030602u);
-      const v2h c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(l0, 1.0f, false);
-      const v2h c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(l0, 1.0f, true);
-      const v2h c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h0, 1.0f, false);
-      const v2h c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(h0, 1.0f, true);
-      va[0][2 * rp] = c0[0];
-      va[0][2 * rp + 1] = c0[1];
-      va[1][2 * rp] = c1[0];
-      va[1][2 * rp + 1] = c1[1];
-      va[2][2 * rp] = c2[0];
-      va[2][2 * rp + 1] = c2[1];
-      va[3][2 * rp] = c3[0];
-      va[3][2 * rp + 1] = c3[1];
+    for (int c = 0; c < 4; ++c) {
+      const uint8_t* row = &s_vt[buf][kg][vt_row(4 * j + c)];
+      const uint2 a0 = *reinterpret_cast<const uint2*>(row + 8 * q4);
+      const uint2 a1 = *reinterpret_cast<const uint2*>(row + 2 * 16 + 8 * q4);
+      va[c] = __builtin_bit_cast(v8h, make_uint4(a0.x, a0.y, a1.x, a1.y));
     }
     uint4 kv[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) kv[t] = *reinterpret_cast<const uint4*>(&s_k[buf][16 * t + j][16 * q4]);
+    for (int t = 0; t < 2; ++t)
+      kv[t] = *reinterpret_cast<const uint4*>(&s_k[buf][kKeyBlock * kg + 16 * t + j][16 * q4]);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       // Raw q.k: lane (q4, j) gets keys 16t + 4q4 + i (slot 4t + i) of row j.
@@ -254,32 +270,87 @@ __global__ __launch_bounds__(256) void extend_attn_kernel(StepParams p) {
         acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[c], pv, acc[rb][c], 0, 0, 0);
     }
   };
-  // Whole pairs in the loop (its back edge always follows the second half, so
-  // the loads are always in the same order there), an odd last block after it.
-  int blk = 0;
-  for (; blk + 1 < nblk; blk += 2) {
-    block_step(blk, dA, eA);
-    block_step(blk + 1, dB, eB);
-  }
-  if (blk < nblk) block_step(blk, dA, eA);
 
-  // o / l of every row to LDS (column 16 q4 + 4 ii + c of row 32 wave + 16 rb + j).
+  // Loads run two stages ahead of the compute (a gather's latency exceeds one
+  // stage's compute), page-table entries two stages ahead of the loads; the
+  // two register sets alternate, so each wait is for the oldest load only.
+  // Primed unconditionally and in the loop's own issue order (data, entry,
+  // data, entry), so the compiler's wait counts at the loop head stay exact.
+  const int last = max(n_stage - 1, 0);
+  const int e0 = st_entry(0), e1 = st_entry(min(1, last));
+  uint4 dA = st_load(e0, 0);
+  int eA = st_entry(min(2, last));
+  uint4 dB = st_load(e1, min(1, last));
+  int eB = st_entry(min(3, last));
+  // The q operands are taken here, once (issued first, they are in by now):
+  // a first use inside the loop would make every iteration wait for all loads.
+  asm volatile("" ::"v"(qop[0][0]), "v"(qop[0][1]), "v"(qop[1][0]), "v"(qop[1][1]));
+
+  auto stage_step = [&](const int s, uint4& data, int& e_next) {
+    const int buf = s & 1;
+    if (st_v)
+      stage_v(buf, data);
+    else
+      *reinterpret_cast<uint4*>(&s_k[buf][st_key][st_c * 16]) = data;
+    lds_barrier();  // stage s in LDS; stage s-2's reads of this buffer are behind every wave
+    // Unconditional (the last stages reload stage n_stage - 1, in bounds and
+    // unused), so the loop has no branch around its loads.
+    data = st_load(e_next, min(s + 2, last));
+    e_next = st_entry(min(s + 4, last));
+    if (2 * s + kg < nblk) compute(buf, 2 * s + kg);
+  };
+  // Whole stage pairs in the loop (its back edge always follows the second
+  // half, so the loads are always in the same order there), an odd last stage
+  // after it.
+  int s = 0;
+  for (; s + 1 < n_stage; s += 2) {
+    stage_step(s, dA, eA);
+    stage_step(s + 1, dB, eB);
+  }
+  if (s < n_stage) stage_step(s, dA, eA);
+
+  // Merge: group 1 leaves its rows' raw accumulators and (m, l) in LDS (the
+  // staging buffers are free once every wave is past the loop); group 0 adds
+  // them at a common reference max and leaves o / l, times the V descale.
+  const float l_own[2] = {rows_sum(lrow[0]), rows_sum(lrow[1])};
+  lds_barrier();
+  if (kg == 1) {
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const float l = rows_sum(lrow[rb]);
-    const float inv = l > 0.0f ? vs * __builtin_amdgcn_rcpf(l) : 0.0f;
-    const int r = 32 * wave + 16 * rb + j;
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = 32 * wq + 16 * rb + j;
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii)
-      *reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]) =
-          make_float4(acc[rb][0][ii] * inv, acc[rb][1][ii] * inv, acc[rb][2][ii] * inv, acc[rb][3][ii] * inv);
+      for (int ii = 0; ii < 4; ++ii)
+        *reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]) =
+            make_float4(acc[rb][0][ii], acc[rb][1][ii], acc[rb][2][ii], acc[rb][3][ii]);
+      if (q4 == 0) s_ml[r] = make_float2(mrow[rb], l_own[rb]);
+    }
   }
   lds_barrier();
-  // Gated epilogue: 16 threads per row, 4 columns each.
+  if (kg == 0) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = 32 * wq + 16 * rb + j;
+      const float2 ml = s_ml[r];
+      const float mt = fmaxf(mrow[rb], ml.x);
+      const float mref = mt == -INFINITY ? 0.0f : mt;
+      const float a0 = __builtin_amdgcn_exp2f(mrow[rb] - mref), a1 = __builtin_amdgcn_exp2f(ml.x - mref);
+      const float l = l_own[rb] * a0 + ml.y * a1;
+      const float inv = l > 0.0f ? vs * __builtin_amdgcn_rcpf(l) : 0.0f;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        float4* o = reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]);
+        const float4 u = *o;
+        *o = make_float4((acc[rb][0][ii] * a0 + u.x * a1) * inv, (acc[rb][1][ii] * a0 + u.y * a1) * inv,
+                         (acc[rb][2][ii] * a0 + u.z * a1) * inv, (acc[rb][3][ii] * a0 + u.w * a1) * inv);
+      }
+    }
+  }
+  lds_barrier();
+  // Gated epilogue: 16 threads per row, 4 columns each, 32 rows per pass.
   const int c4 = (tid & 15) * 4;
 #pragma unroll
-  for (int pass = 0; pass < kExtRows / 16; ++pass) {
-    const int r = pass * 16 + (tid >> 4);
+  for (int pass = 0; pass < kExtRows / (4 * kExtWaves); ++pass) {
+    const int r = pass * (4 * kExtWaves) + (tid >> 4);
     const int ti = r >> 3, h = kGroup * g + (r & 7);
     const bool valid = ti < n_tok;
     const int64_t tok = tok0 + min(ti, n_tok - 1);
@@ -312,7 +383,7 @@ hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t att
   if (e != hipSuccess) return e;
   const unsigned units = (unsigned)p.batch * kKvHeads * (unsigned)((p.q_len + kExtTile - 1) / kExtTile);
   const unsigned grid = (units + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD-aware unit order
-  hipLaunchKernelGGL(extend_attn_kernel, dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(extend_attn_kernel, dim3(grid), dim3(64 * kExtWaves), 0, stream, p);
   return hipGetLastError();
 }
 
