@@ -46,61 +46,95 @@ constexpr int kExtOBytes = kExtRows * (kHeadDim + 4) * 4 + kExtRows * 8;  // mer
 constexpr int kExtSmem = (kExtKBytes + kExtVBytes) > kExtOBytes ? (kExtKBytes + kExtVBytes) : kExtOBytes;
 constexpr int kXcds = 8;                        // MI355X: accelerator complex dies, one L2 each
 
-// One workgroup per new token: 160 items (16 q, 2 k, 2 v head rows x 8
-// column slices), the sincos table on 32 threads that hold no item.
+// Prologue: kExtPrologueTokens new tokens per workgroup, their 160 items each
+// ((16 q, 2 k, 2 v head rows) x 8 column slices, eight lanes per head row) dealt
+// over the 256 threads, three per thread at most; every item's load is issued
+// first.  The threads holding two items compute the tokens' RoPE sincos table
+// while the others finish their third norm; RoPE, the e4m3 codes and the
+// stores follow the barrier.
+constexpr int kExtPrologueTokens = 4;
+constexpr int kExtItems = (kQHeads + 2 * kKvHeads) * 8;                              // per token
+constexpr int kExtPrologueIters = (kExtPrologueTokens * kExtItems + 255) / 256;      // 3
+constexpr int kExtCsBase = 256 - 32 * kExtPrologueTokens;                            // sincos threads
+static_assert(kExtPrologueTokens * kExtItems - 256 * (kExtPrologueIters - 1) <= kExtCsBase,
+              "the sincos threads hold no third item");
+
 __global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
-  constexpr int kItems = (kQHeads + 2 * kKvHeads) * 8;
-  __shared__ float s_cs[kHeadDim / 2][2];
-  const int64_t t = blockIdx.x;
+  __shared__ float s_cs[kExtPrologueTokens][kHeadDim / 2][2];
+  const int64_t T = (int64_t)p.batch * p.q_len;
+  const int64_t t0 = (int64_t)blockIdx.x * kExtPrologueTokens;
   const int tid = threadIdx.x;
-  const int item = min(tid, kItems - 1);
-  const int hr = item >> 3, c8 = item & 7;
-  const bool active = tid < kItems;
-  const uint4 xv = *reinterpret_cast<const uint4*>(p.qkv + t * kWidth + hr * kHeadDim + c8 * 8);
-  const int64_t slot = p.cache_loc[t];
-  const int64_t pos = (p.rope ? p.positions : p.cache_loc)[t];
+  uint4 xv[kExtPrologueIters];
+#pragma unroll
+  for (int it = 0; it < kExtPrologueIters; ++it) {
+    const int item = min(tid + 256 * it, kExtPrologueTokens * kExtItems - 1);
+    const int64_t tk = min(t0 + item / kExtItems, T - 1);
+    const int rem = item % kExtItems;
+    xv[it] = *reinterpret_cast<const uint4*>(p.qkv + tk * kWidth + (rem >> 3) * kHeadDim + (rem & 7) * 8);
+  }
+  // Without RoPE, positions may be absent: a cache row index is read instead
+  // (same type, always present) and ignored.
+  const int cs_tok = max(tid - kExtCsBase, 0) >> 5;
+  const int64_t cs_pos = (p.rope ? p.positions : p.cache_loc)[min(t0 + cs_tok, T - 1)];
   const float freq = p.inv_freq[tid & 31];
   const float ks = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
-  float y[8];
-  if (active) {
-    float x[8];
-    const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+
+  float y[kExtPrologueIters][8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      x[2 * k] = bf16_value(w[k] & 0xffffu);
-      x[2 * k + 1] = bf16_value(w[k] >> 16);
-    }
-    if (hr < kQHeads + kKvHeads) {
-      norm8(x, hr < kQHeads ? p.q_scale : 1.0f, y);
-    } else {
+  for (int it = 0; it < kExtPrologueIters; ++it) {
+    const int item = tid + 256 * it;
+    const int hr = (item % kExtItems) >> 3;
+    // Whole 8-lane groups are active or not together (a group is one head row).
+    if (item < kExtPrologueTokens * kExtItems && t0 + item / kExtItems < T) {
+      float x[8];
+      const uint32_t w[4] = {xv[it].x, xv[it].y, xv[it].z, xv[it].w};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = p.scaled ? round_bf16(x[k] / vs) : x[k];  // raw value
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = bf16_value(w[k] & 0xffffu);
+        x[2 * k + 1] = bf16_value(w[k] >> 16);
+      }
+      if (hr < kQHeads + kKvHeads) {
+        norm8(x, hr < kQHeads ? p.q_scale : 1.0f, y[it]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[it][k] = p.scaled ? round_bf16(x[k] / vs) : x[k];  // raw value
+      }
     }
   }
-  if (p.rope && tid >= 256 - 32) {
-    const float ang = (float)pos * freq;
+  if (p.rope && tid >= kExtCsBase) {
+    const float ang = (float)cs_pos * freq;
     double sd, cd;
     sincos((double)ang, &sd, &cd);
-    s_cs[tid & 31][0] = (float)cd;
-    s_cs[tid & 31][1] = (float)sd;
+    s_cs[cs_tok][tid & 31][0] = (float)cd;
+    s_cs[cs_tok][tid & 31][1] = (float)sd;
   }
   lds_barrier();
-  if (!active) return;
-  if (hr < kQHeads + kKvHeads) {
-    if (p.rope) rope8(s_cs, c8, y);
-    if (hr >= kQHeads && p.scaled) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = round_bf16(y[k] / ks);
+  for (int it = 0; it < kExtPrologueIters; ++it) {
+    const int item = tid + 256 * it;
+    const int tl = item / kExtItems, rem = item % kExtItems;
+    const int hr = rem >> 3, c8 = rem & 7;
+    const int64_t t = t0 + tl;
+    if (item >= kExtPrologueTokens * kExtItems || t >= T) continue;
+    if (hr < kQHeads + kKvHeads) {
+      if (p.rope) rope8(s_cs[tl], c8, y[it]);
+      if (hr >= kQHeads && p.scaled) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) y[it][k] = round_bf16(y[it][k] / ks);
+      }
     }
-  }
-  const uint2 codes = pack_e4m3x8(y);
-  if (hr < kQHeads) {
-    *reinterpret_cast<uint2*>(p.q_out + (t * kQHeads + hr) * kHeadDim + c8 * 8) = codes;
-  } else if (slot >= 0 && slot < p.num_rows) {
-    uint8_t* base = hr < kQHeads + kKvHeads ? p.k_cache + (hr - kQHeads) * kHeadDim
-                                            : p.v_cache + (hr - kQHeads - kKvHeads) * kHeadDim;
-    *reinterpret_cast<uint2*>(base + slot * kRowBytes + c8 * 8) = codes;
+    const uint2 codes = pack_e4m3x8(y[it]);
+    if (hr < kQHeads) {
+      *reinterpret_cast<uint2*>(p.q_out + (t * kQHeads + hr) * kHeadDim + c8 * 8) = codes;
+    } else {
+      const int64_t slot = p.cache_loc[t];
+      if (slot >= 0 && slot < p.num_rows) {
+        uint8_t* base = hr < kQHeads + kKvHeads ? p.k_cache + (hr - kQHeads) * kHeadDim
+                                                : p.v_cache + (hr - kQHeads - kKvHeads) * kHeadDim;
+        *reinterpret_cast<uint2*>(base + slot * kRowBytes + c8 * 8) = codes;
+      }
+    }
   }
 }
 
@@ -195,12 +229,18 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     }
   };
 
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.0f, 0.0f};
-  v4f acc[2][4];
+  // Per row: the running max (log2 units), the output accumulators and the
+  // sum of P, the latter on the matrix cores (an all-ones operand against P:
+  // every lane of a row gets the row's sum of the f16 weights PV uses).
+  float mrow[2] = {-INFINITY, -INFINITY};
+  v4f acc[2][4], lsum[2];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < 2; ++rb) {
+    lsum[rb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  }
+  const v8h ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
 
   // One 32-key block of the wave's key group from stage buffer buf.
   auto compute = [&](const int buf, const int blk) {
@@ -250,21 +290,16 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
         const float mold = mrow[rb];
         const float mnew = mx > mold + kLazyRescale ? mx : mold;
         const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
-        lrow[rb] *= alpha;
+        lsum[rb] *= alpha;
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[rb][c] *= alpha;
         mrow[rb] = mnew;
       }
       const float nmuse = mrow[rb] == -INFINITY ? 0.0f : -mrow[rb];
       v8h pv;
-      float psum = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(z[k], scale, nmuse));
-        psum += e;
-        pv[k] = (_Float16)e;
-      }
-      lrow[rb] += psum;
+      for (int k = 0; k < 8; ++k) pv[k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[k], scale, nmuse));
+      lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pv, lsum[rb], 0, 0, 0);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[c], pv, acc[rb][c], 0, 0, 0);
@@ -312,7 +347,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // Merge: group 1 leaves its rows' raw accumulators and (m, l) in LDS (the
   // staging buffers are free once every wave is past the loop); group 0 adds
   // them at a common reference max and leaves o / l, times the V descale.
-  const float l_own[2] = {rows_sum(lrow[0]), rows_sum(lrow[1])};
+  const float l_own[2] = {lsum[0][0], lsum[1][0]};
   lds_barrier();
   if (kg == 1) {
 #pragma unroll
@@ -377,7 +412,8 @@ hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t att
   if (p.batch == 0) return hipSuccess;
   if (p.sparse_block > 0 || p.q_len <= kMaxQLen || p.q_len > kMaxExtendLen) return hipErrorInvalidValue;
   const unsigned tokens = (unsigned)p.batch * (unsigned)p.q_len;
-  hipLaunchKernelGGL(extend_prologue_kernel, dim3(tokens), dim3(256), 0, stream, p);
+  const unsigned pro_grid = (tokens + kExtPrologueTokens - 1) / kExtPrologueTokens;
+  hipLaunchKernelGGL(extend_prologue_kernel, dim3(pro_grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && attn_start) e = hipEventRecord(attn_start, stream);
   if (e != hipSuccess) return e;
