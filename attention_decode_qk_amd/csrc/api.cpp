@@ -374,7 +374,10 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
     if (ctx->events_used + 2 > ctx->events.size()) {
       for (int k = 0; k < 2; ++k) {
         hipEvent_t e;
-        if (hipEventCreate(&e) != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "hipEventCreate failed");
+        // Timing-only events: no system-scope fence (cache write-back and
+        // invalidate) when they are recorded, which would stretch the interval.
+        if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess)
+          return fail(MI355X_GA_HIP_ERROR, "hipEventCreate failed");
         ctx->events.push_back(e);
       }
     }
