@@ -185,8 +185,9 @@ def test_workspace_init_validates_before_launch(L):
         ga.mi355x_gated_attn_destroy(ctx)
 
 
-def test_empty_batch_is_a_no_op(L):
-    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=0))
+@pytest.mark.parametrize("q_len", [1, 8, 100])
+def test_empty_batch_is_a_no_op(L, q_len):
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=0, q_len=q_len))
     try:
         ga.mi355x_gated_attn_plan(ctx, 100, 0)
         assert L.mi355x_gated_attn_step(ctx, *([None] * 12), 0, None) == ga.MI355X_GA_OK

@@ -137,3 +137,24 @@ def test_extend_full_size_workload(name):
     out_ref = ref.outputs(st, sh)
     got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
     assert_outputs_close(got, out_ref, name + " out")
+
+
+def test_extend_longest_block_served():
+    """q_len 65,536 (the longest block the library serves) for one request over a
+    1k-3k prefix with page 1's window, RoPE and pages of 16: every q and cache
+    byte, sampled output rows (first and last tokens among them)."""
+    w = synth.small(name="longest", batch=1, q_len=65536, window=2048, rope_theta=500000.0,
+                    page_size=16, seq_lo=1000, seq_hi=3000)
+    _say("[gpu] extend L=65536: generating inputs")
+    x = synth.make_inputs(w, seed=5)
+    _say("[gpu] extend L=65536: running step")
+    res = run_gpu(x)
+    _say("[gpu] extend L=65536: oracle prologue")
+    ref = Reference(x)
+    written = x.tokens * w.num_kv_heads * w.head_dim
+    assert_codes_match(res.q, ref.q, ref.q.size, "longest q")
+    assert_codes_match(res.k_cache, ref.k_cache, written, "longest k_cache")
+    assert_codes_match(res.v_cache, ref.v_cache, written, "longest v_cache")
+    st, sh = _sample_rows(x.tokens, w.num_q_heads, np.random.default_rng(3))
+    got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
+    assert_outputs_close(got, ref.outputs(st, sh), "longest out")
