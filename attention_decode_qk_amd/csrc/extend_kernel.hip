@@ -232,7 +232,11 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // Per row: the running max (log2 units), the output accumulators and the
   // sum of P, the latter on the matrix cores (an all-ones operand against P:
   // every lane of a row gets the row's sum of the f16 weights PV uses).
-  float mrow[2] = {-INFINITY, -INFINITY};
+  // The lazy test compares the raw score max against thr = (mrow + 2^8 bound)
+  // / scale (scale > 0), and the exponent offset nm = -mrow (0 before any key);
+  // both change only with mrow.
+  float mrow[2] = {-INFINITY, -INFINITY}, thr[2] = {-INFINITY, -INFINITY}, nm[2] = {0.0f, 0.0f};
+  const float inv_scale = 1.0f / scale;
   v4f acc[2][4], lsum[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
   }
-  const v8h ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+  v8h ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
 
   // One 32-key block of the wave's key group from stage buffer buf.
   auto compute = [&](const int buf, const int blk) {
@@ -284,9 +288,8 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
         }
       }
       float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], -INFINITY));
-      const float lmx = m * scale;
-      if (__any(lmx > mrow[rb] + kLazyRescale)) {
-        const float mx = rows_max(lmx);
+      if (__any(m > thr[rb])) {
+        const float mx = rows_max(m * scale);
         const float mold = mrow[rb];
         const float mnew = mx > mold + kLazyRescale ? mx : mold;
         const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
@@ -294,11 +297,12 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[rb][c] *= alpha;
         mrow[rb] = mnew;
+        nm[rb] = mnew == -INFINITY ? 0.0f : -mnew;
+        thr[rb] = mnew == -INFINITY ? -INFINITY : (mnew + kLazyRescale) * inv_scale;
       }
-      const float nmuse = mrow[rb] == -INFINITY ? 0.0f : -mrow[rb];
       v8h pv;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) pv[k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[k], scale, nmuse));
+      for (int k = 0; k < 8; ++k) pv[k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[k], scale, nm[rb]));
       lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pv, lsum[rb], 0, 0, 0);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
@@ -323,6 +327,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
 
   auto stage_step = [&](const int s, uint4& data, int& e_next) {
     const int buf = s & 1;
+    asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per block
     if (st_v)
       stage_v(buf, data);
     else
