@@ -152,12 +152,19 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // XCD (workgroups reach the XCDs round-robin): one L2 then holds a request's
   // keys for its neighbouring tiles and both KV heads, which share each cache
   // row.  The grid is padded to a multiple of kXcds; the padding exits.
+  // With S key splits (the plan's choice when the units alone do not fill the
+  // chip) the order is (request, split, tile, KV head); split ks of a unit
+  // walks its share of the unit's 64-key stages.
+  const int S = p.splits;
   const int n_units = p.batch * n_tiles * kKvHeads;
-  const int per_xcd = (n_units + kXcds - 1) / kXcds;
-  const int unit = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (unit >= n_units) return;
-  const int g = unit % kKvHeads;
-  const int tile = (unit / kKvHeads) % n_tiles, b = unit / (kKvHeads * n_tiles);
+  const int n_wg = n_units * S;
+  const int per_xcd = (n_wg + kXcds - 1) / kXcds;
+  const int li = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+  if (li >= n_wg) return;
+  const int g = li % kKvHeads;
+  const int tile = (li / kKvHeads) % n_tiles;
+  const int ks = (li / (kKvHeads * n_tiles)) % S, b = li / (kKvHeads * n_tiles * S);
+  const int unit = (b * n_tiles + tile) * kKvHeads + g;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
   const int kg = wave >> 2, wq = wave & 3;  // key group; the wave's rows within the tile
@@ -169,12 +176,15 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const int hi = p_first + n_tok - 1;           // keys lo..hi (the last token's position)
   const int lo = p.window > 0 ? max(0, p_first - p.window + 1) : 0;
   const int nblk = hi >= lo ? (hi - lo) / kKeyBlock + 1 : 0;
-  const int n_stage = (nblk + 1) / 2;
+  const int n_stage_all = (nblk + 1) / 2;
+  const int per_split = (n_stage_all + S - 1) / S;
+  const int s_first = ks * per_split;                                    // this split's stages
+  const int n_stage = max(0, min(n_stage_all - s_first, per_split));
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
   const int64_t tok0 = (int64_t)b * L + i_lo;   // the tile's first token (global)
-  const float ks = p.scaled ? *p.k_scale : 1.0f;
+  const float kscale = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
-  const float scale = p.sm_scale_log2 * ks;
+  const float scale = p.sm_scale_log2 * kscale;
 
   // q operands of the wave's two 16-row blocks: row r = 32 wq + 16 rb + j is
   // token r / 8 of the tile, q head 8 g + r % 8 (both key groups hold the same rows).
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   auto vt_row = [](int r) { return r * kExtVStride + ((r >> 4) & 3) * 8; };
   // Keys past hi reload key hi (masked); with no key at all (hi < lo, hi maybe
   // negative) key 0, in bounds and unused.
-  auto st_keyof = [&](int s) { return max(min(lo + s * kExtStageKeys + st_key, hi), 0); };
+  auto st_keyof = [&](int s) { return max(min(lo + (s_first + s) * kExtStageKeys + st_key, hi), 0); };
   auto st_entry = [&](int s) { return page_entry(p, pt, st_keyof(s)); };
   auto st_load = [&](int entry, int s) {
     const int row = key_row(p, entry, st_keyof(s));
@@ -337,7 +347,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     // unused), so the loop has no branch around its loads.
     data = st_load(e_next, min(s + 2, last));
     e_next = st_entry(min(s + 4, last));
-    if (2 * s + kg < nblk) compute(buf, 2 * s + kg);
+    if (2 * (s_first + s) + kg < nblk) compute(buf, 2 * (s_first + s) + kg);
   };
   // Whole stage pairs in the loop (its back edge always follows the second
   // half, so the loads are always in the same order there), an odd last stage
@@ -351,7 +361,8 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
 
   // Merge: group 1 leaves its rows' raw accumulators and (m, l) in LDS (the
   // staging buffers are free once every wave is past the loop); group 0 adds
-  // them at a common reference max and leaves o / l, times the V descale.
+  // them at a common reference max and leaves o / l (times the V descale when
+  // the unit is whole) and its (m, l).
   const float l_own[2] = {lsum[0][0], lsum[1][0]};
   lds_barrier();
   if (kg == 1) {
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
       const float mref = mt == -INFINITY ? 0.0f : mt;
       const float a0 = __builtin_amdgcn_exp2f(mrow[rb] - mref), a1 = __builtin_amdgcn_exp2f(ml.x - mref);
       const float l = l_own[rb] * a0 + ml.y * a1;
-      const float inv = l > 0.0f ? vs * __builtin_amdgcn_rcpf(l) : 0.0f;
+      const float inv = l > 0.0f ? (S == 1 ? vs : 1.0f) * __builtin_amdgcn_rcpf(l) : 0.0f;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
         float4* o = reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]);
@@ -383,9 +394,81 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
         *o = make_float4((acc[rb][0][ii] * a0 + u.x * a1) * inv, (acc[rb][1][ii] * a0 + u.y * a1) * inv,
                          (acc[rb][2][ii] * a0 + u.z * a1) * inv, (acc[rb][3][ii] * a0 + u.w * a1) * inv);
       }
+      // Every lane of the row has read s_ml[r] (one wave, in order) before this.
+      if (q4 == 0) s_ml[r] = make_float2(mt, l);
     }
   }
   lds_barrier();
+
+  // Key splits: publish this split's rows (o / l in f16, a weighted mean of V
+  // codes; m and l in fp32) with device-coherent stores; the last split of the
+  // unit (an atomic counter per unit) merges them all, as the decode step's
+  // combine does, and runs the epilogue.
+  if (S > 1) {
+    __shared__ int s_last;
+    const int r = tid >> 2, d0 = (tid & 3) * 16;  // 4 threads per row, 16 columns each
+    const int64_t prow = ((int64_t)unit * S + ks) * kExtRows + r;
+    {
+      const float4* o = reinterpret_cast<const float4*>(&s_o[r][d0]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 v = o[c];
+        store_coherent_h4(p.part_o + prow * kHeadDim + d0 + 4 * c, v.x, v.y, v.z, v.w);
+      }
+      if ((tid & 3) == 0) store_coherent(p.part_ml + prow * 2, s_ml[r].x, s_ml[r].y);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
+    __syncthreads();
+    int32_t* counter = p.counters + unit;
+    if (tid == 0) s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    if (!s_last) return;
+    // Eight splits' loads are issued together, then merged at a running max.
+    constexpr int KB = 8;
+    const int64_t prow0 = (int64_t)unit * S * kExtRows + r;
+    float mrun = -INFINITY, lt = 0.0f, o[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[c] = 0.0f;
+    for (int q0 = 0; q0 < S; q0 += KB) {
+      float2 ml[KB];
+      uint2 oh[KB][4];
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        const int64_t pr = prow0 + (int64_t)min(q0 + q, S - 1) * kExtRows;
+        ml[q] = load_coherent(p.part_ml + pr * 2);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) oh[q][c] = load_coherent_h4(p.part_o + pr * kHeadDim + d0 + 4 * c);
+        if (q0 + q >= S) ml[q] = make_float2(-INFINITY, 0.0f);  // past the last split: no weight
+      }
+      float mc = mrun;
+#pragma unroll
+      for (int q = 0; q < KB; ++q) mc = fmaxf(mc, ml[q].x);
+      const float mref = mc == -INFINITY ? 0.0f : mc;
+      const float a = __builtin_amdgcn_exp2f(mrun - mref);
+      lt *= a;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) o[c] *= a;
+#pragma unroll
+      for (int q = 0; q < KB; ++q) {
+        const float w = __builtin_amdgcn_exp2f(ml[q].x - mref) * ml[q].y;  // the split's weight
+        lt += w;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          o[4 * c + 0] += w * h_lo(oh[q][c].x);
+          o[4 * c + 1] += w * h_hi(oh[q][c].x);
+          o[4 * c + 2] += w * h_lo(oh[q][c].y);
+          o[4 * c + 3] += w * h_hi(oh[q][c].y);
+        }
+      }
+      mrun = mc;
+    }
+    const float inv = lt > 0.0f ? vs * __builtin_amdgcn_rcpf(lt) : 0.0f;
+    float4* so = reinterpret_cast<float4*>(&s_o[r][d0]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) so[c] = make_float4(o[4 * c] * inv, o[4 * c + 1] * inv, o[4 * c + 2] * inv, o[4 * c + 3] * inv);
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // re-armed
+    lds_barrier();
+  }
   // Gated epilogue: 16 threads per row, 4 columns each, 32 rows per pass.
   const int c4 = (tid & 15) * 4;
 #pragma unroll
@@ -422,8 +505,10 @@ hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t att
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && attn_start) e = hipEventRecord(attn_start, stream);
   if (e != hipSuccess) return e;
+  if (p.splits < 1) return hipErrorInvalidValue;
   const unsigned units = (unsigned)p.batch * kKvHeads * (unsigned)((p.q_len + kExtTile - 1) / kExtTile);
-  const unsigned grid = (units + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD-aware unit order
+  const unsigned wgs = units * (unsigned)p.splits;
+  const unsigned grid = (wgs + kXcds - 1) / kXcds * kXcds;  // the kernel's XCD-aware order
   hipLaunchKernelGGL(extend_attn_kernel, dim3(grid), dim3(64 * kExtWaves), 0, stream, p);
   return hipGetLastError();
 }

@@ -21,6 +21,35 @@ __device__ inline long as_long(uint32_t lo, uint32_t hi) {
   return (long)(((unsigned long)hi << 32) | (unsigned long)lo);
 }
 
+// Device-coherent (agent-scope) accesses for partial results exchanged
+// between workgroups of one launch.
+__device__ inline void store_coherent(float* dst, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline float2 load_coherent(const float* src) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Four f16 values (round to nearest even) in one 8-byte agent-scope store.
+__device__ inline void store_coherent_h4(_Float16* dst, float a, float b, float c, float d) {
+  const v2h lo = {(_Float16)a, (_Float16)b}, hi = {(_Float16)c, (_Float16)d};
+  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline uint2 load_coherent_h4(const _Float16* src) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+
+__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
+__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
+
 // Cross-lane moves on the VALU (DPP and the gfx950 lane swaps) rather than LDS
 // permutes.  DPP controls: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
 // (lane ^ 2), row_half_mirror (lane i <-> 7 - i in each 8), row_mirror (lane

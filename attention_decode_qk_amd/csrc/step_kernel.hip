@@ -50,33 +50,6 @@ namespace {
 
 constexpr int kHeadRows = kQHeads + 2 * kKvHeads;  // 20 head rows per token
 
-__device__ inline void store_coherent(float* dst, float a, float b) {
-  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline float2 load_coherent(const float* src) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
-}
-
-// Four f16 values (round to nearest even) in one 8-byte agent-scope store.
-__device__ inline void store_coherent_h4(_Float16* dst, float a, float b, float c, float d) {
-  const v2h lo = {(_Float16)a, (_Float16)b}, hi = {(_Float16)c, (_Float16)d};
-  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ inline uint2 load_coherent_h4(const _Float16* src) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
-}
-
-__device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
-__device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
-
 // K/V operands of one 32-key block for NG KV heads starting at head g0.
 template <int NG>
 struct KvBlock {

@@ -46,10 +46,16 @@ METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
 
 
+def _is_extend(workload: str) -> bool:
+    import synth
+    w = synth.WORKLOADS.get(workload)
+    return w is not None and w.q_len > 8
+
+
 def _kernel_prefix(workload: str) -> str:
     if workload.startswith("qk_norm"):
         return "qk_norm"
-    return "extend_attn" if workload.endswith("_extend") else "fused_step"
+    return "extend_attn" if _is_extend(workload) else "fused_step"
 
 
 def counters_file(workload: str) -> str:
@@ -72,7 +78,7 @@ def workload_sources(workload: str):
     """The sources that build the workload's dominant kernel."""
     if workload.startswith("qk_norm"):
         return QK_NORM_SOURCES
-    return EXTEND_SOURCES if workload.endswith("_extend") else KERNEL_SOURCES
+    return EXTEND_SOURCES if _is_extend(workload) else KERNEL_SOURCES
 
 
 def kernel_source_hash(files=None) -> str:

@@ -110,9 +110,12 @@ int mi355x_gated_attn_prepare(const mi355x_gated_attn_config* cfg, int device,
  * window + L - 1, or max_context) is at most 4096 keys, else ceil(L/4).  A step
  * launches B * G * splits workgroups (UNSUPPORTED beyond 2^31-1).
  * q_len > 8 (extend / prefill; page "msa.py", msa_sparse_prefill_main: causal
- * attention with the query offset = the prefix length, here dense) is planned
- * without a key split: num_splits must be 0 or 1 (UNSUPPORTED otherwise) and
- * the chosen count is 1.
+ * attention with the query offset = the prefix length, here dense) has one
+ * work unit per (request, 16-token tile, KV head); 0 chooses a key split only
+ * when the B * 2 * ceil(L/16) units do not fill the chip (S = min(ceil(256 /
+ * units), stages / 4, 32) over 64-key stages of the key bound), and
+ * num_splits > 0 forces it (1..256).  UNSUPPORTED when units * S exceeds one
+ * launch's workgroups.
  * Outputs (either may be NULL): *workspace_bytes = the workspace a step needs,
  * *num_splits_out = the chosen split count.  Host-only.
  */
@@ -190,7 +193,8 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
  *                  Layout after a step: bytes [0, B*L*Hq*D) hold q as e4m3
  *                  [B*L, Hq, D]; then split partials and B*G int32
  *                  counters (G token groups per request, from the plan; for
- *                  q_len > 8 no partials and B counters).
+ *                  q_len > 8 partials only when split, and one counter per
+ *                  (request, 16-token tile, KV head)).
  * Calls that share a workspace, or write the same cache rows, must be ordered
  * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
  */

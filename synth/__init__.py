@@ -92,6 +92,9 @@ WORKLOADS.update(SPARSE)
 EXTEND = {
     "swa_extend": Workload("swa_extend", 4, 1024, 8192, 16384, 2048, 500000.0, seed=1009),
     "full_extend": Workload("full_extend", 2, 2048, 4096, 8192, 0, 0.0, page_size=128, seed=1010),
+    # a speculative block just past the verify kernel's 8 tokens over a long
+    # full-attention context: 8 units, so the plan splits their keys
+    "verify16_32k": Workload("verify16_32k", 4, 16, 32768, 32768, 0, 0.0, seed=1011),
 }
 WORKLOADS.update(EXTEND)
 

@@ -356,23 +356,31 @@ def test_dense_and_sparse_steps_refuse_each_others_configs(L):
         ga.mi355x_gated_attn_destroy(dense)
 
 
-@pytest.mark.parametrize("q_len", [9, 100, 4096])
-def test_extend_plan_holds_q_only_and_runs_without_a_split(L, q_len):
-    """q_len > 8 (extend / prefill) walks each tile's whole key range: one split,
-    no partials, the workspace = the q codes + the per-request counters."""
-    B = 5
-    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=B, q_len=q_len), 0)
-    try:
-        nbytes, splits = ga.mi355x_gated_attn_plan(ctx, 200000, 0)
-        assert splits == 1
-        q = B * q_len * 16 * 64
-        assert nbytes == -(-(-(-q // 256) * 256 + 4 * B) // 256) * 256
-        assert ga.mi355x_gated_attn_plan(ctx, 200000, 1) == (nbytes, 1)
-        with pytest.raises(ga.GatedAttnError) as e:
-            ga.mi355x_gated_attn_plan(ctx, 200000, 2)
-        assert e.value.status == ga.MI355X_GA_UNSUPPORTED
-    finally:
-        ga.mi355x_gated_attn_destroy(ctx)
+@pytest.mark.parametrize("batch,q_len", [(5, 9), (5, 100), (5, 4096), (1, 64)])
+def test_extend_plan_splits_only_when_the_units_do_not_fill_the_chip(L, batch, q_len):
+    """q_len > 8 (extend / prefill): one unit per (request, 16-token tile, KV
+    head); S = min(ceil(256 / units), stages / 4, 32) key splits over the
+    64-key stages of the key bound; the workspace holds q, then (S > 1) f16
+    partial rows and fp32 (m, l) per split and unit row, then one counter per unit."""
+    tiles = -(-q_len // 16)
+    units = batch * 2 * tiles
+    for max_context, window in ((200000, 0), (5000, 0), (300, 0), (200000, 2048)):
+        ctx = ga.mi355x_gated_attn_prepare(cfg(batch=batch, q_len=q_len, window=window), 0)
+        try:
+            nbytes, splits = ga.mi355x_gated_attn_plan(ctx, max_context, 0)
+            keys = min(max_context, window + q_len - 1) if window else max_context
+            want = max(1, min(-(-256 // units), -(-keys // 64) // 4, 32))
+            assert splits == want, (batch, q_len, max_context, window)
+            al = lambda x: -(-x // 256) * 256
+            q = al(batch * q_len * 16 * 64)
+            rows = units * 128
+            po = al(q + (splits * rows * 64 * 2 if splits > 1 else 0))
+            pml = al(po + (splits * rows * 2 * 4 if splits > 1 else 0))
+            assert nbytes == al(pml + 4 * units)
+            forced, s3 = ga.mi355x_gated_attn_plan(ctx, max_context, 3)
+            assert s3 == 3 and forced == al(al(al(q + 3 * rows * 128) + 3 * rows * 8) + 4 * units)
+        finally:
+            ga.mi355x_gated_attn_destroy(ctx)
 
 
 def test_extend_refuses_page_list_driven_configs(L):

@@ -47,8 +47,7 @@ def test_extend_small_case_matches_oracle(name):
     x = synth.make_inputs(w, seed=300 + len(name))
     _say(f"[gpu] extend {name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}")
     res = run_gpu(x)
-    assert res.splits == 1
-    check_full(x, res, Reference(x), name)
+    check_full(x, res, Reference(x), f"{name} S={res.splits}")
 
 
 def test_extend_fresh_prefill_whole_context_in_the_block():
@@ -158,3 +157,67 @@ def test_extend_longest_block_served():
     st, sh = _sample_rows(x.tokens, w.num_q_heads, np.random.default_rng(3))
     got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
     assert_outputs_close(got, ref.outputs(st, sh), "longest out")
+
+
+# Key splits: forced counts (more than a unit's stages leaves some splits empty)
+# and the plan's own count for few units over long key ranges.
+@pytest.mark.parametrize("splits", [1, 2, 3, 7, 16])
+@pytest.mark.parametrize("name", ["ext67_b5_swa", "ext33_scaled_page64", "ext200_page3"])
+def test_extend_forced_split_counts_match_oracle(name, splits):
+    w = synth.small(name=name, seq_lo=20, seq_hi=700, **SMALL[name])
+    x = synth.make_inputs(w, seed=300 + len(name))
+    _say(f"[gpu] extend {name} S={splits}")
+    res = run_gpu(x, num_splits=splits)
+    assert res.splits == splits
+    check_full(x, res, Reference(x), f"{name} S={splits}")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=1, q_len=16, window=0, seq_lo=3000, seq_hi=5000, page_size=16),
+    dict(batch=2, q_len=40, window=500, seq_lo=2000, seq_hi=4000, rope_theta=500000.0),
+    dict(batch=3, q_len=9, window=0, seq_lo=1500, seq_hi=2500, page_size=1, kv_scale=0.5,
+         qkv_std=1.4142135),
+])
+def test_extend_few_units_split_by_the_plan(kw):
+    """Few units over long key ranges: the plan splits the keys (S > 1) and the
+    last split of each unit merges them."""
+    w = synth.small(name="few_units", **kw)
+    x = synth.make_inputs(w, seed=41)
+    res = run_gpu(x)
+    _say(f"[gpu] extend few units {kw}: S={res.splits}")
+    assert res.splits > 1
+    check_full(x, res, Reference(x), f"few units S={res.splits}")
+
+
+def test_extend_split_graph_replay_matches_eager():
+    """Split extend steps captured in a HIP graph and replayed several times
+    (each replay re-arms the per-unit counters): every replay equals eager."""
+    import attention_decode_qk_amd as ga
+    w = synth.small(name="graph_split", batch=1, q_len=20, window=0, seq_lo=2000, seq_hi=2500,
+                    page_size=8)
+    x = synth.make_inputs(w, seed=23)
+    step = ga.GatedAttnStep(abi_config(x), max_context(x))
+    _say(f"[gpu] extend split graph replay S={step.splits}")
+    assert step.splits > 1
+    d = Device(x)
+    d.run(step)
+    torch.cuda.synchronize()
+    eager_out = d.out.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        d.run(step, stream=s)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            d.run(step, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        d.out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(d.out, eager_out), f"replay {rep}"
+    step.close()
+    res = run_gpu(x)
+    check_full(x, res, Reference(x), "graph split")
