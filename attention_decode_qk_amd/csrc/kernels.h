@@ -63,6 +63,7 @@ struct StepParams {
   int32_t q_len;                 // L
   int32_t tgroups;               // G: token_groups(L, short or not)
   int32_t splits;                // S
+  int32_t balanced;              // 1: splits per request by key count (batch <= 64), else S each
   int32_t head_split;            // 1: eight waves per unit, one KV head each
   int32_t key_waves;             // waves per KV head taking blocks round-robin (4, or 8 at q_len 1)
   int32_t max_pages;

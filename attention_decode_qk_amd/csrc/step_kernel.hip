@@ -133,7 +133,7 @@ __device__ inline void norm_rope8(const float (&x)[8], bool rope, const float (*
   }
 }
 
-template <int LU, bool HS, int KW, bool SP>
+template <int LU, bool HS, int KW, bool SP, bool BAL>
 __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(StepParams p) {
   // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
   // LU consecutive tokens; the unit (request b, token group tg, key chunk kc)
@@ -165,14 +165,52 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // A unit size that serves a single q_len (LU = 1: q_len 1) serves it as one group.
   constexpr bool kOneGroup = kMaxL == LU;
   const int L = kOneGroup ? LU : p.q_len;
-  const int kc = blockIdx.x % p.splits;
-  const int bt = blockIdx.x / p.splits;
-  const int b = kOneGroup ? bt : bt % p.batch;
-  const int tg = kOneGroup ? 0 : bt / p.batch;
-  const int t_lo = tg * LU;              // the group's first token (request-local)
-  const int t_n = min(LU, L - t_lo);     // its tokens, >= 1
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  // A token group's B * S units, in order, are the requests' splits: unit ru
+  // is split kc of request b, whose nsp splits are units sbase .. sbase + nsp - 1
+  // (ru is also the unit's partial slot).  Uniform: S splits per request.
+  // BAL (balanced): request l gets 1 + floor(X * K_<=l / K) - floor(X * K_<l / K)
+  // of them, X = B * (S - 1), K_<l the keys of the requests before l and K all
+  // of them, so that every unit carries about K / (B * S) keys: the step then
+  // lasts as long as the average request rather than the longest.
+  int b, kc, nsp, sbase, cs, tg, ru;
+  if constexpr (BAL) {  // batch <= 64: request `lane` per lane, every wave alike
+    const int bs = p.batch * p.splits;
+    ru = kOneGroup ? blockIdx.x : blockIdx.x % bs;
+    tg = kOneGroup ? 0 : blockIdx.x / bs;
+    const int csl = lane < p.batch ? p.cache_seqlens[lane] : 0;
+    const int firstl = p.window > 0 ? max(0, csl - L - p.window + 1) : 0;
+    const long long kl = max(0, csl - firstl);
+    long long incl = kl;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const long long v = __shfl_up(incl, d);
+      if (lane >= d) incl += v;
+    }
+    const long long ktot = __shfl(incl, 63);
+    const int x = bs - p.batch;
+    // Exact in double (x * keys < 2^53); correctly rounded division is monotonic,
+    // so the boundaries strictly increase and the last one is bs.
+    const int rl = ktot > 0 ? lane + (int)floor((double)x * (double)(incl - kl) / (double)ktot)
+                            : lane * p.splits;
+    b = __popcll(__ballot(lane >= 1 && lane < p.batch && rl <= ru));
+    sbase = __builtin_amdgcn_readlane(rl, b);
+    nsp = (b + 1 < p.batch ? __builtin_amdgcn_readlane(rl, b + 1) : bs) - sbase;
+    kc = ru - sbase;
+    cs = __builtin_amdgcn_readlane(csl, b);
+  } else {
+    kc = blockIdx.x % p.splits;
+    const int bt = blockIdx.x / p.splits;
+    b = kOneGroup ? bt : bt % p.batch;
+    tg = kOneGroup ? 0 : bt / p.batch;
+    nsp = p.splits;
+    sbase = b * p.splits;
+    ru = sbase + kc;
+    cs = p.cache_seqlens[b];
+  }
+  const int t_lo = tg * LU;              // the group's first token (request-local)
+  const int t_n = min(LU, L - t_lo);     // its tokens, >= 1
   const int wave = tid >> 6;
   const int kw = wave % KW;            // this wave's place among its head's waves
   const int g0 = HS ? wave / KW : 0;   // first KV head this wave works on
@@ -187,7 +225,6 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // any load off that chain: vector memory counters complete in order, and a
   // slower load issued earlier (a cold projection row) would hold up the wait
   // for the page table.  The other small loads follow, then the K/V loads.
-  const int cs = p.cache_seqlens[b];
   // The cache scales: tiny, shared by every unit, issued with cache_seqlens so
   // that every path reaches the page-table wait with the same loads in flight.
   const float ks = p.scaled ? *p.k_scale : 1.0f;
@@ -206,7 +243,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // list slot v / BS, offset v % BS within that block.
   const int first = SP ? 0 : (p.window > 0 ? max(0, p0 - p.window + 1) : 0);
   const int n = SP ? p.sparse_topk * p.sparse_block : max(0, last - first + 1);
-  int chunk = (n + p.splits - 1) / p.splits;
+  int chunk = (n + nsp - 1) / nsp;
   chunk = (chunk + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
   const int start = first + kc * chunk;
   const int end = min(start + chunk, SP ? n : last + 1);
@@ -827,13 +864,13 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   const int c4 = (tid & 15) * 4;
   const int h = (tid >> 4) & (kQHeads - 1);
   const int th = tid >> 8;
-  // Partial rows are ((b * splits + kc) * L + token) * 16 + head.
+  // Partial rows are ((sbase + kc) * L + token) * 16 + head.
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
-  const int64_t base = (int64_t)b * p.splits * stride + (int64_t)t_lo * kQHeads + h;
+  const int64_t base = (int64_t)sbase * stride + (int64_t)t_lo * kQHeads + h;
   int32_t* counter = p.counters + (kOneGroup ? b : b * p.tgroups + tg);
   float own_m[TPT], own_l[TPT], own_o[TPT][4];  // a single split's result
-  if (p.splits > 1) {
-    const int64_t prow0 = (((int64_t)b * p.splits + kc) * L + t_lo) * kQHeads;
+  if (nsp > 1) {
+    const int64_t prow0 = ((int64_t)ru * L + t_lo) * kQHeads;
     for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
       const int cr = idx >> 4, cc = (idx & 15) * 4;
       float mx, lsum;
@@ -847,7 +884,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
     __syncthreads();
     if (tid == 0)
-      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.splits - 1;
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsp - 1;
     __syncthreads();
     if (!s_last) return;
   } else {  // a single split is its own combine: no publish, no counter
@@ -888,7 +925,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[k][c] = 0.0f;
   }
-  if (p.splits == 1) {
+  if (nsp == 1) {
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       mrun[k] = own_m[k];
@@ -897,7 +934,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       for (int c = 0; c < 4; ++c) o[k][c] = own_o[k][c];
     }
   }
-  for (int s0 = 0; p.splits > 1 && s0 < p.splits; s0 += KS) {
+  for (int s0 = 0; nsp > 1 && s0 < nsp; s0 += KS) {
     float2 ml[TPT][KS];
     uint2 oh[TPT][KS];
 #pragma unroll
@@ -907,7 +944,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
         const int ti = th + TS * k;
         ml[k][q] = make_float2(-INFINITY, 0.0f);
         oh[k][q] = make_uint2(0, 0);
-        if (ti < t_n && s0 + q < p.splits) {
+        if (ti < t_n && s0 + q < nsp) {
           const int64_t pr = base + (int64_t)(s0 + q) * stride + ti * kQHeads;
           ml[k][q] = load_coherent(p.part_ml + pr * 2);
           oh[k][q] = load_coherent_h4(p.part_o + pr * kHeadDim + c4);
@@ -965,13 +1002,13 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
           make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
   }
-  if (tid == 0 && p.splits > 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0 && nsp > 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int LU, bool HS, int KW, bool SP = false>
+template <int LU, bool HS, int KW, bool SP = false, bool BAL = false>
 hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
-  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW, SP>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
+  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW, SP, BAL>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
                      stream, p);
   return hipGetLastError();
 }
@@ -980,9 +1017,13 @@ template <int LU>
 hipError_t launch_served(const StepParams& p, hipStream_t stream) {
   if constexpr (max_q_len_for(LU) >= LU) {
     if (p.head_split) return launch_lu<LU, true, kAttnWaves>(p, stream);
+    // Balanced splits (the plan sets them only with both KV heads per wave).
     if constexpr (LU == 1)
-      if (p.key_waves == 2 * kAttnWaves) return launch_lu<LU, false, 2 * kAttnWaves>(p, stream);
-    return launch_lu<LU, false, kAttnWaves>(p, stream);
+      if (p.key_waves == 2 * kAttnWaves)
+        return p.balanced ? launch_lu<LU, false, 2 * kAttnWaves, false, true>(p, stream)
+                          : launch_lu<LU, false, 2 * kAttnWaves>(p, stream);
+    return p.balanced ? launch_lu<LU, false, kAttnWaves, false, true>(p, stream)
+                      : launch_lu<LU, false, kAttnWaves>(p, stream);
   }
   return hipErrorInvalidValue;
 }
