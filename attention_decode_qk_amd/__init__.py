@@ -25,7 +25,8 @@ EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_g
             "mi355x_gated_attn_workspace_init", "mi355x_gated_attn_step", "mi355x_gated_attn_destroy",
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
             "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta",
-            "mi355x_qk_norm_supports", "mi355x_qk_norm", "mi355x_gated_attn_sparse_step"]
+            "mi355x_qk_norm_supports", "mi355x_qk_norm", "mi355x_gated_attn_sparse_step",
+            "mi355x_gated_attn_ragged_step"]
 
 MI355X_QKN_BF16 = 0
 MI355X_QKN_FP16 = 1
@@ -71,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_step_meta.argtypes = [P] * 7
         L.mi355x_gated_attn_sparse_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
+        L.mi355x_gated_attn_ragged_step.argtypes = [P] * 5 + [ctypes.c_int64] + [P] * 8 + \
+            [ctypes.c_size_t, P]
         L.mi355x_gated_attn_destroy.argtypes = [P]
         L.mi355x_gated_attn_destroy.restype = None
         L.mi355x_gated_attn_last_error.argtypes = []
@@ -181,6 +184,29 @@ def mi355x_gated_attn_sparse_step(ctx, qkv, positions, cache_loc, cache_seqlens,
         _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
 
 
+def mi355x_gated_attn_ragged_step(ctx, qkv, positions, cache_loc, cu_seqlens_q, total_q: int,
+                                  cache_seqlens, page_table, k_cache, v_cache, k_scale, v_scale,
+                                  out, workspace, stream=None):
+    """Launch one ragged extend step: request b's new tokens are rows
+    cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (contiguous int32 device tensor
+    [B+1]) of the packed qkv / positions / cache_loc / out, total_q of them;
+    otherwise as mi355x_gated_attn_step."""
+    import torch
+    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, cu_seqlens_q=cu_seqlens_q,
+                   cache_seqlens=cache_seqlens, page_table=page_table, k_cache=k_cache,
+                   v_cache=v_cache, out=out, workspace=workspace)
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_ragged_step(
+        ctx, _ptr(qkv), _ptr(positions), _ptr(cache_loc), _ptr(cu_seqlens_q), int(total_q),
+        _ptr(cache_seqlens), _ptr(page_table), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+        _ptr(v_scale), _ptr(out), _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
+
+
 def mi355x_gated_attn_step_meta(ctx, seq_lens, page_table, positions, cache_loc, cache_seqlens,
                                 stream=None):
     """Build a step's positions, cache rows and key counts on the device (int32
@@ -257,6 +283,14 @@ class GatedAttnStep:
         mi355x_gated_attn_sparse_step(self.ctx, qkv, positions, cache_loc, cache_seqlens,
                                       page_table, block_idx, k_cache, v_cache, k_scale, v_scale,
                                       out, self.workspace, stream)
+        return out
+
+    def ragged(self, qkv, positions, cache_loc, cu_seqlens_q, total_q, cache_seqlens, page_table,
+               k_cache, v_cache, k_scale, v_scale, out, stream=None):
+        """One ragged extend step (a config with q_len > 8 bounding every segment)."""
+        mi355x_gated_attn_ragged_step(self.ctx, qkv, positions, cache_loc, cu_seqlens_q, total_q,
+                                      cache_seqlens, page_table, k_cache, v_cache, k_scale,
+                                      v_scale, out, self.workspace, stream)
         return out
 
     def meta(self, seq_lens, page_table, positions, cache_loc, cache_seqlens, stream=None):

@@ -332,7 +332,8 @@ namespace {
 int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
              const int64_t* cache_loc, const int32_t* cache_seqlens, const int32_t* page_table,
              const int32_t* block_idx, void* k_cache, void* v_cache, const float* k_scale,
-             const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+             const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+             const int32_t* cu_seqlens_q = nullptr, int64_t total_q = -1) {
   if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
   if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
   const auto& c = ctx->cfg;
@@ -396,6 +397,8 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   sp.block_idx = block_idx;
   sp.sparse_block = c.sparse_block;
   sp.sparse_topk = c.sparse_topk;
+  sp.cu_seqlens_q = cu_seqlens_q;
+  sp.total_q = cu_seqlens_q ? total_q : (int64_t)c.batch * c.q_len;
   std::memcpy(sp.inv_freq, ctx->inv_freq, sizeof sp.inv_freq);
 
   hipEvent_t* ev = nullptr;
@@ -436,6 +439,29 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
   (void)seq_lens;  // the page's attention call takes cache_seqlens only
   return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, nullptr, k_cache,
                   v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream);
+}
+
+int mi355x_gated_attn_ragged_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                  const int64_t* positions, const int64_t* cache_loc,
+                                  const int32_t* cu_seqlens_q, int64_t total_q,
+                                  const int32_t* cache_seqlens, const int32_t* page_table,
+                                  void* k_cache, void* v_cache, const float* k_scale,
+                                  const float* v_scale, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  const auto& c = ctx->cfg;
+  if (c.batch == 0) return ok();
+  if (c.q_len <= kMaxQLen || c.sparse_block > 0)
+    return fail(MI355X_GA_INVALID_ARGUMENT,
+                "ragged_step needs a dense extend config: q_len (the bound on every segment) > %d",
+                kMaxQLen);
+  if (!cu_seqlens_q) return fail(MI355X_GA_INVALID_ARGUMENT, "cu_seqlens_q is NULL");
+  if (total_q < 0 || total_q > (int64_t)c.batch * c.q_len)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "total_q %lld outside 0..batch * q_len = %lld",
+                (long long)total_q, (long long)c.batch * c.q_len);
+  return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, nullptr, k_cache,
+                  v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream, cu_seqlens_q,
+                  total_q);
 }
 
 int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,

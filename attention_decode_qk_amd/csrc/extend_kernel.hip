@@ -61,7 +61,7 @@ static_assert(kExtPrologueTokens * kExtItems - 256 * (kExtPrologueIters - 1) <= 
 
 __global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
   __shared__ float s_cs[kExtPrologueTokens][kHeadDim / 2][2];
-  const int64_t T = (int64_t)p.batch * p.q_len;
+  const int64_t T = p.total_q;
   const int64_t t0 = (int64_t)blockIdx.x * kExtPrologueTokens;
   const int tid = threadIdx.x;
   uint4 xv[kExtPrologueIters];
@@ -170,9 +170,20 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const int kg = wave >> 2, wq = wave & 3;  // key group; the wave's rows within the tile
   const int j = lane & 15, q4 = lane >> 4;
   const int cs = p.cache_seqlens[b];
+  // Ragged batches: request b's segment is tokens cu[b] .. cu[b+1]-1 (clamped
+  // to q_len and to the step's tokens); a tile past its segment has no rows
+  // and its workgroups leave before any shared state is touched.
+  int Lb = L;
+  int64_t base = (int64_t)b * L;
+  if (p.cu_seqlens_q) {
+    const int c0 = p.cu_seqlens_q[b], c1 = p.cu_seqlens_q[b + 1];
+    Lb = max(0, min(c1 - c0, L));
+    base = max<int64_t>(0, min<int64_t>(c0, p.total_q - Lb));
+  }
   const int i_lo = tile * kExtTile;             // the tile's first token (request-local)
-  const int n_tok = min(kExtTile, L - i_lo);
-  const int p_first = cs - L + i_lo;            // its position
+  if (i_lo >= Lb) return;
+  const int n_tok = min(kExtTile, Lb - i_lo);
+  const int p_first = cs - Lb + i_lo;           // its position
   const int hi = p_first + n_tok - 1;           // keys lo..hi (the last token's position)
   const int lo = p.window > 0 ? max(0, p_first - p.window + 1) : 0;
   const int nblk = hi >= lo ? (hi - lo) / kKeyBlock + 1 : 0;
@@ -181,7 +192,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const int s_first = ks * per_split;                                    // this split's stages
   const int n_stage = max(0, min(n_stage_all - s_first, per_split));
   const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
-  const int64_t tok0 = (int64_t)b * L + i_lo;   // the tile's first token (global)
+  const int64_t tok0 = base + i_lo;             // the tile's first token (global)
   const float kscale = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
   const float scale = p.sm_scale_log2 * kscale;
@@ -498,8 +509,11 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
 
 hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t attn_start) {
   if (p.batch == 0) return hipSuccess;
-  if (p.sparse_block > 0 || p.q_len <= kMaxQLen || p.q_len > kMaxExtendLen) return hipErrorInvalidValue;
-  const unsigned tokens = (unsigned)p.batch * (unsigned)p.q_len;
+  if (p.sparse_block > 0 || p.q_len <= kMaxQLen || p.q_len > kMaxExtendLen ||
+      p.total_q < 0 || p.total_q > (int64_t)p.batch * p.q_len)
+    return hipErrorInvalidValue;
+  if (p.total_q == 0) return hipSuccess;  // a ragged batch without new tokens
+  const unsigned tokens = (unsigned)p.total_q;
   const unsigned pro_grid = (tokens + kExtPrologueTokens - 1) / kExtPrologueTokens;
   hipLaunchKernelGGL(extend_prologue_kernel, dim3(pro_grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();

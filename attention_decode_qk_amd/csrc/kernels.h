@@ -77,6 +77,9 @@ struct StepParams {
   const int32_t* block_idx;      // page-list-driven decode: int32 [Hkv, B, topk] block lists (-1 pad)
   int32_t sparse_block;          // keys per listed block (a multiple of 32); 0: dense step
   int32_t sparse_topk;           // list slots per (KV head, request), <= kMaxSparseTopk
+  const int32_t* cu_seqlens_q;   // ragged extend: [B+1], request b's tokens cu[b] .. cu[b+1]-1 (at most
+                                 // q_len each); null: b*q_len .. (b+1)*q_len-1
+  int64_t total_q;               // tokens of the step: cu[B] when ragged, else B*q_len
   float inv_freq[kHeadDim / 2];
 };
 

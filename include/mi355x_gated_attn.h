@@ -237,6 +237,38 @@ int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Ragged extend / prefill batch: page "msa.py" (msa_sparse_prefill_main:
+ * per-request query segments given by cumulative lengths cu_seqlens,
+ * qo_segment_lens = cu_seqlens[1:] - cu_seqlens[:-1], causal with the query
+ * offset qo_offset = the prefix length; here with dense keys and page 1's
+ * window).  The step of mi355x_gated_attn_step for q_len > 8, with request b's
+ * new tokens being rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of a packed
+ * batch instead of b*L .. (b+1)*L-1:
+ *   segment length L_b = cu_seqlens_q[b+1] - cu_seqlens_q[b], 0 <= L_b <= the
+ *   config's q_len (which must be > 8: the bound on every segment, sizing the
+ *   plan and workspace); token i < L_b of request b sits at position
+ *   cache_seqlens[b] - L_b + i (its own key is cache row cache_loc of that
+ *   token) and sees the keys up to that position (within the window).
+ *   cu_seqlens_q  device int32 [B+1], nondecreasing from 0 to total_q
+ *   total_q       host int64, the batch's new tokens, 0..B*q_len
+ *   qkv           bf16 [total_q, (2Hq + 2Hkv) * D]; positions and cache_loc
+ *                 int64 [total_q]; out bf16 [total_q, Hq * D]
+ * Other arguments, ownership and effects as mi355x_gated_attn_step (seq_lens
+ * is not taken).  INVALID_ARGUMENT for a config with q_len <= 8 or
+ * sparse_block > 0, a NULL cu_seqlens_q, or total_q outside 0..B*q_len;
+ * device values that break the layout above (a segment longer than q_len,
+ * offsets past total_q) are a caller error: the kernels clamp them to stay
+ * in bounds, with undefined results.  A segment of length 0 writes nothing.
+ */
+int mi355x_gated_attn_ragged_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                  const int64_t* positions, const int64_t* cache_loc,
+                                  const int32_t* cu_seqlens_q, int64_t total_q,
+                                  const int32_t* cache_seqlens, const int32_t* page_table,
+                                  void* k_cache, void* v_cache, const float* k_scale,
+                                  const float* v_scale, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
  * Measurement hook (not part of the page's interface): while enabled, each
  * step records a HIP event pair on its stream around its attention kernel
  * (the step's one launch for q_len <= 8; the second of its two, attention and

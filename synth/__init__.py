@@ -194,6 +194,27 @@ def make_inputs(w: Workload, seed: int | None = None, seq_lens: np.ndarray | Non
                   extra=extra)
 
 
+def ragged(x: Inputs, lens: np.ndarray) -> dict:
+    """A packed ragged batch cut from uniform inputs x (q_len L): request b keeps
+    its first lens[b] new tokens (0 <= lens[b] <= L), so its cached length
+    becomes seq_lens[b] + lens[b] while positions, cache rows and projection
+    rows stay those of x.  Returns qkv [total_q, width], positions, cache_loc
+    [total_q], cache_seqlens [B], cu_seqlens_q [B+1] (0, then running sums of
+    lens) and total_q."""
+    B, L = x.w.batch, x.w.q_len
+    lens = np.asarray(lens, np.int32)
+    assert lens.shape == (B,) and lens.min(initial=0) >= 0 and lens.max(initial=0) <= L
+    idx = np.concatenate([b * L + np.arange(int(lens[b]), dtype=np.int64) for b in range(B)]
+                         + [np.zeros(0, np.int64)])
+    width = x.qkv.shape[-1]
+    return dict(qkv=np.ascontiguousarray(x.qkv.reshape(B * L, width)[idx]),
+                positions=np.ascontiguousarray(x.positions[idx]),
+                cache_loc=np.ascontiguousarray(x.cache_loc[idx]),
+                cache_seqlens=(x.seq_lens + lens).astype(np.int32),
+                cu_seqlens_q=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+                total_q=int(lens.sum()))
+
+
 def make_block_lists(rng: np.random.Generator, cache_seqlens: np.ndarray, block_size: int,
                      topk: int, num_kv_heads: int) -> np.ndarray:
     """int32 [Hkv, B, topk] top-k block lists: per (KV head, request) the

@@ -109,6 +109,35 @@ class Reference:
         return oracle.epilogue(self.cfg, o, x.qkv, sel_t, sel_h)
 
 
+def ragged_reference(x: synth.Inputs, r: dict, lens):
+    """Oracle result of a ragged batch r = synth.ragged(x, lens): the oracle
+    step run request by request (batch 1, q_len lens[b]) on one shared copy of
+    the caches.  Each request reads and writes only its own pages, so this is
+    the batch's result.  Returns q codes [total_q, Hq, D], the caches, and
+    outputs bf16 bits [total_q, Hq*D]."""
+    k, v = x.k_cache.copy(), x.v_cache.copy()
+    qs, outs = [], []
+    cu = r["cu_seqlens_q"]
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        cfg = oracle_config(x)
+        cfg.batch, cfg.q_len = 1, int(n)
+        s = slice(int(cu[b]), int(cu[b + 1]))
+        q, out, _ = oracle.step(cfg, np.ascontiguousarray(r["qkv"][s]),
+                                np.ascontiguousarray(r["positions"][s]),
+                                np.ascontiguousarray(r["cache_loc"][s]),
+                                np.ascontiguousarray(r["cache_seqlens"][b:b + 1]),
+                                np.ascontiguousarray(x.page_table[b:b + 1]), k, v,
+                                x.k_scale, x.v_scale)
+        qs.append(q)
+        outs.append(out.reshape(int(n), -1))
+    H, D = x.w.num_q_heads, x.w.head_dim
+    q = np.concatenate(qs) if qs else np.zeros((0, H, D), np.uint8)
+    out = np.concatenate(outs) if outs else np.zeros((0, H * D), np.uint16)
+    return q, k, v, out
+
+
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16) \
         .double().numpy()

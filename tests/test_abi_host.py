@@ -386,3 +386,35 @@ def test_extend_plan_splits_only_when_the_units_do_not_fill_the_chip(L, batch, q
 def test_extend_refuses_page_list_driven_configs(L):
     assert ga.mi355x_gated_attn_supports(
         cfg(q_len=16, window=0, sparse_block=32, sparse_topk=4)) == ga.MI355X_GA_UNSUPPORTED
+
+
+def test_ragged_step_validates_before_any_launch(L):
+    """The ragged extend entry point: a dense extend config only (q_len > 8
+    bounding every segment), a cu_seqlens_q array, and total_q within
+    0..B*q_len, all checked on the host with no launch; an empty batch is a
+    no-op."""
+    P = ctypes.c_void_p
+    ext = ga.mi355x_gated_attn_prepare(cfg(batch=4, q_len=64, window=0))
+    dec = ga.mi355x_gated_attn_prepare(cfg(batch=4, q_len=8, window=0))
+    empty = ga.mi355x_gated_attn_prepare(cfg(batch=0, q_len=64, window=0))
+    try:
+        ws, _ = ga.mi355x_gated_attn_plan(ext, 5000, 0)
+        ga.mi355x_gated_attn_plan(dec, 5000, 0)
+
+        def call(ctx, cu=P(0x4000), total=100):
+            return L.mi355x_gated_attn_ragged_step(
+                ctx, P(0x1000), P(0x2000), P(0x3000), cu, total, P(0x5000), P(0x6000),
+                P(0x10000), P(0x20000), P(0x7000), P(0x8000), P(0x9000), P(0x100000), ws, None)
+        assert call(dec) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "q_len" in ga.mi355x_gated_attn_last_error()
+        assert call(ext, cu=None) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "cu_seqlens_q" in ga.mi355x_gated_attn_last_error()
+        assert call(ext, total=-1) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert call(ext, total=4 * 64 + 1) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "total_q" in ga.mi355x_gated_attn_last_error()
+        assert call(empty) == ga.MI355X_GA_OK
+        assert L.mi355x_gated_attn_ragged_step(None, *([None] * 4), 0, *([None] * 8), 0, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+    finally:
+        for c in (ext, dec, empty):
+            ga.mi355x_gated_attn_destroy(c)

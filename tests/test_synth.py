@@ -59,3 +59,39 @@ def test_identity_table_for_the_tiny_workload():
     x = synth.make_inputs(synth.WORKLOADS["tiny_decode"])
     np.testing.assert_array_equal(x.page_table[0, :513], np.arange(513))
     assert x.cache_loc[0] == 512 and x.positions[0] == 512
+
+
+def test_ragged_batch_cut_and_its_reference():
+    """synth.ragged keeps each request's first lens[b] tokens with their own
+    positions, cache rows and projection rows, and cache_seqlens = seq_lens +
+    lens; the request-by-request oracle composition used for ragged parity
+    equals the oracle's batch step when every segment is at the bound, and a
+    request's rows equal a batch of that request alone at its length."""
+    from gpu_support import Reference, ragged_reference
+    w = synth.small(name="rg", batch=3, q_len=12, window=7, rope_theta=500000.0, page_size=4,
+                    seq_lo=20, seq_hi=60)
+    x = synth.make_inputs(w, seed=5)
+    lens = np.array([12, 5, 0], np.int32)
+    r = synth.ragged(x, lens)
+    assert r["total_q"] == 17 and list(r["cu_seqlens_q"]) == [0, 12, 17, 17]
+    assert list(r["cache_seqlens"]) == list(x.seq_lens + lens)
+    np.testing.assert_array_equal(r["positions"][12:], x.positions[12:17])
+    np.testing.assert_array_equal(r["qkv"][12:], x.qkv.reshape(36, -1)[12:17])
+    full = synth.ragged(x, np.full(3, 12, np.int32))
+    q, k, v, out = ragged_reference(x, full, [12, 12, 12])
+    ref = Reference(x)
+    np.testing.assert_array_equal(q, ref.q)
+    np.testing.assert_array_equal(k, ref.k_cache)
+    np.testing.assert_array_equal(out, ref.outputs().reshape(36, -1))
+    # request 1 alone at length 5
+    w1 = synth.small(name="rg1", batch=1, q_len=5, window=7, rope_theta=500000.0, page_size=4,
+                     seq_lo=20, seq_hi=60)
+    x1 = synth.make_inputs(w1, seed=5, seq_lens=x.seq_lens[1:2])
+    x1.qkv = np.ascontiguousarray(x.qkv[1:2, :5])
+    x1.page_table = np.ascontiguousarray(x.page_table[1:2])
+    x1.positions = np.ascontiguousarray(x.positions[12:17])
+    x1.cache_loc = np.ascontiguousarray(x.cache_loc[12:17])
+    x1.k_cache, x1.v_cache = x.k_cache, x.v_cache
+    x1.max_pages, x1.num_pages = x.max_pages, x.num_pages
+    _, _, _, out_r = ragged_reference(x, r, lens)
+    np.testing.assert_array_equal(out_r[12:], Reference(x1).outputs().reshape(5, -1))
