@@ -115,6 +115,30 @@ def extend_flops(w, cache_seqlens):
     return f, f
 
 
+def ragged_accounting(w, x, lens):
+    """A ragged batch (request b keeps lens[b] new tokens, cached length
+    seq_lens[b] + lens[b]): KV bytes (the union of each request's visible
+    keys), the step's algorithmic bytes as for the uniform step, and the
+    attention's flops (QK^T, PV)."""
+    import numpy as np
+    per_token = (w.width * 2 + 2 * w.num_kv_heads * w.head_dim
+                 + w.num_q_heads * w.head_dim * 2 + 16)
+    keys = pages = rows = 0
+    for sl, n in zip(x.seq_lens.tolist(), lens.tolist()):
+        if n == 0:
+            continue
+        cs = sl + n
+        first = max(0, cs - n - w.window + 1) if w.window > 0 else 0
+        keys += cs - first
+        pages += (cs - 1) // w.page_size - first // w.page_size + 1
+        p = np.arange(cs - n, cs, dtype=np.int64)
+        vis = np.minimum(p + 1, w.window) if w.window > 0 else p + 1
+        rows += int(vis.sum())
+    kv = keys * w.num_kv_heads * w.head_dim * 2
+    f = 2 * w.head_dim * rows * w.num_q_heads
+    return kv, kv + 4 * pages + int(lens.sum()) * per_token, f, f
+
+
 def mfma_peak(f_fp8: float, f_f16: float) -> float:
     """The matrix cores' peak for this mix: both products at their own dtype's
     dense peak, back to back (TFLOP/s)."""
@@ -414,6 +438,18 @@ def main():
     w = synth.WORKLOADS[args.workload]
     x0 = synth.make_inputs(w)
     kv_bytes, step_bytes = algorithmic_bytes(w, x0)
+    # Page 2's ragged prefill batch: each request keeps its first lens[b] new
+    # tokens, packed (ragged_step); the layers' rows are cut the same way.
+    ragged = None
+    if w.ragged_lo > 0:
+        lens = synth.ragged_lens(w)
+        r0 = synth.ragged(x0, lens)
+        kv_bytes, step_bytes, rf8, rf16 = ragged_accounting(w, x0, lens)
+        idx = np.concatenate([b * w.q_len + np.arange(int(n)) for b, n in enumerate(lens)])
+        ragged = dict(lens=lens, total=r0["total_q"], idx=torch.from_numpy(idx).to(dev),
+                      cu=torch.from_numpy(r0["cu_seqlens_q"]).to(dev),
+                      cs=torch.from_numpy(r0["cache_seqlens"]).to(dev),
+                      pos=torch.from_numpy(r0["positions"]).to(dev))
     pool_bytes = x0.k_cache.nbytes + x0.v_cache.nbytes + (0 if args.shared_table else x0.page_table.nbytes)
     n_layers = layer_pool_count(step_bytes, pool_bytes, args.cold_bytes * (1 << 30))
     print(f"[bench] {w.name}: B={w.batch} L={w.q_len} W={w.window} P={w.page_size}; "
@@ -464,6 +500,11 @@ def main():
         cl = (pt.gather(1, pos_b // P).to(torch.int64) * P + pos_b % P).reshape(-1).contiguous()
         out = torch.empty((w.batch, w.q_len, w.num_q_heads * w.head_dim), dtype=torch.int16,
                           device=dev)
+        if ragged is not None:  # the packed rows of the kept tokens
+            qkv = qkv.view(w.batch * w.q_len, w.width)[ragged["idx"]].contiguous()
+            cl = cl[ragged["idx"]].contiguous()
+            out = torch.empty((ragged["total"], w.num_q_heads * w.head_dim), dtype=torch.int16,
+                              device=dev)
         layers.append(dict(qkv=qkv, cache_loc=cl, page_table=pt, k_cache=kc, v_cache=vc, out=out))
     torch.cuda.synchronize()
 
@@ -473,6 +514,11 @@ def main():
 
     def run(li, stream=None):
         L_ = layers[li]
+        if ragged is not None:
+            step.ragged(L_["qkv"], ragged["pos"], L_["cache_loc"], ragged["cu"], ragged["total"],
+                        ragged["cs"], L_["page_table"], L_["k_cache"], L_["v_cache"], k_scale,
+                        v_scale, L_["out"], stream)
+            return
         if block_idx is not None:
             step.sparse(L_["qkv"], positions, L_["cache_loc"], cache_seqlens, L_["page_table"],
                         block_idx, L_["k_cache"], L_["v_cache"], k_scale, v_scale, L_["out"], stream)
@@ -558,7 +604,7 @@ def main():
     achieved = step_bytes / (us_step * 1e-6) / 1e9
     traffic = load_traffic(w.name)
     if extend:
-        f8, f16 = extend_flops(w, x0.cache_seqlens)
+        f8, f16 = (rf8, rf16) if ragged is not None else extend_flops(w, x0.cache_seqlens)
         peak = mfma_peak(f8, f16)
         achieved_tf = (f8 + f16) / (kernel_us * 1e-6) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": round(peak, 1),
@@ -607,8 +653,13 @@ def main():
     }
     if extend:
         result["kernel_us"] = round(kernel_us, 3)  # the attention launch; the step has two
-        result["tokens_per_s"] = round(x0.tokens / (us_step * 1e-6), 1)
-    if not args.no_cpu_baseline and extend:
+        n_tok = ragged["total"] if ragged is not None else x0.tokens
+        result["tokens_per_s"] = round(n_tok / (us_step * 1e-6), 1)
+        if ragged is not None:
+            result["config"]["segments"] = [int(n) for n in ragged["lens"]]
+    if not args.no_cpu_baseline and ragged is not None:
+        pass  # the oracle's extend sample is for uniform batches; none for ragged ones
+    elif not args.no_cpu_baseline and extend:
         est, sample = cpu_baseline_extend(x0, args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(kv_bytes / est / 1e9, 6), "unit": "GB/s",
                                   "cores": 1, "kind": "oracle", "sample": sample}

@@ -42,6 +42,7 @@ class Workload:
     sm_scale: float = 0.125
     spare_pages: int = 0   # pool pages no request references
     seed: int = 0
+    ragged_lo: int = 0     # > 0: a ragged batch, request b keeping ragged_lens(w)[b] new tokens
 
     @property
     def width(self) -> int:
@@ -95,6 +96,10 @@ EXTEND = {
     # a speculative block just past the verify kernel's 8 tokens over a long
     # full-attention context: 8 units, so the plan splits their keys
     "verify16_32k": Workload("verify16_32k", 4, 16, 32768, 32768, 0, 0.0, seed=1011),
+    # page 2's ragged prefill batch: 8 requests keeping 1..1,024 new tokens each
+    # (seeded, uniform) over an 8k-16k prefix, page 1's window and RoPE
+    "ragged_extend": Workload("ragged_extend", 8, 1024, 8192, 16384, 2048, 500000.0,
+                              ragged_lo=1, seed=1012),
 }
 WORKLOADS.update(EXTEND)
 
@@ -192,6 +197,12 @@ def make_inputs(w: Workload, seed: int | None = None, seq_lens: np.ndarray | Non
                   k_cache=k_cache, v_cache=v_cache, k_scale=float(w.kv_scale),
                   v_scale=float(w.kv_scale), max_pages=int(max_pages), num_pages=num_pages,
                   extra=extra)
+
+
+def ragged_lens(w: Workload) -> np.ndarray:
+    """Segment lengths of a ragged workload: uniform in [ragged_lo, q_len], seeded."""
+    rng = np.random.default_rng(w.seed + 1)
+    return rng.integers(w.ragged_lo, w.q_len, size=w.batch, endpoint=True).astype(np.int32)
 
 
 def ragged(x: Inputs, lens: np.ndarray) -> dict:

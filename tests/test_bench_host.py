@@ -111,3 +111,20 @@ def test_mfma_peak_of_the_mix():
 def test_extend_workloads_use_their_own_counter_files():
     assert bench.counters_file("swa_extend").endswith("extend_attn_swa_extend_counters.md")
     assert bench.counters_file("swa_decode").endswith("fused_step_swa_decode_counters.md")
+
+
+def test_ragged_accounting_reduces_to_the_uniform_one():
+    """With every segment at the bound, the ragged batch's KV bytes, step bytes
+    and flops are the uniform step's; shorter segments count only their own
+    tokens, keys and rows."""
+    import numpy as np
+    w = synth.small(name="acct", batch=3, q_len=40, window=30, rope_theta=500000.0, page_size=4,
+                    seq_lo=50, seq_hi=200)
+    x = synth.make_inputs(w, seed=3)
+    kv, step_b, f8, f16 = bench.ragged_accounting(w, x, np.full(3, 40, np.int32))
+    assert (kv, step_b) == bench.algorithmic_bytes(w, x)
+    assert (f8, f16) == bench.extend_flops(w, x.cache_seqlens)
+    kv1, step1, g8, _ = bench.ragged_accounting(w, x, np.array([40, 0, 0], np.int32))
+    s = int(x.seq_lens[0])
+    assert kv1 == (s + 40 - max(0, s - 30 + 1)) * 2 * 64 * 2
+    assert g8 == 2 * 64 * 16 * sum(min(p + 1, 30) for p in range(s, s + 40))
