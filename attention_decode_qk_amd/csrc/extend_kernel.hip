@@ -156,16 +156,53 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // chip) the order is (request, split, tile, KV head); split ks of a unit
   // walks its share of the unit's 64-key stages.
   const int S = p.splits;
-  const int n_units = p.batch * n_tiles * kKvHeads;
-  const int n_wg = n_units * S;
-  const int per_xcd = (n_wg + kXcds - 1) / kXcds;
-  const int li = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
-  if (li >= n_wg) return;
-  const int g = li % kKvHeads;
-  const int tile = (li / kKvHeads) % n_tiles;
-  const int ks = (li / (kKvHeads * n_tiles)) % S, b = li / (kKvHeads * n_tiles * S);
-  const int unit = (b * n_tiles + tile) * kKvHeads + g;
   const int tid = threadIdx.x, lane = tid & 63;
+  int g, tile, ks, b;
+  if (p.cu_seqlens_q && p.batch <= 64) {
+    // A ragged batch of at most 64 requests: only the tiles that hold rows get
+    // workgroups, in the same order, so every XCD takes an equal share of them
+    // whatever the segments' lengths (in the padded order a request's tiles,
+    // rows or not, fill one XCD).  Two scalar passes over the segments: their
+    // tile count, then the request holding workgroup li (empty segments hold
+    // none and are passed over).
+    auto seg_tiles = [&](int r) {
+      const int n = p.cu_seqlens_q[r + 1] - p.cu_seqlens_q[r];
+      return (max(0, min(n, L)) + kExtTile - 1) / kExtTile;
+    };
+    int tot = 0;
+    for (int r = 0; r < p.batch; ++r) tot += seg_tiles(r);
+    const int n_wg = tot * kKvHeads * S;
+    const int per_xcd = (n_wg + kXcds - 1) / kXcds;
+    const int kx = (int)(blockIdx.x / kXcds);  // the grid holds the padded order's count
+    if (kx >= per_xcd) return;
+    const int li = (int)(blockIdx.x % kXcds) * per_xcd + kx;
+    if (li >= n_wg) return;
+    int first = 0, tb = 0;
+    b = 0;
+    for (int r = 0; r < p.batch; ++r) {
+      tb = seg_tiles(r);
+      const int u = tb * kKvHeads * S;
+      if (li < first + u) {
+        b = r;
+        break;
+      }
+      first += u;
+    }
+    const int rr = li - first;
+    g = rr % kKvHeads;
+    tile = (rr / kKvHeads) % tb;
+    ks = rr / (kKvHeads * tb);
+  } else {
+    const int n_wg = p.batch * n_tiles * kKvHeads * S;
+    const int per_xcd = (n_wg + kXcds - 1) / kXcds;
+    const int li = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    if (li >= n_wg) return;
+    g = li % kKvHeads;
+    tile = (li / kKvHeads) % n_tiles;
+    ks = (li / (kKvHeads * n_tiles)) % S;
+    b = li / (kKvHeads * n_tiles * S);
+  }
+  const int unit = (b * n_tiles + tile) * kKvHeads + g;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
   const int kg = wave >> 2, wq = wave & 3;  // key group; the wave's rows within the tile
   const int j = lane & 15, q4 = lane >> 4;

@@ -147,3 +147,17 @@ def test_ragged_graph_replay_matches_eager():
     assert_outputs_close(eager.cpu().numpy().view(np.uint16), out_ref, "ragged graph")
     assert_codes_match(kc.cpu().numpy(), k_ref, T * 128, "ragged graph k_cache")
     step.close()
+
+
+@pytest.mark.parametrize("batch", [64, 65])
+def test_ragged_many_requests(batch):
+    """Up to 64 requests deal only the tiles that hold rows over the XCDs (a
+    lane per request); 65 keep the padded order.  Many empty and one-token
+    segments among longer ones."""
+    rng = np.random.default_rng(batch)
+    lens = rng.choice([0, 1, 5, 16, 17, 33, 40], size=batch).astype(np.int32)
+    w = synth.small(name="ragged_many", batch=batch, q_len=40, window=64, rope_theta=500000.0,
+                    seq_lo=20, seq_hi=300, page_size=4)
+    x = synth.make_inputs(w, seed=1600 + batch)
+    _say(f"[gpu] ragged many requests B={batch} tokens={int(lens.sum())}")
+    _run(x, lens, what=f"ragged B={batch}")
