@@ -26,7 +26,7 @@ EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_g
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
             "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta",
             "mi355x_qk_norm_supports", "mi355x_qk_norm", "mi355x_gated_attn_sparse_step",
-            "mi355x_gated_attn_ragged_step"]
+            "mi355x_gated_attn_ragged_step", "mi355x_gated_attn_sparse_prefill_step"]
 
 MI355X_QKN_BF16 = 0
 MI355X_QKN_FP16 = 1
@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_step_meta.argtypes = [P] * 7
         L.mi355x_gated_attn_sparse_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
+        L.mi355x_gated_attn_sparse_prefill_step.argtypes = [P] * 5 + [ctypes.c_int32] + \
+            [P] * 9 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_ragged_step.argtypes = [P] * 5 + [ctypes.c_int64] + [P] * 8 + \
             [ctypes.c_size_t, P]
         L.mi355x_gated_attn_destroy.argtypes = [P]
@@ -207,6 +209,31 @@ def mi355x_gated_attn_ragged_step(ctx, qkv, positions, cache_loc, cu_seqlens_q, 
         _ptr(v_scale), _ptr(out), _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
 
 
+def mi355x_gated_attn_sparse_prefill_step(ctx, qkv, positions, cache_loc, token_req,
+                                          num_requests: int, cache_seqlens, page_table,
+                                          block_idx, k_cache, v_cache, k_scale, v_scale, out,
+                                          workspace, stream=None):
+    """Launch one page-list-driven prefill: the config's batch is the number of
+    queries; token_req (int32 [batch]) names each query's page-table row,
+    cache_seqlens (int32 [batch]) is each query's position + 1, block_idx is
+    int32 [Hkv, batch, topk]; otherwise as mi355x_gated_attn_sparse_step."""
+    import torch
+    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, token_req=token_req,
+                   cache_seqlens=cache_seqlens, page_table=page_table, block_idx=block_idx,
+                   k_cache=k_cache, v_cache=v_cache, out=out, workspace=workspace)
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous device tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_sparse_prefill_step(
+        ctx, _ptr(qkv), _ptr(positions), _ptr(cache_loc), _ptr(token_req), int(num_requests),
+        _ptr(cache_seqlens), _ptr(page_table), _ptr(block_idx), _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), _ptr(out), _ptr(workspace), _nbytes(workspace),
+        ctypes.c_void_p(handle)))
+
+
 def mi355x_gated_attn_step_meta(ctx, seq_lens, page_table, positions, cache_loc, cache_seqlens,
                                 stream=None):
     """Build a step's positions, cache rows and key counts on the device (int32
@@ -283,6 +310,16 @@ class GatedAttnStep:
         mi355x_gated_attn_sparse_step(self.ctx, qkv, positions, cache_loc, cache_seqlens,
                                       page_table, block_idx, k_cache, v_cache, k_scale, v_scale,
                                       out, self.workspace, stream)
+        return out
+
+    def sparse_prefill(self, qkv, positions, cache_loc, token_req, num_requests, cache_seqlens,
+                       page_table, block_idx, k_cache, v_cache, k_scale, v_scale, out,
+                       stream=None):
+        """One page-list-driven prefill (a sparse config whose batch counts queries)."""
+        mi355x_gated_attn_sparse_prefill_step(self.ctx, qkv, positions, cache_loc, token_req,
+                                              num_requests, cache_seqlens, page_table, block_idx,
+                                              k_cache, v_cache, k_scale, v_scale, out,
+                                              self.workspace, stream)
         return out
 
     def ragged(self, qkv, positions, cache_loc, cu_seqlens_q, total_q, cache_seqlens, page_table,

@@ -333,7 +333,8 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
              const int64_t* cache_loc, const int32_t* cache_seqlens, const int32_t* page_table,
              const int32_t* block_idx, void* k_cache, void* v_cache, const float* k_scale,
              const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
-             const int32_t* cu_seqlens_q = nullptr, int64_t total_q = -1) {
+             const int32_t* cu_seqlens_q = nullptr, int64_t total_q = -1,
+             const int32_t* token_req = nullptr, int32_t pt_rows = 0) {
   if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
   if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
   const auto& c = ctx->cfg;
@@ -399,6 +400,8 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   sp.sparse_topk = c.sparse_topk;
   sp.cu_seqlens_q = cu_seqlens_q;
   sp.total_q = cu_seqlens_q ? total_q : (int64_t)c.batch * c.q_len;
+  sp.token_req = token_req;
+  sp.pt_rows = pt_rows;
   std::memcpy(sp.inv_freq, ctx->inv_freq, sizeof sp.inv_freq);
 
   hipEvent_t* ev = nullptr;
@@ -421,6 +424,9 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   // second launch of an extend step.
   const bool extend = c.q_len > kMaxQLen;
   if (ev && !extend) e = hipEventRecord(ev[0], st);
+  // Sparse prefill: every query's K/V row is stored before any query reads
+  // the cache (its own row included), as the extend path does.
+  if (e == hipSuccess && token_req) e = launch_extend_prologue(sp, st);
   if (e == hipSuccess) e = launch_step(sp, st, ev && extend ? ev[0] : nullptr);
   if (e == hipSuccess && ev) e = hipEventRecord(ev[1], st);
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
@@ -462,6 +468,27 @@ int mi355x_gated_attn_ragged_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
   return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, nullptr, k_cache,
                   v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream, cu_seqlens_q,
                   total_q);
+}
+
+int mi355x_gated_attn_sparse_prefill_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                          const int64_t* positions, const int64_t* cache_loc,
+                                          const int32_t* token_req, int32_t num_requests,
+                                          const int32_t* cache_seqlens, const int32_t* page_table,
+                                          const int32_t* block_idx, void* k_cache, void* v_cache,
+                                          const float* k_scale, const float* v_scale, void* out,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  const auto& c = ctx->cfg;
+  if (c.batch == 0) return ok();
+  if (c.sparse_block == 0)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "sparse_prefill_step on a dense config (sparse_block 0)");
+  if (!token_req || !block_idx)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "token_req or block_idx is NULL");
+  if (num_requests < 1)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "num_requests %d < 1", num_requests);
+  return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, block_idx, k_cache,
+                  v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream, nullptr, -1,
+                  token_req, num_requests);
 }
 
 int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,

@@ -544,6 +544,13 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
 
 }  // namespace
 
+hipError_t launch_extend_prologue(const StepParams& p, hipStream_t stream) {
+  if (p.total_q <= 0) return hipSuccess;
+  const unsigned pro_grid = (unsigned)((p.total_q + kExtPrologueTokens - 1) / kExtPrologueTokens);
+  hipLaunchKernelGGL(extend_prologue_kernel, dim3(pro_grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t attn_start) {
   if (p.batch == 0) return hipSuccess;
   if (p.sparse_block > 0 || p.q_len <= kMaxQLen || p.q_len > kMaxExtendLen ||

@@ -80,6 +80,9 @@ struct StepParams {
   const int32_t* cu_seqlens_q;   // ragged extend: [B+1], request b's tokens cu[b] .. cu[b+1]-1 (at most
                                  // q_len each); null: b*q_len .. (b+1)*q_len-1
   int64_t total_q;               // tokens of the step: cu[B] when ragged, else B*q_len
+  const int32_t* token_req;      // sparse prefill: [B] page-table row of each query (its request);
+                                 // null: query b uses row b
+  int32_t pt_rows;               // sparse prefill: rows of page_table (token_req is clamped to them)
   float inv_freq[kHeadDim / 2];
 };
 
@@ -89,6 +92,9 @@ hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_
 // The q_len > kMaxQLen path of launch_step (two launches: prologue, then
 // attention and epilogue; attn_start as above).
 hipError_t launch_extend(const StepParams& p, hipStream_t stream, hipEvent_t attn_start);
+// The extend path's prologue alone over p.total_q tokens: norm, RoPE, q e4m3 to
+// the workspace, the new K/V rows stored at cache_loc.
+hipError_t launch_extend_prologue(const StepParams& p, hipStream_t stream);
 
 // Per-head RMSNorm with an output scale (qk_norm_kernel.hip).
 struct QkNormParams {

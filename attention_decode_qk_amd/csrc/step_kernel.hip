@@ -249,7 +249,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   const int end = min(start + chunk, SP ? n : last + 1);
   const int nblk = end > start ? (end - start + kKeyBlock - 1) / kKeyBlock : 0;
   const int nb = nblk > kw ? (nblk - kw + KW - 1) / KW : 0;  // this wave's
-  const int32_t* pt = p.page_table + (int64_t)b * p.max_pages;
+  const int pt_row = SP && p.token_req ? min(max(p.token_req[b], 0), p.pt_rows - 1) : b;
+  const int32_t* pt = p.page_table + (int64_t)pt_row * p.max_pages;
   // Key of this lane in the wave's block i.  Blocks past the wave's last are
   // clamped to it, so the pipeline's loads are unconditional (which keeps the
   // compiler's memory-counter waits exact) and the extra ones hit cache lines

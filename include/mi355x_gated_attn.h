@@ -237,6 +237,38 @@ int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Page-list-driven (top-k block-sparse) prefill: page "msa.py"
+ * (msa_sparse_prefill_main: every new token of a chunk is a query with its
+ * own per-KV-head block list, topk_idx [Hkv, total_q, topk], causal with the
+ * prefix as query offset; block_size_k == page_size there).  Each of the
+ * config's `batch` queries is served as its own one-token step of
+ * mi355x_gated_attn_sparse_step, after every query's K/V row has been stored
+ * (a first launch runs the extend path's prologue over all of them):
+ *   query t of request r = token_req[t] sits at position positions[t] =
+ *   cache_seqlens[t] - 1, reads page_table row r, and attends, per KV head g,
+ *   to the keys of the blocks block_idx[(g * batch + t) * sparse_topk + i]
+ *   (-1 unused) below cache_seqlens[t]: the new tokens of the same chunk
+ *   before it included, those after it not (no window).
+ *   token_req      device int32 [batch], the page-table row of each query
+ *                  (clamped to 0..num_requests-1)
+ *   num_requests   host int32 >= 1, rows of page_table
+ *   cache_seqlens  device int32 [batch], per query: its position + 1
+ *   qkv, positions, cache_loc, out: per query ([batch, 1, ...]), as
+ *                  mi355x_gated_attn_step at q_len 1
+ * The config is a page-list-driven decode config (q_len 1, window 0,
+ * sparse_block > 0) whose batch is the number of queries.  INVALID_ARGUMENT
+ * for a dense config, a NULL token_req or block_idx, or num_requests < 1.
+ * Other arguments, ownership and effects as mi355x_gated_attn_sparse_step.
+ */
+int mi355x_gated_attn_sparse_prefill_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                          const int64_t* positions, const int64_t* cache_loc,
+                                          const int32_t* token_req, int32_t num_requests,
+                                          const int32_t* cache_seqlens, const int32_t* page_table,
+                                          const int32_t* block_idx, void* k_cache, void* v_cache,
+                                          const float* k_scale, const float* v_scale, void* out,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Ragged extend / prefill batch: page "msa.py" (msa_sparse_prefill_main:
  * per-request query segments given by cumulative lengths cu_seqlens,
  * qo_segment_lens = cu_seqlens[1:] - cu_seqlens[:-1], causal with the query

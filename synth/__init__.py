@@ -245,6 +245,24 @@ def make_block_lists(rng: np.random.Generator, cache_seqlens: np.ndarray, block_
     return out
 
 
+def sparse_prefill(x: Inputs, block_size: int, topk: int, seed: int) -> dict:
+    """Page-list-driven prefill inputs cut from uniform inputs x (B requests, L
+    new tokens each): every new token is a query of its own — token_req its
+    request, cache_seqlens its position + 1 — with per-KV-head block lists
+    drawn by make_block_lists at that length ([Hkv, B*L, topk]).  Also the
+    page table expanded to a row per query (page_table_q) for a plain batch of
+    one-token queries."""
+    B, L = x.w.batch, x.w.q_len
+    T = B * L
+    token_req = np.repeat(np.arange(B, dtype=np.int32), L)
+    cs = (x.positions + 1).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    return dict(qkv=np.ascontiguousarray(x.qkv.reshape(T, 1, -1)), positions=x.positions,
+                cache_loc=x.cache_loc, token_req=token_req, cache_seqlens=cs,
+                page_table_q=np.ascontiguousarray(x.page_table[token_req]),
+                block_idx=make_block_lists(rng, cs, block_size, topk, x.w.num_kv_heads))
+
+
 def small(name: str = "small", batch: int = 3, q_len: int = 1, seq_lo: int = 40, seq_hi: int = 300,
           window: int = 0, rope_theta: float = 0.0, page_size: int = 1, kv_scale: float = 1.0,
           qkv_std: float = 1.0, table: str = "perm", sm_scale: float = 0.125,

@@ -418,3 +418,30 @@ def test_ragged_step_validates_before_any_launch(L):
     finally:
         for c in (ext, dec, empty):
             ga.mi355x_gated_attn_destroy(c)
+
+
+def test_sparse_prefill_step_validates_before_any_launch(L):
+    """Page-list-driven prefill: a sparse config only, token_req and block_idx
+    present, at least one page-table row; an empty batch is a no-op."""
+    P = ctypes.c_void_p
+    sparse = ga.mi355x_gated_attn_prepare(cfg(batch=40, sparse_block=64, sparse_topk=4, window=0))
+    dense = ga.mi355x_gated_attn_prepare(cfg(batch=40, window=0))
+    empty = ga.mi355x_gated_attn_prepare(cfg(batch=0, sparse_block=64, sparse_topk=4, window=0))
+    try:
+        ws, _ = ga.mi355x_gated_attn_plan(sparse, 1 << 16, 0)
+        ga.mi355x_gated_attn_plan(dense, 1 << 16, 0)
+
+        def call(ctx, tr=P(0x4000), nreq=2, bi=P(0x6000)):
+            return L.mi355x_gated_attn_sparse_prefill_step(
+                ctx, P(0x1000), P(0x2000), P(0x3000), tr, nreq, P(0x5000), P(0x5800), bi,
+                P(0x10000), P(0x20000), P(0x7000), P(0x8000), P(0x9000), P(0x100000), ws, None)
+        assert call(dense) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "dense" in ga.mi355x_gated_attn_last_error()
+        assert call(sparse, tr=None) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert call(sparse, bi=None) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert call(sparse, nreq=0) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "num_requests" in ga.mi355x_gated_attn_last_error()
+        assert call(empty) == ga.MI355X_GA_OK
+    finally:
+        for c in (sparse, dense, empty):
+            ga.mi355x_gated_attn_destroy(c)
