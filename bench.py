@@ -47,9 +47,11 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}  # MI355X dense matrix-core pe
 
 
 def _is_extend(workload: str) -> bool:
+    """Whether the workload's dominant kernel is the extend attention kernel (a
+    block-sparse prefill's is the step kernel, whatever its chunk length)."""
     import synth
     w = synth.WORKLOADS.get(workload)
-    return w is not None and w.q_len > 8
+    return w is not None and w.q_len > 8 and w.prefill_block == 0
 
 
 def _kernel_prefix(workload: str) -> str:
@@ -137,6 +139,24 @@ def ragged_accounting(w, x, lens):
     kv = keys * w.num_kv_heads * w.head_dim * 2
     f = 2 * w.head_dim * rows * w.num_q_heads
     return kv, kv + 4 * pages + int(lens.sum()) * per_token, f, f
+
+
+def sparse_prefill_accounting(w, x, sp):
+    """Block-sparse prefill: per (KV head, query) the listed blocks' keys below
+    the query's cached length, each a half row (one KV head) of K and of V; the
+    listed blocks' page-table entries (one page per block) and the lists; per
+    token the projection row, K/V row stores, output row, position and cache row."""
+    import numpy as np
+    bi = sp["block_idx"].astype(np.int64)                  # [Hkv, T, topk]
+    cs = sp["cache_seqlens"].astype(np.int64)[None, :, None]
+    BS = w.prefill_block
+    keys = np.clip(cs - bi * BS, 0, BS) * (bi >= 0)
+    kv = int(keys.sum()) * w.head_dim * 2
+    pages = int(((keys > 0).sum()) * -(-BS // w.page_size))
+    per_token = (w.width * 2 + 2 * w.num_kv_heads * w.head_dim
+                 + w.num_q_heads * w.head_dim * 2 + 16)
+    lists = 4 * bi.size
+    return kv, kv + 4 * pages + lists + x.tokens * per_token
 
 
 def mfma_peak(f_fp8: float, f_f16: float) -> float:
@@ -440,6 +460,16 @@ def main():
     kv_bytes, step_bytes = algorithmic_bytes(w, x0)
     # Page 2's ragged prefill batch: each request keeps its first lens[b] new
     # tokens, packed (ragged_step); the layers' rows are cut the same way.
+    # Page 2's block-sparse prefill: every new token a one-token query of the
+    # block-sparse step (sparse_prefill_step), its list drawn at its position.
+    sprefill = None
+    if w.prefill_block > 0:
+        sp0 = synth.sparse_prefill(x0, w.prefill_block, w.prefill_topk, seed=w.seed + 2)
+        kv_bytes, step_bytes = sparse_prefill_accounting(w, x0, sp0)
+        sprefill = dict(token_req=torch.from_numpy(sp0["token_req"]).to(dev),
+                        cs=torch.from_numpy(sp0["cache_seqlens"]).to(dev),
+                        block_idx=torch.from_numpy(sp0["block_idx"]).to(dev),
+                        max_cs=int(sp0["cache_seqlens"].max()))
     ragged = None
     if w.ragged_lo > 0:
         lens = synth.ragged_lens(w)
@@ -459,7 +489,12 @@ def main():
     cfg = ga.make_config(w.batch, w.q_len, w.page_size, w.window, x0.max_pages, x0.num_pages,
                          w.rope_theta, w.sm_scale, w.kv_scale, q_scale=w.q_scale,
                          sparse_block=w.sparse_block, sparse_topk=w.sparse_topk)
-    step = ga.GatedAttnStep(cfg, int(w.seq_hi + w.q_len), args.splits)
+    if sprefill is not None:  # a sparse config whose batch counts the queries
+        cfg = ga.make_config(x0.tokens, 1, w.page_size, 0, x0.max_pages, x0.num_pages,
+                             w.rope_theta, w.sm_scale, w.kv_scale, q_scale=w.q_scale,
+                             sparse_block=w.prefill_block, sparse_topk=w.prefill_topk)
+    step = ga.GatedAttnStep(cfg, sprefill["max_cs"] if sprefill else int(w.seq_hi + w.q_len),
+                            args.splits)
 
     # Layer pools: pool 0 is the tests' seeded input; the others are drawn on
     # the device with the same recipe (own caches, page-table permutation and
@@ -500,6 +535,9 @@ def main():
         cl = (pt.gather(1, pos_b // P).to(torch.int64) * P + pos_b % P).reshape(-1).contiguous()
         out = torch.empty((w.batch, w.q_len, w.num_q_heads * w.head_dim), dtype=torch.int16,
                           device=dev)
+        if sprefill is not None:  # one-token queries
+            out = torch.empty((x0.tokens, 1, w.num_q_heads * w.head_dim), dtype=torch.int16,
+                              device=dev)
         if ragged is not None:  # the packed rows of the kept tokens
             qkv = qkv.view(w.batch * w.q_len, w.width)[ragged["idx"]].contiguous()
             cl = cl[ragged["idx"]].contiguous()
@@ -514,6 +552,12 @@ def main():
 
     def run(li, stream=None):
         L_ = layers[li]
+        if sprefill is not None:
+            step.sparse_prefill(L_["qkv"].view(x0.tokens, 1, w.width), positions, L_["cache_loc"],
+                                sprefill["token_req"], w.batch, sprefill["cs"], L_["page_table"],
+                                sprefill["block_idx"], L_["k_cache"], L_["v_cache"], k_scale,
+                                v_scale, L_["out"], stream)
+            return
         if ragged is not None:
             step.ragged(L_["qkv"], ragged["pos"], L_["cache_loc"], ragged["cu"], ragged["total"],
                         ragged["cs"], L_["page_table"], L_["k_cache"], L_["v_cache"], k_scale,
@@ -600,7 +644,7 @@ def main():
     # average duration over the timed region (rocprofv3's kernel trace agrees).
     # An extend step is two launches: its roofline takes the attention kernel's
     # event-timed duration (the hook brackets that launch alone).
-    extend = w.q_len > 8
+    extend = w.q_len > 8 and sprefill is None
     achieved = step_bytes / (us_step * 1e-6) / 1e9
     traffic = load_traffic(w.name)
     if extend:
@@ -657,8 +701,12 @@ def main():
         result["tokens_per_s"] = round(n_tok / (us_step * 1e-6), 1)
         if ragged is not None:
             result["config"]["segments"] = [int(n) for n in ragged["lens"]]
-    if not args.no_cpu_baseline and ragged is not None:
-        pass  # the oracle's extend sample is for uniform batches; none for ragged ones
+    if sprefill is not None:
+        result["tokens_per_s"] = round(x0.tokens / (us_step * 1e-6), 1)
+        result["config"]["prefill_block"] = w.prefill_block
+        result["config"]["prefill_topk"] = w.prefill_topk
+    if not args.no_cpu_baseline and (ragged is not None or sprefill is not None):
+        pass  # the sampled oracle baselines are written for uniform batches
     elif not args.no_cpu_baseline and extend:
         est, sample = cpu_baseline_extend(x0, args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(kv_bytes / est / 1e9, 6), "unit": "GB/s",

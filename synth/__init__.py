@@ -43,6 +43,8 @@ class Workload:
     spare_pages: int = 0   # pool pages no request references
     seed: int = 0
     ragged_lo: int = 0     # > 0: a ragged batch, request b keeping ragged_lens(w)[b] new tokens
+    prefill_block: int = 0  # > 0: block-sparse prefill (page "msa.py") over blocks of this many keys
+    prefill_topk: int = 0   # blocks each query's list selects per KV head
 
     @property
     def width(self) -> int:
@@ -100,6 +102,11 @@ EXTEND = {
     # (seeded, uniform) over an 8k-16k prefix, page 1's window and RoPE
     "ragged_extend": Workload("ragged_extend", 8, 1024, 8192, 16384, 2048, 500000.0,
                               ragged_lo=1, seed=1012),
+    # page 2's block-sparse prefill: 2 requests x 1,024 new tokens over 8k-16k
+    # prefixes, every token a query selecting 16 blocks of 128 keys (one page
+    # each) per KV head, no window, no RoPE
+    "sparse_prefill": Workload("sparse_prefill", 2, 1024, 8192, 16384, 0, 0.0, page_size=128,
+                               prefill_block=128, prefill_topk=16, seed=1013),
 }
 WORKLOADS.update(EXTEND)
 

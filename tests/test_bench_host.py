@@ -128,3 +128,25 @@ def test_ragged_accounting_reduces_to_the_uniform_one():
     s = int(x.seq_lens[0])
     assert kv1 == (s + 40 - max(0, s - 30 + 1)) * 2 * 64 * 2
     assert g8 == 2 * 64 * 16 * sum(min(p + 1, 30) for p in range(s, s + 40))
+
+
+def test_sparse_prefill_accounting_counts_the_listed_keys():
+    """Block-sparse prefill: KV bytes are, per (KV head, query), the keys of its
+    listed blocks below its cached length, a 64-byte half row of K and of V
+    each (brute force over the lists)."""
+    import dataclasses
+    w = dataclasses.replace(synth.small(name="spacct", batch=2, q_len=6, window=0, page_size=32,
+                                        seq_lo=40, seq_hi=200),
+                            prefill_block=32, prefill_topk=3)
+    x = synth.make_inputs(w, seed=4)
+    sp = synth.sparse_prefill(x, 32, 3, seed=9)
+    kv, step_b = bench.sparse_prefill_accounting(w, x, sp)
+    keys = 0
+    for g in range(2):
+        for t in range(x.tokens):
+            cs = int(sp["cache_seqlens"][t])
+            for j in sp["block_idx"][g, t].tolist():
+                if j >= 0:
+                    keys += len([k for k in range(32 * j, 32 * j + 32) if k < cs])
+    assert kv == keys * 64 * 2
+    assert step_b > kv
