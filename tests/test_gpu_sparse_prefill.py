@@ -82,3 +82,44 @@ def test_sparse_prefill_matches_oracle(name):
     assert_codes_match(vc.cpu().numpy(), v_ref, written, name + " v_cache")
     assert_outputs_close(out.cpu().numpy().view(np.uint16), o_ref, name + " out")
     step.close()
+
+
+def test_sparse_prefill_graph_replay_matches_eager():
+    """The prefill's two launches captured in a HIP graph and replayed three
+    times with eager work between: every replay equals the eager step."""
+    block, topk = 64, 4
+    w = synth.small(name="sp_graph", batch=2, q_len=24, window=0, seq_lo=100, seq_hi=600,
+                    page_size=8, rope_theta=500000.0)
+    x = synth.make_inputs(w, seed=1900)
+    sp = synth.sparse_prefill(x, block, topk, seed=1901)
+    T = x.tokens
+    cfg = ga.make_config(T, 1, w.page_size, 0, x.max_pages, x.num_pages, w.rope_theta,
+                         w.sm_scale, w.kv_scale, sparse_block=block, sparse_topk=topk)
+    step = ga.GatedAttnStep(cfg, int(sp["cache_seqlens"].max()), 2)
+    args = [_t(sp["qkv"].view(np.int16)), _t(sp["positions"]), _t(sp["cache_loc"]),
+            _t(sp["token_req"]), w.batch, _t(sp["cache_seqlens"]), _t(x.page_table),
+            _t(sp["block_idx"])]
+    kc, vc = _t(x.k_cache), _t(x.v_cache)
+    ks = torch.tensor([x.k_scale], dtype=torch.float32, device=DEV)
+    vs = torch.tensor([x.v_scale], dtype=torch.float32, device=DEV)
+    eager = torch.zeros((T, 1, 1024), dtype=torch.int16, device=DEV)
+    _say("[gpu] sparse prefill graph replay")
+    step.sparse_prefill(*args, kc, vc, ks, vs, eager)
+    torch.cuda.synchronize()
+    out = torch.zeros_like(eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            step.sparse_prefill(*args, kc, vc, ks, vs, out, stream=s)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.zero_()
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+        del junk
+    step.close()
