@@ -115,10 +115,85 @@ def mi355x_gated_attn_supports(cfg: Config) -> int:
     return lib().mi355x_gated_attn_supports(ctypes.byref(cfg))
 
 
+# The configuration and device of every live context, so that the launch
+# wrappers can check each tensor against them before the C ABI sees a pointer.
+_CTX = {}
+
+
 def mi355x_gated_attn_prepare(cfg: Config, device: int = 0) -> ctypes.c_void_p:
     ctx = ctypes.c_void_p()
     _check(lib().mi355x_gated_attn_prepare(ctypes.byref(cfg), device, ctypes.byref(ctx)))
+    _CTX[ctx.value] = (Config.from_buffer_copy(cfg), int(device))
     return ctx
+
+
+def _ctx_key(ctx):
+    return ctx.value if isinstance(ctx, ctypes.c_void_p) else ctx
+
+
+def _dt(*names):
+    import torch
+    return tuple(getattr(torch, n) for n in names if hasattr(torch, n))
+
+
+def _check_tensors(specs, device):
+    """specs: (name, tensor, dtypes, numel, min_numel, required) per argument.
+    Presence, dtype and size of every tensor are checked first, then device
+    and layout (so that a wrong dtype or size is named even on the host);
+    raises ValueError naming the argument."""
+    for name, t, dtypes, numel, min_numel, required in specs:
+        if t is None:
+            if required:
+                raise ValueError(f"{name} is required")
+            continue
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name}: dtype {t.dtype} is not one of "
+                             f"{', '.join(str(d) for d in dtypes)}")
+        if numel is not None and t.numel() != numel:
+            raise ValueError(f"{name}: {t.numel()} elements, the configuration needs {numel}")
+        if min_numel is not None and t.numel() < min_numel:
+            raise ValueError(f"{name}: {t.numel()} elements, the configuration needs at least "
+                             f"{min_numel}")
+    for name, t, *_ in specs:
+        if t is None:
+            continue
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if device is not None and t.device.index != device:
+            raise ValueError(f"{name} is on cuda:{t.device.index}, the context on cuda:{device}")
+
+
+def _ctx_entry(ctx):
+    entry = _CTX.get(_ctx_key(ctx))
+    if entry is None:
+        raise ValueError("unknown or destroyed context")
+    return entry
+
+
+def _step_specs(c, tokens, qkv, positions, cache_loc, cache_seqlens, page_table, k_cache, v_cache,
+                k_scale, v_scale, out, workspace, page_rows=None, seq_lens=None):
+    """Specs of the tensors every step variant takes, against config c: tokens =
+    the step's new tokens (B*L, or total_q for a ragged batch), page_rows = rows
+    of page_table (B unless stated)."""
+    two = _dt("bfloat16", "int16", "uint16")
+    one = _dt("uint8", "int8", "float8_e4m3fn")
+    i32, i64, f32 = _dt("int32"), _dt("int64"), _dt("float32")
+    width = (2 * c.num_q_heads + 2 * c.num_kv_heads) * c.head_dim
+    rows = c.batch if page_rows is None else page_rows
+    cache = c.num_pages * c.page_size * c.num_kv_heads * c.head_dim
+    scaled = c.kv_scale != 1.0
+    return [("qkv", qkv, two, tokens * width, None, True),
+            ("positions", positions, i64, tokens, None, c.rope_theta != 0.0),
+            ("cache_loc", cache_loc, i64, tokens, None, True),
+            ("cache_seqlens", cache_seqlens, i32, c.batch, None, True),
+            ("page_table", page_table, i32, rows * c.max_pages, None, True),
+            ("seq_lens", seq_lens, i32, c.batch, None, False),
+            ("k_cache", k_cache, one, None, cache, True),
+            ("v_cache", v_cache, one, None, cache, True),
+            ("k_scale", k_scale, f32, 1, None, scaled),
+            ("v_scale", v_scale, f32, 1, None, scaled),
+            ("out", out, two, tokens * c.num_q_heads * c.head_dim, None, True),
+            ("workspace", workspace, _dt("uint8", "int8"), None, None, True)]
 
 
 def mi355x_gated_attn_plan(ctx, max_context: int, num_splits: int = 0):
@@ -150,12 +225,12 @@ def mi355x_gated_attn_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_t
     workspace); `stream` is a torch stream, a raw handle, or None for torch's
     current stream."""
     import torch
-    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, cache_seqlens=cache_seqlens,
-                   page_table=page_table, k_cache=k_cache, v_cache=v_cache, out=out,
-                   workspace=workspace)
-    for name, t in tensors.items():
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    _check_tensors(_step_specs(c, c.batch * c.q_len, qkv, positions, cache_loc, cache_seqlens,
+                               page_table, k_cache, v_cache, k_scale, v_scale, out, workspace,
+                               seq_lens=seq_lens), dev)
     if stream is None:
         stream = torch.cuda.current_stream(qkv.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -171,12 +246,14 @@ def mi355x_gated_attn_sparse_step(ctx, qkv, positions, cache_loc, cache_seqlens,
     """Launch one page-list-driven decode step (block_idx: contiguous int32
     device tensor [Hkv, B, topk], -1 padded); otherwise as mi355x_gated_attn_step."""
     import torch
-    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, cache_seqlens=cache_seqlens,
-                   page_table=page_table, block_idx=block_idx, k_cache=k_cache, v_cache=v_cache,
-                   out=out, workspace=workspace)
-    for name, t in tensors.items():
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    specs = _step_specs(c, c.batch * c.q_len, qkv, positions, cache_loc, cache_seqlens, page_table,
+                        k_cache, v_cache, k_scale, v_scale, out, workspace)
+    specs.append(("block_idx", block_idx, _dt("int32"), c.num_kv_heads * c.batch * c.sparse_topk,
+                  None, True))
+    _check_tensors(specs, dev)
     if stream is None:
         stream = torch.cuda.current_stream(qkv.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -194,12 +271,15 @@ def mi355x_gated_attn_ragged_step(ctx, qkv, positions, cache_loc, cu_seqlens_q, 
     [B+1]) of the packed qkv / positions / cache_loc / out, total_q of them;
     otherwise as mi355x_gated_attn_step."""
     import torch
-    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, cu_seqlens_q=cu_seqlens_q,
-                   cache_seqlens=cache_seqlens, page_table=page_table, k_cache=k_cache,
-                   v_cache=v_cache, out=out, workspace=workspace)
-    for name, t in tensors.items():
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    if not 0 <= int(total_q) <= c.batch * c.q_len:
+        raise ValueError(f"total_q {total_q} outside 0..batch * q_len = {c.batch * c.q_len}")
+    specs = _step_specs(c, int(total_q), qkv, positions, cache_loc, cache_seqlens, page_table,
+                        k_cache, v_cache, k_scale, v_scale, out, workspace)
+    specs.append(("cu_seqlens_q", cu_seqlens_q, _dt("int32"), c.batch + 1, None, True))
+    _check_tensors(specs, dev)
     if stream is None:
         stream = torch.cuda.current_stream(qkv.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -218,12 +298,17 @@ def mi355x_gated_attn_sparse_prefill_step(ctx, qkv, positions, cache_loc, token_
     cache_seqlens (int32 [batch]) is each query's position + 1, block_idx is
     int32 [Hkv, batch, topk]; otherwise as mi355x_gated_attn_sparse_step."""
     import torch
-    tensors = dict(qkv=qkv, positions=positions, cache_loc=cache_loc, token_req=token_req,
-                   cache_seqlens=cache_seqlens, page_table=page_table, block_idx=block_idx,
-                   k_cache=k_cache, v_cache=v_cache, out=out, workspace=workspace)
-    for name, t in tensors.items():
-        if t is not None and (not t.is_cuda or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    if int(num_requests) < 1:
+        raise ValueError(f"num_requests {num_requests} < 1")
+    specs = _step_specs(c, c.batch, qkv, positions, cache_loc, cache_seqlens, page_table, k_cache,
+                        v_cache, k_scale, v_scale, out, workspace, page_rows=int(num_requests))
+    specs += [("token_req", token_req, _dt("int32"), c.batch, None, True),
+              ("block_idx", block_idx, _dt("int32"), c.num_kv_heads * c.batch * c.sparse_topk,
+               None, True)]
+    _check_tensors(specs, dev)
     if stream is None:
         stream = torch.cuda.current_stream(qkv.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -240,10 +325,16 @@ def mi355x_gated_attn_step_meta(ctx, seq_lens, page_table, positions, cache_loc,
     seq_lens [B] and page_table [B, max_pages] in; int64 positions and cache_loc
     [B*L], int32 cache_seqlens [B] out)."""
     import torch
-    for name, t in dict(seq_lens=seq_lens, page_table=page_table, positions=positions,
-                        cache_loc=cache_loc, cache_seqlens=cache_seqlens).items():
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    T = c.batch * c.q_len
+    i32, i64 = _dt("int32"), _dt("int64")
+    _check_tensors([("seq_lens", seq_lens, i32, c.batch, None, True),
+                    ("page_table", page_table, i32, c.batch * c.max_pages, None, True),
+                    ("positions", positions, i64, T, None, True),
+                    ("cache_loc", cache_loc, i64, T, None, True),
+                    ("cache_seqlens", cache_seqlens, i32, c.batch, None, True)], dev)
     if stream is None:
         stream = torch.cuda.current_stream(seq_lens.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -255,6 +346,8 @@ def mi355x_gated_attn_step_meta(ctx, seq_lens, page_table, positions, cache_loc,
 def mi355x_gated_attn_workspace_init(ctx, workspace, stream=None):
     """Zero a new workspace's counters (once, before its first step)."""
     import torch
+    _, dev = _ctx_entry(ctx)
+    _check_tensors([("workspace", workspace, _dt("uint8", "int8"), None, None, True)], dev)
     if stream is None:
         stream = torch.cuda.current_stream(workspace.device)
     handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
@@ -263,6 +356,7 @@ def mi355x_gated_attn_workspace_init(ctx, workspace, stream=None):
 
 
 def mi355x_gated_attn_destroy(ctx):
+    _CTX.pop(_ctx_key(ctx), None)
     lib().mi355x_gated_attn_destroy(ctx)
 
 

@@ -22,17 +22,27 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-CFLAGS = ["-O2", "-fPIC", "-shared", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
-          "-Wall", "-Wextra"]
+CFLAGS = ["-O2", "-fPIC", "-shared", "-std=c11", "-fopenmp", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+# The sanitizer build (address + undefined behaviour, host code only): the
+# same source into its own library, selected with ORACLE_SANITIZE=1 (the
+# process must then preload the ASan runtime, see tests/test_sanitizers.py).
+SAN_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+             "-fno-sanitize-recover=undefined"]
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
 
 
-def build(force: bool = False) -> str:
-    """Compile oracle.c into liboracle.so with gcc (no GPU toolchain involved)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = False, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so (or, sanitize=True, the address and
+    undefined-behaviour sanitized liboracle_san.so) with gcc (no GPU toolchain
+    involved)."""
+    out = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(out) or os.path.getmtime(out) < os.path.getmtime(_SRC):
+        tmp = out + ".tmp"
+        flags = CFLAGS + (SAN_FLAGS if sanitize else [])
+        subprocess.check_call(["gcc", *flags, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 class _Cfg(ctypes.Structure):
@@ -51,9 +61,11 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
-        L = ctypes.CDLL(_LIB)
+        san = os.environ.get("ORACLE_SANITIZE") == "1"
+        path = _SAN_LIB if san else _LIB
+        if not os.path.exists(path):
+            build(sanitize=san)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         L.orc_bf16_round.argtypes = [ctypes.c_double]
         L.orc_bf16_round.restype = ctypes.c_uint16
@@ -88,6 +100,8 @@ def lib():
                                       ctypes.c_int32, P, P, ctypes.c_float, ctypes.c_float, P, P, P]
         L.orc_qk_norm.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_float, ctypes.c_float, P]
+        L.orc_threads.argtypes = [ctypes.c_int]
+        L.orc_threads.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -126,6 +140,13 @@ def _p(a: np.ndarray | None):
 def _check(rc: int, what: str):
     if rc != 0:
         raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def threads(n: int = 0) -> int:
+    """Set the OpenMP thread count of the oracle's attention loops (n > 0) and
+    return the count they will use.  Results do not depend on it: each
+    (token, head) pair is computed by one thread in a fixed order."""
+    return int(lib().orc_threads(int(n)))
 
 
 # --- number formats --------------------------------------------------------

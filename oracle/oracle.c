@@ -20,7 +20,7 @@
  * intermediate bf16 rounding the page writes; attention and the epilogue are
  * evaluated in double (the page fixes no precision there beyond bf16 output).
  *
- * Build: gcc -O2 -fPIC -shared -ffp-contract=off -fno-fast-math oracle.c -lm
+ * Build: gcc -O2 -fPIC -shared -fopenmp -ffp-contract=off -fno-fast-math oracle.c -lm
  * (contraction must stay off so every fp32 step rounds exactly once).
  */
 #include <math.h>
@@ -337,6 +337,43 @@ static int64_t key_row(const orc_config* cfg, const int32_t* page_table, int64_t
   return phys * cfg->page_size + j % cfg->page_size;
 }
 
+/* One (token t, q head h) pair of orc_attention; sc: scratch of at least
+ * the pair's key count. */
+static int attend_pair(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cache,
+                       const uint8_t* v_cache, const int32_t* page_table,
+                       const int32_t* cache_seqlens, double kd, double vd, int64_t t, int h,
+                       double* sc, double* o) {
+  const int hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
+  const int64_t b = t / cfg->q_len;
+  const int g = h / (hq / hkv);
+  double qv[256];
+  for (int c = 0; c < d; ++c) o[c] = 0.0;
+  int64_t lo;
+  const int64_t cnt = key_range(cfg, cache_seqlens, t, &lo);
+  if (cnt == 0) return ORC_OK;
+  for (int c = 0; c < d; ++c) qv[c] = orc_e4m3_decode(q[(t * hq + h) * d + c]);
+  double mx = -INFINITY;
+  for (int64_t k = 0; k < cnt; ++k) {
+    const int64_t r = key_row(cfg, page_table, b, lo + k);
+    if (r < 0) return ORC_BAD_ROW;
+    const uint8_t* kr = k_cache + (r * hkv + g) * d;
+    double dot = 0.0;
+    for (int c = 0; c < d; ++c) dot += qv[c] * orc_e4m3_decode(kr[c]);
+    sc[k] = dot * kd * (double)cfg->sm_scale;
+    if (sc[k] > mx) mx = sc[k];
+  }
+  double wsum = 0.0;
+  for (int64_t k = 0; k < cnt; ++k) {
+    const double w = exp(sc[k] - mx);
+    wsum += w;
+    const int64_t r = key_row(cfg, page_table, b, lo + k);
+    const uint8_t* vr = v_cache + (r * hkv + g) * d;
+    for (int c = 0; c < d; ++c) o[c] += w * orc_e4m3_decode(vr[c]);
+  }
+  for (int c = 0; c < d; ++c) o[c] = vd * o[c] / wsum;
+  return ORC_OK;
+}
+
 /*
  * Attention output before any rounding, for selected (token, q head) pairs.
  *   q          e4m3 [T, Hq, D]
@@ -348,67 +385,52 @@ static int64_t key_row(const orc_config* cfg, const int32_t* page_table, int64_t
  * are the cache scales on the scaled path and 1 otherwise (the page passes
  * k_descale / v_descale only when the scales are set).  A query with no
  * visible key gets o = 0 (READING).
+ * The pairs are independent, so they are spread over OpenMP threads (when
+ * the library is built with OpenMP); each pair's arithmetic and its order
+ * are the same whatever the thread count.
  */
 int orc_attention(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cache,
                   const uint8_t* v_cache, const int32_t* page_table, const int32_t* cache_seqlens,
                   float k_scale, float v_scale, int64_t n_sel, const int64_t* sel_t,
                   const int32_t* sel_h, double* o_out) {
   if (!cfg_ok(cfg)) return ORC_BAD_ARG;
-  const int hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
-  const int grp = hq / hkv;
+  const int hq = cfg->num_q_heads, d = cfg->head_dim;
   const int64_t T = (int64_t)cfg->batch * cfg->q_len;
   const int scaled = cfg->kv_scale != 1.0f;
   const double kd = scaled ? (double)k_scale : 1.0, vd = scaled ? (double)v_scale : 1.0;
   if (!sel_t) n_sel = T * hq;
-  double qv[256];
-  double* sc = NULL;
-  int64_t sc_cap = 0;
   for (int64_t n = 0; n < n_sel; ++n) {
-    int64_t t = sel_t ? sel_t[n] : n / hq;
-    int h = sel_h ? sel_h[n] : (int)(n % hq);
-    if (t < 0 || t >= T || h < 0 || h >= hq) {
-      free(sc);
-      return ORC_BAD_ARG;
-    }
-    int64_t b = t / cfg->q_len;
-    int g = h / grp;
-    double* o = o_out + n * d;
-    for (int c = 0; c < d; ++c) o[c] = 0.0;
-    int64_t lo;
-    int64_t cnt = key_range(cfg, cache_seqlens, t, &lo);
-    if (cnt == 0) continue;
-    if (cnt > sc_cap) {
-      free(sc);
-      sc_cap = cnt;
-      sc = (double*)malloc(sizeof(double) * (size_t)cnt);
-      if (!sc) return ORC_BAD_ARG;
-    }
-    for (int c = 0; c < d; ++c) qv[c] = orc_e4m3_decode(q[(t * hq + h) * d + c]);
-    double mx = -INFINITY;
-    for (int64_t k = 0; k < cnt; ++k) {
-      int64_t r = key_row(cfg, page_table, b, lo + k);
-      if (r < 0) {
-        free(sc);
-        return ORC_BAD_ROW;
-      }
-      const uint8_t* kr = k_cache + (r * hkv + g) * d;
-      double dot = 0.0;
-      for (int c = 0; c < d; ++c) dot += qv[c] * orc_e4m3_decode(kr[c]);
-      sc[k] = dot * kd * (double)cfg->sm_scale;
-      if (sc[k] > mx) mx = sc[k];
-    }
-    double wsum = 0.0;
-    for (int64_t k = 0; k < cnt; ++k) {
-      double w = exp(sc[k] - mx);
-      wsum += w;
-      int64_t r = key_row(cfg, page_table, b, lo + k);
-      const uint8_t* vr = v_cache + (r * hkv + g) * d;
-      for (int c = 0; c < d; ++c) o[c] += w * orc_e4m3_decode(vr[c]);
-    }
-    for (int c = 0; c < d; ++c) o[c] = vd * o[c] / wsum;
+    const int64_t t = sel_t ? sel_t[n] : n / hq;
+    const int h = sel_h ? sel_h[n] : (int)(n % hq);
+    if (t < 0 || t >= T || h < 0 || h >= hq) return ORC_BAD_ARG;
   }
-  free(sc);
-  return ORC_OK;
+  int rc = ORC_OK;
+#pragma omp parallel
+  {
+    double* sc = NULL;
+    int64_t sc_cap = 0;
+#pragma omp for schedule(dynamic, 4)
+    for (int64_t n = 0; n < n_sel; ++n) {
+      const int64_t t = sel_t ? sel_t[n] : n / hq;
+      const int h = sel_h ? sel_h[n] : (int)(n % hq);
+      int64_t lo;
+      const int64_t cnt = key_range(cfg, cache_seqlens, t, &lo);
+      if (cnt > sc_cap) {
+        free(sc);
+        sc_cap = cnt;
+        sc = (double*)malloc(sizeof(double) * (size_t)cnt);
+      }
+      int r = (cnt > 0 && !sc) ? ORC_BAD_ARG
+                               : attend_pair(cfg, q, k_cache, v_cache, page_table, cache_seqlens,
+                                             kd, vd, t, h, sc, o_out + n * d);
+      if (r != ORC_OK) {
+#pragma omp critical
+        rc = r;
+      }
+    }
+    free(sc);
+  }
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -425,74 +447,88 @@ int orc_attention(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cach
 /* repeated index adds nothing); no window applies.  Scores, weights,        */
 /* descales and the empty-set output 0 are as in orc_attention.              */
 /* ------------------------------------------------------------------------ */
+/* One (request b, KV head g) of orc_sparse_attention: its visible-key set and
+ * its grp query heads; vis and sc hold at least max(cs, 1) entries. */
+static int sparse_head(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cache,
+                       const uint8_t* v_cache, const int32_t* page_table, int64_t cs,
+                       const int32_t* block_idx, int32_t block_size, int32_t topk, double kd,
+                       double vd, int64_t b, int g, unsigned char* vis, double* sc,
+                       double* o_out) {
+  const int hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
+  const int grp = hq / hkv;
+  const int64_t B = cfg->batch;
+  double qv[256];
+  /* visible keys of this KV head: the union of its selected blocks, below cs */
+  memset(vis, 0, (size_t)(cs > 0 ? cs : 1));
+  for (int i = 0; i < topk; ++i) {
+    const int64_t j = block_idx[((int64_t)g * B + b) * topk + i];
+    if (j < 0) continue;
+    for (int64_t key = j * block_size; key < (j + 1) * block_size && key < cs; ++key) vis[key] = 1;
+  }
+  for (int hh = 0; hh < grp; ++hh) {
+    const int h = g * grp + hh;
+    double* o = o_out + (b * hq + h) * d;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    for (int c = 0; c < d; ++c) qv[c] = orc_e4m3_decode(q[(b * hq + h) * d + c]);
+    double mx = -INFINITY;
+    int64_t cnt = 0;
+    for (int64_t key = 0; key < cs; ++key) {
+      if (!vis[key]) continue;
+      const int64_t r = key_row(cfg, page_table, b, key);
+      if (r < 0) return ORC_BAD_ROW;
+      const uint8_t* kr = k_cache + (r * hkv + g) * d;
+      double dot = 0.0;
+      for (int c = 0; c < d; ++c) dot += qv[c] * orc_e4m3_decode(kr[c]);
+      sc[key] = dot * kd * (double)cfg->sm_scale;
+      if (sc[key] > mx) mx = sc[key];
+      ++cnt;
+    }
+    if (cnt == 0) continue;
+    double wsum = 0.0;
+    for (int64_t key = 0; key < cs; ++key) {
+      if (!vis[key]) continue;
+      const double w = exp(sc[key] - mx);
+      wsum += w;
+      const int64_t r = key_row(cfg, page_table, b, key);
+      const uint8_t* vr = v_cache + (r * hkv + g) * d;
+      for (int c = 0; c < d; ++c) o[c] += w * orc_e4m3_decode(vr[c]);
+    }
+    for (int c = 0; c < d; ++c) o[c] = vd * o[c] / wsum;
+  }
+  return ORC_OK;
+}
+
+/* The (request, KV head) pairs are independent and spread over OpenMP
+ * threads; each pair's arithmetic is the same whatever the thread count. */
 int orc_sparse_attention(const orc_config* cfg, const uint8_t* q, const uint8_t* k_cache,
                          const uint8_t* v_cache, const int32_t* page_table,
                          const int32_t* cache_seqlens, const int32_t* block_idx,
                          int32_t block_size, int32_t topk, float k_scale, float v_scale,
                          double* o_out) {
   if (!cfg_ok(cfg) || cfg->q_len != 1 || block_size < 1 || topk < 1) return ORC_BAD_ARG;
-  const int hq = cfg->num_q_heads, hkv = cfg->num_kv_heads, d = cfg->head_dim;
-  const int grp = hq / hkv;
+  const int hkv = cfg->num_kv_heads;
   const int64_t B = cfg->batch;
   const int scaled = cfg->kv_scale != 1.0f;
   const double kd = scaled ? (double)k_scale : 1.0, vd = scaled ? (double)v_scale : 1.0;
-  double qv[256];
-  for (int64_t b = 0; b < B; ++b) {
+  int rc = ORC_OK;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bg = 0; bg < B * hkv; ++bg) {
+    const int64_t b = bg / hkv;
+    const int g = (int)(bg % hkv);
     const int64_t cs = cache_seqlens[b];
-    /* visible keys per KV head: the union of its selected blocks, below cs */
     unsigned char* vis = (unsigned char*)calloc((size_t)(cs > 0 ? cs : 1), 1);
     double* sc = (double*)malloc(sizeof(double) * (size_t)(cs > 0 ? cs : 1));
-    if (!vis || !sc) {
-      free(vis);
-      free(sc);
-      return ORC_BAD_ARG;
-    }
-    for (int g = 0; g < hkv; ++g) {
-      memset(vis, 0, (size_t)(cs > 0 ? cs : 1));
-      for (int i = 0; i < topk; ++i) {
-        const int64_t j = block_idx[((int64_t)g * B + b) * topk + i];
-        if (j < 0) continue;
-        for (int64_t key = j * block_size; key < (j + 1) * block_size && key < cs; ++key) vis[key] = 1;
-      }
-      for (int hh = 0; hh < grp; ++hh) {
-        const int h = g * grp + hh;
-        double* o = o_out + (b * hq + h) * d;
-        for (int c = 0; c < d; ++c) o[c] = 0.0;
-        for (int c = 0; c < d; ++c) qv[c] = orc_e4m3_decode(q[(b * hq + h) * d + c]);
-        double mx = -INFINITY;
-        int64_t cnt = 0;
-        for (int64_t key = 0; key < cs; ++key) {
-          if (!vis[key]) continue;
-          const int64_t r = key_row(cfg, page_table, b, key);
-          if (r < 0) {
-            free(vis);
-            free(sc);
-            return ORC_BAD_ROW;
-          }
-          const uint8_t* kr = k_cache + (r * hkv + g) * d;
-          double dot = 0.0;
-          for (int c = 0; c < d; ++c) dot += qv[c] * orc_e4m3_decode(kr[c]);
-          sc[key] = dot * kd * (double)cfg->sm_scale;
-          if (sc[key] > mx) mx = sc[key];
-          ++cnt;
-        }
-        if (cnt == 0) continue;
-        double wsum = 0.0;
-        for (int64_t key = 0; key < cs; ++key) {
-          if (!vis[key]) continue;
-          const double w = exp(sc[key] - mx);
-          wsum += w;
-          const int64_t r = key_row(cfg, page_table, b, key);
-          const uint8_t* vr = v_cache + (r * hkv + g) * d;
-          for (int c = 0; c < d; ++c) o[c] += w * orc_e4m3_decode(vr[c]);
-        }
-        for (int c = 0; c < d; ++c) o[c] = vd * o[c] / wsum;
-      }
-    }
+    int r = (!vis || !sc) ? ORC_BAD_ARG
+                          : sparse_head(cfg, q, k_cache, v_cache, page_table, cs, block_idx,
+                                        block_size, topk, kd, vd, b, g, vis, sc, o_out);
     free(vis);
     free(sc);
+    if (r != ORC_OK) {
+#pragma omp critical
+      rc = r;
+    }
   }
-  return ORC_OK;
+  return rc;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -686,4 +722,22 @@ int orc_qk_norm(const uint16_t* x, int64_t M, int32_t num_heads, int32_t head_di
     }
   }
   return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Thread control of the OpenMP loops above (test and benchmark use only):   */
+/* n > 0 sets the thread count; returns the count the next loop will use (1  */
+/* when the library was built without OpenMP).                               */
+/* ------------------------------------------------------------------------ */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int orc_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
 }

@@ -445,3 +445,155 @@ def test_sparse_prefill_step_validates_before_any_launch(L):
     finally:
         for c in (sparse, dense, empty):
             ga.mi355x_gated_attn_destroy(c)
+
+
+def _good_step_tensors(c):
+    """CPU tensors of the right dtypes and sizes for config c (the binding checks
+    dtype and size before device and layout)."""
+    import torch
+    T = c.batch * c.q_len
+    width = (2 * c.num_q_heads + 2 * c.num_kv_heads) * c.head_dim
+    cache = c.num_pages * c.page_size * c.num_kv_heads * c.head_dim
+    return dict(
+        qkv=torch.zeros(T * width, dtype=torch.int16),
+        positions=torch.zeros(T, dtype=torch.int64),
+        cache_loc=torch.zeros(T, dtype=torch.int64),
+        cache_seqlens=torch.zeros(c.batch, dtype=torch.int32),
+        page_table=torch.zeros(c.batch * c.max_pages, dtype=torch.int32),
+        seq_lens=torch.zeros(c.batch, dtype=torch.int32),
+        k_cache=torch.zeros(cache, dtype=torch.uint8),
+        v_cache=torch.zeros(cache, dtype=torch.uint8),
+        k_scale=torch.ones(1, dtype=torch.float32),
+        v_scale=torch.ones(1, dtype=torch.float32),
+        out=torch.zeros(T * c.num_q_heads * c.head_dim, dtype=torch.bfloat16),
+        workspace=torch.zeros(256, dtype=torch.uint8))
+
+
+@pytest.mark.parametrize("name,bad,msg", [
+    ("qkv", lambda t: t.float(), "dtype"),
+    ("qkv", lambda t: t[:-8], "elements"),
+    ("positions", lambda t: t.int(), "dtype"),
+    ("positions", lambda t: t[:-1], "elements"),
+    ("cache_loc", lambda t: t.int(), "dtype"),
+    ("cache_loc", lambda t: t.repeat(2), "elements"),
+    ("cache_seqlens", lambda t: t.long(), "dtype"),
+    ("cache_seqlens", lambda t: t[:-1], "elements"),
+    ("page_table", lambda t: t.long(), "dtype"),
+    ("page_table", lambda t: t[:-1], "elements"),
+    ("seq_lens", lambda t: t.long(), "dtype"),
+    ("k_cache", lambda t: t.half(), "dtype"),
+    ("k_cache", lambda t: t[:-1], "at least"),
+    ("v_cache", lambda t: t[:-64], "at least"),
+    ("k_scale", lambda t: t.double(), "dtype"),
+    ("k_scale", lambda t: t.repeat(2), "elements"),
+    ("k_scale", lambda t: None, "required"),
+    ("v_scale", lambda t: t.half(), "dtype"),
+    ("v_scale", lambda t: None, "required"),
+    ("out", lambda t: t.float(), "dtype"),
+    ("out", lambda t: t[:-1], "elements"),
+    ("workspace", lambda t: t.float(), "dtype"),
+])
+def test_binding_checks_every_tensor_against_the_config(L, name, bad, msg):
+    """The step wrapper checks each tensor's dtype and size against the
+    context's config (and its device and layout) before any pointer reaches the
+    C ABI: a mis-sized or mistyped tensor raises ValueError naming it."""
+    c = cfg(batch=3, q_len=2, max_pages=40, num_pages=100, page_size=4, kv_scale=0.5)
+    ctx = ga.mi355x_gated_attn_prepare(c)
+    try:
+        t = _good_step_tensors(c)
+        t[name] = bad(t[name])
+        with pytest.raises(ValueError, match=msg) as e:
+            ga.mi355x_gated_attn_step(ctx, t["qkv"], t["positions"], t["cache_loc"],
+                                      t["cache_seqlens"], t["page_table"], t["seq_lens"],
+                                      t["k_cache"], t["v_cache"], t["k_scale"], t["v_scale"],
+                                      t["out"], t["workspace"])
+        assert name in str(e.value)
+        # right dtypes and sizes on the host: the device check is what remains
+        good = _good_step_tensors(c)
+        with pytest.raises(ValueError, match="device tensor"):
+            ga.mi355x_gated_attn_step(ctx, *[good[k] for k in (
+                "qkv", "positions", "cache_loc", "cache_seqlens", "page_table", "seq_lens",
+                "k_cache", "v_cache", "k_scale", "v_scale", "out", "workspace")])
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+
+
+def test_binding_checks_the_variants_own_tensors(L):
+    """block_idx (sparse), cu_seqlens_q and total_q (ragged), token_req and the
+    page-table rows (sparse prefill) and the metadata tensors are checked too;
+    positions may be absent without RoPE and the scales without a scaled cache."""
+    import torch
+    # sparse decode: block_idx [Hkv, B, topk]
+    c = cfg(batch=3, q_len=1, window=0, max_pages=40, num_pages=100, page_size=4,
+            sparse_block=32, sparse_topk=5)
+    ctx = ga.mi355x_gated_attn_prepare(c)
+    try:
+        t = _good_step_tensors(c)
+        args = [t[k] for k in ("qkv", "positions", "cache_loc", "cache_seqlens", "page_table")]
+        rest = [t[k] for k in ("k_cache", "v_cache", "k_scale", "v_scale", "out", "workspace")]
+        with pytest.raises(ValueError, match="block_idx: 29 elements"):
+            ga.mi355x_gated_attn_sparse_step(ctx, *args, torch.zeros(29, dtype=torch.int32), *rest)
+        with pytest.raises(ValueError, match="block_idx: dtype"):
+            ga.mi355x_gated_attn_sparse_step(ctx, *args, torch.zeros(30, dtype=torch.int64), *rest)
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    # ragged: cu_seqlens_q [B+1], total_q bounds, packed rows of total_q tokens
+    c = cfg(batch=2, q_len=16, window=0, max_pages=40, num_pages=100, page_size=4,
+            rope_theta=0.0)
+    ctx = ga.mi355x_gated_attn_prepare(c)
+    try:
+        t = _good_step_tensors(c)
+        n = 20
+        W = 2304
+        qkv = torch.zeros(n * W, dtype=torch.int16)
+        loc = torch.zeros(n, dtype=torch.int64)
+        out = torch.zeros(n * 1024, dtype=torch.int16)
+        common = (t["cache_seqlens"], t["page_table"], t["k_cache"], t["v_cache"], None, None,
+                  out, t["workspace"])
+        with pytest.raises(ValueError, match="total_q 33"):
+            ga.mi355x_gated_attn_ragged_step(ctx, qkv, None, loc, torch.zeros(3, dtype=torch.int32),
+                                             33, *common)
+        with pytest.raises(ValueError, match="qkv: "):
+            ga.mi355x_gated_attn_ragged_step(ctx, qkv, None, loc, torch.zeros(3, dtype=torch.int32),
+                                             19, *common)
+        with pytest.raises(ValueError, match="cu_seqlens_q: 2 elements"):
+            ga.mi355x_gated_attn_ragged_step(ctx, qkv, None, loc, torch.zeros(2, dtype=torch.int32),
+                                             n, *common)
+        with pytest.raises(ValueError, match="device tensor"):  # positions may be absent
+            ga.mi355x_gated_attn_ragged_step(ctx, qkv, None, loc, torch.zeros(3, dtype=torch.int32),
+                                             n, *common)
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    # sparse prefill: page_table has num_requests rows, token_req one per query
+    c = cfg(batch=6, q_len=1, window=0, max_pages=40, num_pages=100, page_size=4,
+            sparse_block=32, sparse_topk=2)
+    ctx = ga.mi355x_gated_attn_prepare(c)
+    try:
+        t = _good_step_tensors(c)
+        pt2 = torch.zeros(2 * 40, dtype=torch.int32)
+        rest = (t["k_cache"], t["v_cache"], t["k_scale"], t["v_scale"], t["out"], t["workspace"])
+        bi = torch.zeros(2 * 6 * 2, dtype=torch.int32)
+        with pytest.raises(ValueError, match="page_table: 240 elements"):
+            ga.mi355x_gated_attn_sparse_prefill_step(ctx, t["qkv"], t["positions"], t["cache_loc"],
+                                                     torch.zeros(6, dtype=torch.int32), 2,
+                                                     t["cache_seqlens"], t["page_table"], bi, *rest)
+        with pytest.raises(ValueError, match="token_req: 5 elements"):
+            ga.mi355x_gated_attn_sparse_prefill_step(ctx, t["qkv"], t["positions"], t["cache_loc"],
+                                                     torch.zeros(5, dtype=torch.int32), 2,
+                                                     t["cache_seqlens"], pt2, bi, *rest)
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    # step metadata
+    c = cfg(batch=3, q_len=2, max_pages=40, num_pages=100)
+    ctx = ga.mi355x_gated_attn_prepare(c)
+    try:
+        i32 = lambda n: torch.zeros(n, dtype=torch.int32)
+        i64 = lambda n: torch.zeros(n, dtype=torch.int64)
+        with pytest.raises(ValueError, match="positions: 5 elements"):
+            ga.mi355x_gated_attn_step_meta(ctx, i32(3), i32(120), i64(5), i64(6), i32(3))
+        with pytest.raises(ValueError, match="cache_seqlens: dtype"):
+            ga.mi355x_gated_attn_step_meta(ctx, i32(3), i32(120), i64(6), i64(6), i64(3))
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    with pytest.raises(ValueError, match="unknown or destroyed"):
+        ga.mi355x_gated_attn_step_meta(ctx, i32(3), i32(120), i64(6), i64(6), i32(3))

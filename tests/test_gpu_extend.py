@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from gpu_support import (Device, Reference, abi_config, assert_codes_match, assert_outputs_close,
                          check_full, max_context, run_gpu)
@@ -110,15 +111,9 @@ def test_extend_graph_replay_matches_eager():
     step.close()
 
 
-def _sample_rows(T, hq, rng, n=96):
-    t = [0] * hq + [T - 1] * hq + list(rng.integers(0, T, n))
-    h = list(range(hq)) * 2 + list(rng.integers(0, hq, n))
-    return np.array(t, np.int64), np.array(h, np.int32)
-
-
 @pytest.mark.parametrize("name", list(synth.EXTEND))
 def test_extend_full_size_workload(name):
-    """Every q and cache byte and sampled output rows of one full-size extend."""
+    """Every q and cache byte and every output row of one full-size extend."""
     w = synth.WORKLOADS[name]
     _say(f"[gpu] full-size {name}: generating inputs")
     x = synth.make_inputs(w)
@@ -130,18 +125,17 @@ def test_extend_full_size_workload(name):
     assert_codes_match(res.q, ref.q, ref.q.size, name + " q")
     assert_codes_match(res.k_cache, ref.k_cache, written, name + " k_cache")
     assert_codes_match(res.v_cache, ref.v_cache, written, name + " v_cache")
-    rng = np.random.default_rng(11)
-    st, sh = _sample_rows(x.tokens, w.num_q_heads, rng)
-    _say(f"[gpu] full-size {name}: oracle attention on {len(st)} rows")
-    out_ref = ref.outputs(st, sh)
-    got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
-    assert_outputs_close(got, out_ref, name + " out")
+    _say(f"[gpu] full-size {name}: oracle attention on all {x.tokens * w.num_q_heads} rows "
+         f"({oracle.threads()} threads)")
+    out_ref = ref.outputs().reshape(res.out.shape)
+    assert_outputs_close(res.out, out_ref, name + " out")
 
 
 def test_extend_longest_block_served():
     """q_len 65,536 (the longest block the library serves) for one request over a
     1k-3k prefix with page 1's window, RoPE and pages of 16: every q and cache
-    byte, sampled output rows (first and last tokens among them)."""
+    byte; every output row of the first and last 1,024 tokens (the window's
+    start, the tiles' and splits' ends) and of 1,024 random tokens."""
     w = synth.small(name="longest", batch=1, q_len=65536, window=2048, rope_theta=500000.0,
                     page_size=16, seq_lo=1000, seq_hi=3000)
     _say("[gpu] extend L=65536: generating inputs")
@@ -154,8 +148,13 @@ def test_extend_longest_block_served():
     assert_codes_match(res.q, ref.q, ref.q.size, "longest q")
     assert_codes_match(res.k_cache, ref.k_cache, written, "longest k_cache")
     assert_codes_match(res.v_cache, ref.v_cache, written, "longest v_cache")
-    st, sh = _sample_rows(x.tokens, w.num_q_heads, np.random.default_rng(3))
-    got = res.out.reshape(x.tokens, w.num_q_heads, w.head_dim)[st, sh]
+    T, H = x.tokens, w.num_q_heads
+    toks = np.unique(np.concatenate([np.arange(1024), np.arange(T - 1024, T),
+                                     np.random.default_rng(3).integers(0, T, 1024)]))
+    st = np.repeat(toks, H).astype(np.int64)
+    sh = np.tile(np.arange(H), len(toks)).astype(np.int32)
+    _say(f"[gpu] extend L=65536: oracle attention on {len(st)} rows ({oracle.threads()} threads)")
+    got = res.out.reshape(T, H, w.head_dim)[st, sh]
     assert_outputs_close(got, ref.outputs(st, sh), "longest out")
 
 

@@ -218,3 +218,31 @@ def test_step_composes_the_parts(orc):
     np.testing.assert_array_equal(q, q2)
     np.testing.assert_array_equal(kc, kc2)
     np.testing.assert_array_equal(out.reshape(-1, 64), out2)
+
+
+def test_thread_count_does_not_change_the_oracle(orc):
+    """The attention loops run their (token, head) pairs (and the sparse step its
+    (request, KV head) pairs) on OpenMP threads: one thread and all of them give
+    the same bytes, the selected-row form included."""
+    w = synth.small(batch=3, q_len=4, window=50, rope_theta=500000.0, page_size=4, seq_lo=60,
+                    seq_hi=300)
+    x = synth.make_inputs(w, seed=12)
+    cfg = _cfg(orc, x)
+    kc, vc = x.k_cache.copy(), x.v_cache.copy()
+    q = orc.prologue(cfg, x.qkv, x.positions, x.cache_loc, kc, vc, x.k_scale, x.v_scale)
+    n0 = orc.threads()
+    try:
+        outs = []
+        for n in (1, max(2, n0)):
+            orc.threads(n)
+            assert orc.threads() == n or n0 == 1
+            o = orc.attention(cfg, q, kc, vc, x.page_table, x.cache_seqlens, x.k_scale, x.v_scale)
+            st = np.array([5, 0, 11, 7], np.int64)
+            sh = np.array([3, 15, 0, 8], np.int32)
+            osel = orc.attention(cfg, q, kc, vc, x.page_table, x.cache_seqlens, x.k_scale,
+                                 x.v_scale, st, sh)
+            np.testing.assert_array_equal(osel, o[st * 16 + sh])
+            outs.append(o)
+        np.testing.assert_array_equal(outs[0], outs[1])
+    finally:
+        orc.threads(n0)
