@@ -182,9 +182,10 @@ def _step_specs(c, tokens, qkv, positions, cache_loc, cache_seqlens, page_table,
     rows = c.batch if page_rows is None else page_rows
     cache = c.num_pages * c.page_size * c.num_kv_heads * c.head_dim
     scaled = c.kv_scale != 1.0
-    return [("qkv", qkv, two, tokens * width, None, True),
-            ("positions", positions, i64, tokens, None, c.rope_theta != 0.0),
-            ("cache_loc", cache_loc, i64, tokens, None, True),
+    per_tok = (lambda n: n * tokens) if tokens else (lambda n: None)  # no token: none is read
+    return [("qkv", qkv, two, per_tok(width), None, True),
+            ("positions", positions, i64, per_tok(1), None, c.rope_theta != 0.0),
+            ("cache_loc", cache_loc, i64, per_tok(1), None, True),
             ("cache_seqlens", cache_seqlens, i32, c.batch, None, True),
             ("page_table", page_table, i32, rows * c.max_pages, None, True),
             ("seq_lens", seq_lens, i32, c.batch, None, False),
@@ -192,7 +193,7 @@ def _step_specs(c, tokens, qkv, positions, cache_loc, cache_seqlens, page_table,
             ("v_cache", v_cache, one, None, cache, True),
             ("k_scale", k_scale, f32, 1, None, scaled),
             ("v_scale", v_scale, f32, 1, None, scaled),
-            ("out", out, two, tokens * c.num_q_heads * c.head_dim, None, True),
+            ("out", out, two, per_tok(c.num_q_heads * c.head_dim), None, True),
             ("workspace", workspace, _dt("uint8", "int8"), None, None, True)]
 
 
