@@ -26,7 +26,8 @@ EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_g
             "mi355x_gated_attn_last_error", "mi355x_gated_attn_timing",
             "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta",
             "mi355x_qk_norm_supports", "mi355x_qk_norm", "mi355x_gated_attn_sparse_step",
-            "mi355x_gated_attn_ragged_step", "mi355x_gated_attn_sparse_prefill_step"]
+            "mi355x_gated_attn_ragged_step", "mi355x_gated_attn_sparse_prefill_step",
+            "mi355x_gated_attn_step_noalloc"]
 
 MI355X_QKN_BF16 = 0
 MI355X_QKN_FP16 = 1
@@ -70,6 +71,7 @@ def lib() -> ctypes.CDLL:
                                              ctypes.POINTER(ctypes.c_int32)]
         L.mi355x_gated_attn_workspace_init.argtypes = [P, P, ctypes.c_size_t, P]
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
+        L.mi355x_gated_attn_step_noalloc.argtypes = [P] * 13
         L.mi355x_gated_attn_step_meta.argtypes = [P] * 7
         L.mi355x_gated_attn_sparse_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_sparse_prefill_step.argtypes = [P] * 5 + [ctypes.c_int32] + \
@@ -239,6 +241,27 @@ def mi355x_gated_attn_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_t
         ctx, _ptr(qkv), _ptr(positions), _ptr(cache_loc), _ptr(cache_seqlens), _ptr(page_table),
         _ptr(seq_lens), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
         _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(handle)))
+
+
+def mi355x_gated_attn_step_noalloc(ctx, qkv, positions, cache_loc, cache_seqlens, page_table,
+                                   seq_lens, k_cache, v_cache, k_scale, v_scale, out, stream=None):
+    """Launch one step without a workspace (the library's static per-GPU scratch
+    holds q, the partials and the counters); otherwise as mi355x_gated_attn_step."""
+    import torch
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    specs = _step_specs(c, c.batch * c.q_len, qkv, positions, cache_loc, cache_seqlens,
+                        page_table, k_cache, v_cache, k_scale, v_scale, out, None,
+                        seq_lens=seq_lens)
+    _check_tensors([sp for sp in specs if sp[0] != "workspace"], dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(qkv.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_step_noalloc(
+        ctx, _ptr(qkv), _ptr(positions), _ptr(cache_loc), _ptr(cache_seqlens), _ptr(page_table),
+        _ptr(seq_lens), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+        ctypes.c_void_p(handle)))
 
 
 def mi355x_gated_attn_sparse_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table,

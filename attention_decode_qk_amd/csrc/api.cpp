@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -67,6 +68,8 @@ struct mi355x_gated_attn_ctx {
   int32_t key_waves = kAttnWaves;
   bool balanced = false;  // splits per request by key count
   size_t q_bytes = 0, po_off = 0, pml_off = 0, cnt_off = 0, ws_bytes = 0;
+  size_t po_bytes = 0, pml_bytes = 0;  // partial o / l and (m, l) region sizes
+  int64_t n_counters = 0;              // int32 counters (B x groups)
   bool timing = false;
   std::vector<hipEvent_t> events;  // 2 per timed step, reused
   size_t events_used = 0;
@@ -208,9 +211,12 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
                   c.batch, (long long)tiles, s);
     const size_t rows = (size_t)units * 128;  // (tile token, q head) rows of every unit
     ctx->q_bytes = T * kQHeads * kHeadDim;
+    ctx->po_bytes = s > 1 ? (size_t)s * rows * kHeadDim * sizeof(uint16_t) : 0;
+    ctx->pml_bytes = s > 1 ? (size_t)s * rows * 2 * sizeof(float) : 0;
+    ctx->n_counters = units;
     ctx->po_off = align_up(ctx->q_bytes, 256);
-    ctx->pml_off = align_up(ctx->po_off + (s > 1 ? (size_t)s * rows * kHeadDim * sizeof(uint16_t) : 0), 256);
-    ctx->cnt_off = align_up(ctx->pml_off + (s > 1 ? (size_t)s * rows * 2 * sizeof(float) : 0), 256);
+    ctx->pml_off = align_up(ctx->po_off + ctx->po_bytes, 256);
+    ctx->cnt_off = align_up(ctx->pml_off + ctx->pml_bytes, 256);
     ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)units * sizeof(int32_t), 256);
     if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
     ctx->splits = s;
@@ -261,9 +267,12 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
     return fail(MI355X_GA_UNSUPPORTED, "batch %d x %d splits exceeds one launch's workgroups", c.batch, s);
   const size_t rows = T * kQHeads;  // (token, q head) rows
   ctx->q_bytes = T * kQHeads * kHeadDim;
+  ctx->po_bytes = (size_t)s * rows * kHeadDim * sizeof(uint16_t);
+  ctx->pml_bytes = (size_t)s * rows * 2 * sizeof(float);
+  ctx->n_counters = (int64_t)c.batch * groups;
   ctx->po_off = align_up(ctx->q_bytes, 256);
-  ctx->pml_off = align_up(ctx->po_off + (size_t)s * rows * kHeadDim * sizeof(uint16_t), 256);
-  ctx->cnt_off = align_up(ctx->pml_off + (size_t)s * rows * 2 * sizeof(float), 256);
+  ctx->pml_off = align_up(ctx->po_off + ctx->po_bytes, 256);
+  ctx->cnt_off = align_up(ctx->pml_off + ctx->pml_bytes, 256);
   ctx->ws_bytes = align_up(ctx->cnt_off + (size_t)c.batch * groups * sizeof(int32_t), 256);
   if (ctx->ws_bytes == 0) ctx->ws_bytes = 256;
   ctx->splits = s;
@@ -293,7 +302,7 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
   rc = check_device(ctx);
   if (rc) return rc;
   int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) + ctx->cnt_off);
-  hipError_t e = launch_zero_counters(counters, ctx->cfg.batch * ctx->groups,
+  hipError_t e = launch_zero_counters(counters, (int)ctx->n_counters,
                                      reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -329,12 +338,32 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
 
 namespace {
 
+// Where a step keeps q, the split partials and the counters: the caller's
+// workspace (at the plan's offsets) or the library's static scratch.
+struct Regions {
+  uint8_t* q = nullptr;
+  uint8_t* po = nullptr;
+  uint8_t* pml = nullptr;
+  int32_t* counters = nullptr;
+};
+
+Regions workspace_regions(const mi355x_gated_attn_ctx* ctx, void* workspace) {
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  Regions r;
+  r.q = ws;
+  r.po = ws + ctx->po_off;
+  r.pml = ws + ctx->pml_off;
+  r.counters = reinterpret_cast<int32_t*>(ws + ctx->cnt_off);
+  return r;
+}
+
 int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
              const int64_t* cache_loc, const int32_t* cache_seqlens, const int32_t* page_table,
              const int32_t* block_idx, void* k_cache, void* v_cache, const float* k_scale,
              const float* v_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
              const int32_t* cu_seqlens_q = nullptr, int64_t total_q = -1,
-             const int32_t* token_req = nullptr, int32_t pt_rows = 0) {
+             const int32_t* token_req = nullptr, int32_t pt_rows = 0,
+             const Regions* fixed = nullptr) {
   if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
   if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
   const auto& c = ctx->cfg;
@@ -347,12 +376,12 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   const bool scaled = c.kv_scale != 1.0f;
   const bool rope = c.rope_theta != 0.0f;
   if (!qkv || !cache_loc || !cache_seqlens || !page_table || !k_cache || !v_cache || !out ||
-      !workspace)
+      (!fixed && !workspace))
     return fail(MI355X_GA_INVALID_ARGUMENT, "a required pointer is NULL");
   if (rope && !positions) return fail(MI355X_GA_INVALID_ARGUMENT, "positions is NULL with RoPE on");
   if (scaled && (!k_scale || !v_scale))
     return fail(MI355X_GA_INVALID_ARGUMENT, "k_scale/v_scale are NULL on the scaled path");
-  int rc = check_workspace(ctx, workspace, workspace_bytes);
+  int rc = fixed ? MI355X_GA_OK : check_workspace(ctx, workspace, workspace_bytes);
   if (rc) return rc;
   if (reinterpret_cast<uintptr_t>(qkv) % 16 || reinterpret_cast<uintptr_t>(k_cache) % 16 ||
       reinterpret_cast<uintptr_t>(v_cache) % 16 || reinterpret_cast<uintptr_t>(out) % 8)
@@ -361,7 +390,7 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   if (rc) return rc;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  const Regions reg = fixed ? *fixed : workspace_regions(ctx, workspace);
 
   StepParams sp{};
   sp.qkv = reinterpret_cast<const uint16_t*>(qkv);
@@ -374,10 +403,10 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   sp.k_scale = k_scale;
   sp.v_scale = v_scale;
   sp.out = reinterpret_cast<uint16_t*>(out);
-  sp.q_out = ws;
-  sp.part_o = reinterpret_cast<_Float16*>(ws + ctx->po_off);
-  sp.part_ml = reinterpret_cast<float*>(ws + ctx->pml_off);
-  sp.counters = reinterpret_cast<int32_t*>(ws + ctx->cnt_off);
+  sp.q_out = reg.q;
+  sp.part_o = reinterpret_cast<_Float16*>(reg.po);
+  sp.part_ml = reinterpret_cast<float*>(reg.pml);
+  sp.counters = reg.counters;
   sp.num_pages = c.num_pages;
   sp.num_rows = c.num_pages * (int64_t)c.page_size;
   sp.batch = c.batch;
@@ -405,7 +434,7 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   std::memcpy(sp.inv_freq, ctx->inv_freq, sizeof sp.inv_freq);
 
   hipEvent_t* ev = nullptr;
-  if (ctx->timing) {
+  if (ctx->timing && !fixed) {  // the no-allocation entry point creates no events
     if (ctx->events_used + 2 > ctx->events.size()) {
       for (int k = 0; k < 2; ++k) {
         hipEvent_t e;
@@ -503,6 +532,91 @@ int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
     return fail(MI355X_GA_INVALID_ARGUMENT, "sparse_step on a dense config (sparse_block 0)");
   return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, block_idx, k_cache,
                   v_cache, k_scale, v_scale, out, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- The step without allocation: a static scratch array per GPU ----------
+// For callers that cannot call hipMalloc (code under HIP graph capture, tight
+// serving loops, harnesses that forbid allocation).  `scratch` is this
+// module's device global, so every GPU the library runs on holds its own copy,
+// at its own address, until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: the address hipGetSymbolAddress returns
+// on each device is used instead.  Layout: the counters first (zeroed once
+// per device; every completed step leaves them at zero again), then the
+// partial o / l, the partial (m, l) and q, each 256-byte aligned.
+namespace {
+constexpr size_t kScratchBytes = size_t(32) << 20;          // 32 MiB per GPU
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;   // 16,384 int32 counters
+constexpr int kMaxScratchDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch[kMaxScratchDevices];  // device address of `scratch` per device; null until set up
+
+// The calling thread's current device must be `device`.  The first call on a
+// device takes the array's address there and zeroes its counters with a
+// kernel on `stream` (stream-ordered before the step that follows).
+int scratch_on(int device, hipStream_t stream, uint8_t** out) {
+  if (device < 0 || device >= kMaxScratchDevices)
+    return fail(MI355X_GA_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", device,
+                kMaxScratchDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[device]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MI355X_GA_HIP_ERROR, "hipGetSymbolAddress(scratch) on device %d: %s", device,
+                  hipGetErrorString(e));
+    const hipError_t z = launch_zero_counters(reinterpret_cast<int32_t*>(ptr),
+                                              (int)(kScratchCounterBytes / sizeof(int32_t)), stream);
+    if (z != hipSuccess)
+      return fail(MI355X_GA_HIP_ERROR, "zeroing the scratch counters: %s", hipGetErrorString(z));
+    g_scratch[device] = reinterpret_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch[device];
+  return MI355X_GA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mi355x_gated_attn_step_noalloc(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                   const int64_t* positions, const int64_t* cache_loc,
+                                   const int32_t* cache_seqlens, const int32_t* page_table,
+                                   const int32_t* seq_lens, void* k_cache, void* v_cache,
+                                   const float* k_scale, const float* v_scale, void* out,
+                                   void* stream) {
+  (void)seq_lens;
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
+  if (ctx->cfg.batch == 0) return ok();
+  const size_t need = align_up(ctx->po_bytes, 256) + align_up(ctx->pml_bytes, 256) +
+                      align_up(ctx->q_bytes, 256);
+  if ((size_t)ctx->n_counters * sizeof(int32_t) > kScratchCounterBytes ||
+      need > kScratchBytes - kScratchCounterBytes)
+    return fail(MI355X_GA_WORKSPACE_TOO_SMALL,
+                "the plan needs %zu bytes of scratch and %lld counters; the static scratch holds "
+                "%zu bytes and %zu counters (use mi355x_gated_attn_step with a workspace)",
+                need, (long long)ctx->n_counters, kScratchBytes - kScratchCounterBytes,
+                kScratchCounterBytes / sizeof(int32_t));
+  int rc = check_device(ctx);
+  if (rc) return rc;
+  uint8_t* base = nullptr;
+  rc = scratch_on(ctx->device, reinterpret_cast<hipStream_t>(stream), &base);
+  if (rc) return rc;
+  Regions r;
+  r.counters = reinterpret_cast<int32_t*>(base);
+  r.po = base + kScratchCounterBytes;
+  r.pml = r.po + align_up(ctx->po_bytes, 256);
+  r.q = r.pml + align_up(ctx->pml_bytes, 256);
+  return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, nullptr, k_cache,
+                  v_cache, k_scale, v_scale, out, nullptr, 0, stream, nullptr, -1, nullptr, 0, &r);
 }
 
 void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx) {

@@ -204,6 +204,34 @@ int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const in
                            void* v_cache, const float* k_scale, const float* v_scale, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mi355x_gated_attn_step without a workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing and calls no
+ * allocating routine.  q, the split partials and the counters live in a
+ * static device array of the library, 32 MiB per GPU (the counters in its
+ * first 64 KiB), held by each GPU the library runs on until the process
+ * ends.  The first call on a device takes the array's address there and
+ * zeroes its counters with one extra small kernel on `stream`; every
+ * completed step leaves them at zero.  Every call on a GPU shares that GPU's
+ * array and finds the last call's contents in it: calls that overlap on one
+ * GPU (other streams, other threads, other contexts) race and must be
+ * ordered by the caller.  The timing hook does not record these calls.
+ * Arguments, effects and results are those of mi355x_gated_attn_step (same
+ * kernels, same outputs and cache writes) without workspace and
+ * workspace_bytes; the config must be dense (sparse_block 0).
+ * MI355X_GA_WORKSPACE_TOO_SMALL when the plan needs more than the array holds
+ * (32 MiB - 64 KiB of partials and q, 16,384 counters: e.g. an extend block
+ * of more than about 31k new tokens); MI355X_GA_UNSUPPORTED for a device
+ * index above 63; otherwise as mi355x_gated_attn_step.
+ */
+int mi355x_gated_attn_step_noalloc(mi355x_gated_attn_ctx* ctx, const void* qkv,
+                                   const int64_t* positions, const int64_t* cache_loc,
+                                   const int32_t* cache_seqlens, const int32_t* page_table,
+                                   const int32_t* seq_lens, void* k_cache, void* v_cache,
+                                   const float* k_scale, const float* v_scale, void* out,
+                                   void* stream);
+
 /* Release a context (NULL is ignored).  Does not synchronise. */
 void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx);
 

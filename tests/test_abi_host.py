@@ -597,3 +597,27 @@ def test_binding_checks_the_variants_own_tensors(L):
         ga.mi355x_gated_attn_destroy(ctx)
     with pytest.raises(ValueError, match="unknown or destroyed"):
         ga.mi355x_gated_attn_step_meta(ctx, i32(3), i32(120), i64(6), i64(6), i32(3))
+
+
+def test_noalloc_step_rejects_plans_beyond_its_static_scratch(L):
+    """The no-allocation step refuses, before touching a device, a plan whose
+    q and partials exceed the static scratch (an extend block of 65,536
+    tokens needs 64 MiB of q alone), and an unplanned or NULL context."""
+    big = cfg(batch=1, q_len=65536, window=2048)
+    ctx = ga.mi355x_gated_attn_prepare(big)
+    try:
+        assert L.mi355x_gated_attn_step_noalloc(ctx, *([None] * 12)) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "plan" in ga.mi355x_gated_attn_last_error()
+        ga.mi355x_gated_attn_plan(ctx, 70000, 0)
+        assert L.mi355x_gated_attn_step_noalloc(ctx, *([None] * 12)) == \
+            ga.MI355X_GA_WORKSPACE_TOO_SMALL
+        assert "static scratch" in ga.mi355x_gated_attn_last_error()
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    assert L.mi355x_gated_attn_step_noalloc(None, *([None] * 12)) == ga.MI355X_GA_INVALID_ARGUMENT
+    small = ga.mi355x_gated_attn_prepare(cfg(batch=0))
+    try:
+        ga.mi355x_gated_attn_plan(small, 100, 0)
+        assert L.mi355x_gated_attn_step_noalloc(small, *([None] * 12)) == ga.MI355X_GA_OK
+    finally:
+        ga.mi355x_gated_attn_destroy(small)
