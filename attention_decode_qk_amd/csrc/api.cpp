@@ -301,9 +301,13 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
   if (rc) return rc;
   rc = check_device(ctx);
   if (rc) return rc;
-  int32_t* counters = reinterpret_cast<int32_t*>(reinterpret_cast<uint8_t*>(workspace) + ctx->cnt_off);
-  hipError_t e = launch_zero_counters(counters, (int)ctx->n_counters,
-                                     reinterpret_cast<hipStream_t>(stream));
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_zero_counters(reinterpret_cast<int32_t*>(ws + ctx->cnt_off),
+                                      (int)ctx->n_counters, st);
+  // The decode step's partial slots start empty (every word the sentinel).
+  if (e == hipSuccess && ctx->cfg.q_len <= kMaxQLen)
+    e = launch_fill_sentinel(ws + ctx->po_off, ctx->pml_off + ctx->pml_bytes - ctx->po_off, st);
   if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -544,10 +548,13 @@ int mi355x_gated_attn_sparse_step(mi355x_gated_attn_ctx* ctx, const void* qkv,
 // array's name to a kernel or a copy: the address hipGetSymbolAddress returns
 // on each device is used instead.  Layout: the counters first (zeroed once
 // per device; every completed step leaves them at zero again), then the
-// partial o / l, the partial (m, l) and q, each 256-byte aligned.
+// decode steps' partial slots (set to the empty-slot sentinel once per
+// device; every completed decode step leaves them so again), then the extend
+// steps' partials and q, each 256-byte aligned.
 namespace {
 constexpr size_t kScratchBytes = size_t(32) << 20;          // 32 MiB per GPU
 constexpr size_t kScratchCounterBytes = size_t(64) << 10;   // 16,384 int32 counters
+constexpr size_t kScratchSlotBytes = size_t(8) << 20;       // decode partial slots
 constexpr int kMaxScratchDevices = 64;
 }  // namespace
 
@@ -572,10 +579,13 @@ int scratch_on(int device, hipStream_t stream, uint8_t** out) {
     if (e != hipSuccess || !ptr)
       return fail(MI355X_GA_HIP_ERROR, "hipGetSymbolAddress(scratch) on device %d: %s", device,
                   hipGetErrorString(e));
-    const hipError_t z = launch_zero_counters(reinterpret_cast<int32_t*>(ptr),
-                                              (int)(kScratchCounterBytes / sizeof(int32_t)), stream);
+    hipError_t z = launch_zero_counters(reinterpret_cast<int32_t*>(ptr),
+                                        (int)(kScratchCounterBytes / sizeof(int32_t)), stream);
+    if (z == hipSuccess)
+      z = launch_fill_sentinel(reinterpret_cast<uint8_t*>(ptr) + kScratchCounterBytes, kScratchSlotBytes,
+                               stream);
     if (z != hipSuccess)
-      return fail(MI355X_GA_HIP_ERROR, "zeroing the scratch counters: %s", hipGetErrorString(z));
+      return fail(MI355X_GA_HIP_ERROR, "preparing the scratch: %s", hipGetErrorString(z));
     g_scratch[device] = reinterpret_cast<uint8_t*>(ptr);
   }
   *out = g_scratch[device];
@@ -596,14 +606,19 @@ int mi355x_gated_attn_step_noalloc(mi355x_gated_attn_ctx* ctx, const void* qkv,
   if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
   if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
   if (ctx->cfg.batch == 0) return ok();
-  const size_t need = align_up(ctx->po_bytes, 256) + align_up(ctx->pml_bytes, 256) +
-                      align_up(ctx->q_bytes, 256);
-  if ((size_t)ctx->n_counters * sizeof(int32_t) > kScratchCounterBytes ||
-      need > kScratchBytes - kScratchCounterBytes)
+  // Decode partials live in the sentinel slot region, extend partials after it.
+  const bool decode = ctx->cfg.q_len <= kMaxQLen;
+  const size_t parts = align_up(ctx->po_bytes, 256) + align_up(ctx->pml_bytes, 256);
+  const size_t slot_need = decode ? parts : 0;
+  const size_t rest_need = (decode ? 0 : parts) + align_up(ctx->q_bytes, 256);
+  const size_t rest_have = kScratchBytes - kScratchCounterBytes - kScratchSlotBytes;
+  if ((size_t)ctx->n_counters * sizeof(int32_t) > kScratchCounterBytes || slot_need > kScratchSlotBytes ||
+      rest_need > rest_have)
     return fail(MI355X_GA_WORKSPACE_TOO_SMALL,
-                "the plan needs %zu bytes of scratch and %lld counters; the static scratch holds "
-                "%zu bytes and %zu counters (use mi355x_gated_attn_step with a workspace)",
-                need, (long long)ctx->n_counters, kScratchBytes - kScratchCounterBytes,
+                "the plan needs %zu bytes of decode partial slots, %zu bytes of other scratch and "
+                "%lld counters; the static scratch holds %zu, %zu and %zu (use "
+                "mi355x_gated_attn_step with a workspace)",
+                slot_need, rest_need, (long long)ctx->n_counters, kScratchSlotBytes, rest_have,
                 kScratchCounterBytes / sizeof(int32_t));
   int rc = check_device(ctx);
   if (rc) return rc;
@@ -612,9 +627,11 @@ int mi355x_gated_attn_step_noalloc(mi355x_gated_attn_ctx* ctx, const void* qkv,
   if (rc) return rc;
   Regions r;
   r.counters = reinterpret_cast<int32_t*>(base);
-  r.po = base + kScratchCounterBytes;
+  uint8_t* const slots = base + kScratchCounterBytes;
+  uint8_t* const rest = slots + kScratchSlotBytes;
+  r.po = decode ? slots : rest;
   r.pml = r.po + align_up(ctx->po_bytes, 256);
-  r.q = r.pml + align_up(ctx->pml_bytes, 256);
+  r.q = decode ? rest : r.pml + align_up(ctx->pml_bytes, 256);
   return run_step(ctx, qkv, positions, cache_loc, cache_seqlens, page_table, nullptr, k_cache,
                   v_cache, k_scale, v_scale, out, nullptr, 0, stream, nullptr, -1, nullptr, 0, &r);
 }

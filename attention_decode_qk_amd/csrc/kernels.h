@@ -56,7 +56,9 @@ struct StepParams {
   uint8_t* q_out;                // e4m3 [T, kQHeads, kHeadDim] (workspace)
   _Float16* part_o;              // f16 [B, S, L*kQHeads, kHeadDim]: o / l of the split
   float* part_ml;                // fp32 [B, S, L*kQHeads, 2]: running max (log2 units), sum
-  int32_t* counters;             // [B, G] finished units per (request, token group), 0 between steps
+                                 // (q_len <= kMaxQLen: every 8-byte word of both is the empty-slot
+                                 // sentinel between steps)
+  int32_t* counters;             // extend: one per unit, finished splits, 0 between steps
   int64_t num_pages;
   int64_t num_rows;              // num_pages * page_size (< 2^31)
   int32_t batch;
@@ -126,5 +128,8 @@ struct MetaParams {
 };
 hipError_t launch_step_meta(const MetaParams& m, hipStream_t stream);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t stream);
+// Set every 8-byte word of [p, p + bytes) to the decode step's empty-slot
+// sentinel (all bits set); bytes is a multiple of 8.
+hipError_t launch_fill_sentinel(void* p, size_t bytes, hipStream_t stream);
 
 }  // namespace mi355x_ga

@@ -47,6 +47,40 @@ __device__ inline uint2 load_coherent_h4(const _Float16* src) {
   return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
 }
 
+// The decode step's split exchange.  Every 8-byte word of a partial slot
+// holds the sentinel (all bits set) between steps: a producer stores its words
+// (never the sentinel: a value with that pattern, which only a NaN payload
+// could give, is stored as a canonical NaN instead) and the group's combiner
+// polls them until no sentinel is left, then stores the sentinel back.
+constexpr uint64_t kPartialSentinel = ~0ull;
+constexpr uint64_t kEmptyPartialMl = 0x00000000FF800000ull;  // (m, l) = (-inf, 0)
+constexpr uint64_t kPartialWaitTicks = 10000000;             // 100 ms of the 100 MHz wall clock
+
+__device__ inline void publish_word(void* dst, uint64_t v, uint64_t nan_form) {
+  if (v == kPartialSentinel) v = nan_form;
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void publish_ml(float* dst, float m, float l) {
+  publish_word(dst, (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(l) << 32),
+               0x7FC000007FC00000ull);
+}
+
+__device__ inline void publish_h4(_Float16* dst, float a, float b, float c, float d) {
+  const v2h lo = {(_Float16)a, (_Float16)b}, hi = {(_Float16)c, (_Float16)d};
+  publish_word(dst, (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32),
+               0x7E007E007E007E00ull);
+}
+
+__device__ inline uint64_t poll_word(const void* src) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ inline void reset_word(void* dst) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), kPartialSentinel, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ inline float h_lo(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[0]; }
 __device__ inline float h_hi(uint32_t w) { return (float)__builtin_bit_cast(v2h, w)[1]; }
 

@@ -28,17 +28,23 @@
 //     by more than 2^8); P in f16; PV as O^T = V^T P^T on
 //     v_mfma_f32_16x16x32_f16 with V transposed in registers and widened
 //     exactly to f16.
-//  C. The four waves merge through LDS and publish the unit's partial (o / l
-//     in f16, m and l in fp32) with device-coherent stores; an atomic counter per (request, token group)
-//     elects the group's last unit, which reads the group's partials with
-//     device-coherent loads, merges them, rounds the attention output to bf16,
-//     applies RMSNorm x sigmoid(gate), writes bf16 out and re-arms the counter.
+//  C. The waves merge through LDS.  A request-group's split 0 is its combiner;
+//     the other splits publish their partial (o / l in f16, m and l in fp32),
+//     each 8-byte word one device-coherent store, and leave without waiting.
+//  D. The combiner keeps its own partial in registers, polls the others' words
+//     until none holds the empty-slot sentinel, merges them (log-sum-exp),
+//     rounds the attention output to bf16, applies RMSNorm x sigmoid(gate),
+//     writes bf16 out and sets the consumed words back to the sentinel.
 //
-// Cross-workgroup visibility (C): partials are written and read only with
-// agent-scope atomic accesses (sc1: coherent across the XCDs' L2 caches), and
-// each wave waits for its own stores to complete (s_waitcnt vmcnt(0)) before
-// the workgroup barrier that precedes the counter increment.  No L2 write-back
-// or invalidate is needed, unlike a generic device-scope fence.
+// Cross-workgroup visibility (C, D): the partials are written and read only
+// with agent-scope atomic accesses (sc1: coherent across the XCDs' L2 caches;
+// workgroup-scope loads can return a stale line even within one XCD), and an
+// 8-byte aligned atomic access is single-copy atomic, so a word is either the
+// sentinel or the producer's value.  No unit waits for its own stores, no
+// counter is taken, and no L2 write-back or invalidate is needed.  The
+// combiner's wait is bounded (100 ms): a split that never arrives (the launch's
+// workgroups could not all run) gives NaN output instead of a hang.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernels.h"
@@ -158,7 +164,6 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   __shared__ float s_cs[kMaxQLen][kHeadDim / 2][2];
   __shared__ __align__(16) float s_mo[KW][kRows][kHeadDim];
   __shared__ __align__(16) float s_ml[KW][kRows][2];
-  __shared__ int s_last;
   // SP (page-list-driven decode): the request's block lists, one per KV head.
   __shared__ int s_blk[SP ? kKvHeads : 1][SP ? kMaxSparseTopk : 1];
 
@@ -868,9 +873,9 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // Partial rows are ((sbase + kc) * L + token) * 16 + head.
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
   const int64_t base = (int64_t)sbase * stride + (int64_t)t_lo * kQHeads + h;
-  int32_t* counter = p.counters + (kOneGroup ? b : b * p.tgroups + tg);
-  float own_m[TPT], own_l[TPT], own_o[TPT][4];  // a single split's result
-  if (nsp > 1) {
+  if (nsp > 1 && kc != 0) {
+    // A producer: merge the waves and publish the unit's partial, each 8-byte
+    // word one device-coherent store (never the sentinel pattern); no wait.
     const int64_t prow0 = ((int64_t)ru * L + t_lo) * kQHeads;
     for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
       const int cr = idx >> 4, cc = (idx & 15) * 4;
@@ -879,35 +884,18 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       merge(cr, cc, mx, lsum, o);
       // o / l is a weighted mean of V codes (|.| <= 448): f16 holds it.
       const float rl = lsum > 0.0f ? __builtin_amdgcn_rcpf(lsum) : 0.0f;
-      store_coherent_h4(p.part_o + (prow0 + cr) * kHeadDim + cc, o.x * rl, o.y * rl, o.z * rl, o.w * rl);
-      if (cc == 0) store_coherent(p.part_ml + (prow0 + cr) * 2, mx, lsum);
+      publish_h4(p.part_o + (prow0 + cr) * kHeadDim + cc, o.x * rl, o.y * rl, o.z * rl, o.w * rl);
+      if (cc == 0) publish_ml(p.part_ml + (prow0 + cr) * 2, mx, lsum);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores are complete
-    __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == nsp - 1;
-    __syncthreads();
-    if (!s_last) return;
-  } else {  // a single split is its own combine: no publish, no counter
-#pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      const int ti = th + TS * k;
-      own_m[k] = -INFINITY;
-      own_l[k] = 0.0f;
-      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ti < t_n) merge(ti * kQHeads + h, c4, own_m[k], own_l[k], o);
-      own_o[k][0] = o.x;
-      own_o[k][1] = o.y;
-      own_o[k][2] = o.z;
-      own_o[k][3] = o.w;
-    }
+    return;
   }
 
-  // ---------------- D. combine + gated epilogue (last unit of the group) ----------------
-  // With several splits the partials (the unit's own included, as published)
-  // are read KS splits at a time for all the thread's tokens at once, so the
-  // chain of device-coherent round trips is ceil(splits / KS) long whatever the
-  // number of tokens; a single split is taken from registers.
+  // ---------------- D. combine + gated epilogue (split 0 of the group) ----------------
+  // The unit's own partial comes from its waves' LDS slots; the other splits'
+  // are polled until none of their words holds the sentinel (a producer
+  // publishes without waiting, so the first poll usually finds them), KS
+  // splits at a time for all the thread's tokens, then merged.  The consumed
+  // words are set back to the sentinel for the next step.
   constexpr int KS = TPT >= 4 ? 4 : (TPT == 3 ? 5 : (TPT == 2 ? 8 : 16));
   uint2 graw[TPT];
 #pragma unroll
@@ -921,42 +909,69 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   float mrun[TPT], lrun[TPT], o[TPT][4];
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
+    const int ti = th + TS * k;
     mrun[k] = -INFINITY;
     lrun[k] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) o[k][c] = 0.0f;
+    float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ti < t_n) merge(ti * kQHeads + h, c4, mrun[k], lrun[k], ov);
+    o[k][0] = ov.x;
+    o[k][1] = ov.y;
+    o[k][2] = ov.z;
+    o[k][3] = ov.w;
   }
-  if (nsp == 1) {
+  bool lost = false;  // a split never arrived within the wait bound
+  const uint64_t t_wait0 = wall_clock64();
+  for (int s0 = 1; nsp > 1 && s0 < nsp; s0 += KS) {
+    uint64_t mlw[TPT][KS], ow[TPT][KS];
+    auto ml_at = [&](int q, int k) { return p.part_ml + (base + (int64_t)(s0 + q) * stride + (th + TS * k) * kQHeads) * 2; };
+    auto o_at = [&](int q, int k) { return p.part_o + (base + (int64_t)(s0 + q) * stride + (th + TS * k) * kQHeads) * kHeadDim + c4; };
+    auto used = [&](int q, int k) { return th + TS * k < t_n && s0 + q < nsp; };
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      mrun[k] = own_m[k];
-      lrun[k] = own_l[k];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) o[k][c] = own_o[k][c];
-    }
-  }
-  for (int s0 = 0; nsp > 1 && s0 < nsp; s0 += KS) {
-    float2 ml[TPT][KS];
-    uint2 oh[TPT][KS];
-#pragma unroll
-    for (int q = 0; q < KS; ++q) {
+    for (int q = 0; q < KS; ++q)
 #pragma unroll
       for (int k = 0; k < TPT; ++k) {
-        const int ti = th + TS * k;
-        ml[k][q] = make_float2(-INFINITY, 0.0f);
-        oh[k][q] = make_uint2(0, 0);
-        if (ti < t_n && s0 + q < nsp) {
-          const int64_t pr = base + (int64_t)(s0 + q) * stride + ti * kQHeads;
-          ml[k][q] = load_coherent(p.part_ml + pr * 2);
-          oh[k][q] = load_coherent_h4(p.part_o + pr * kHeadDim + c4);
+        mlw[k][q] = kEmptyPartialMl;
+        ow[k][q] = 0;
+        if (used(q, k)) {
+          mlw[k][q] = poll_word(ml_at(q, k));
+          ow[k][q] = poll_word(o_at(q, k));
         }
       }
+    // Every lane waits for its own words; the wait is bounded.
+    for (;;) {
+      bool pending = false;
+#pragma unroll
+      for (int q = 0; q < KS; ++q)
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) pending |= mlw[k][q] == kPartialSentinel || ow[k][q] == kPartialSentinel;
+      if (!pending) break;
+      if (wall_clock64() - t_wait0 > kPartialWaitTicks) {
+        lost = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int q = 0; q < KS; ++q)
+#pragma unroll
+        for (int k = 0; k < TPT; ++k) {
+          if (mlw[k][q] == kPartialSentinel) mlw[k][q] = poll_word(ml_at(q, k));
+          if (ow[k][q] == kPartialSentinel) ow[k][q] = poll_word(o_at(q, k));
+        }
     }
+    // The words are consumed: back to the sentinel for the next step.
+#pragma unroll
+    for (int q = 0; q < KS; ++q)
+#pragma unroll
+      for (int k = 0; k < TPT; ++k)
+        if (used(q, k)) {
+          reset_word(ml_at(q, k));
+          reset_word(o_at(q, k));
+        }
 #pragma unroll
     for (int k = 0; k < TPT; ++k) {
       float mc = mrun[k];
 #pragma unroll
-      for (int q = 0; q < KS; ++q) mc = fmaxf(mc, ml[k][q].x);
+      for (int q = 0; q < KS; ++q) mc = fmaxf(mc, __uint_as_float((uint32_t)mlw[k][q]));
       const float muse = mc == -INFINITY ? 0.0f : mc;
       const float a = __builtin_amdgcn_exp2f(mrun[k] - muse);
       lrun[k] *= a;
@@ -965,12 +980,13 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
       for (int q = 0; q < KS; ++q) {
         // A split's weight is its l times 2^(m - max); its partial is o / l.
-        const float wk = __builtin_amdgcn_exp2f(ml[k][q].x - muse) * ml[k][q].y;
+        const float wk = __builtin_amdgcn_exp2f(__uint_as_float((uint32_t)mlw[k][q]) - muse) *
+                         __uint_as_float((uint32_t)(mlw[k][q] >> 32));
         lrun[k] += wk;
-        o[k][0] += wk * h_lo(oh[k][q].x);
-        o[k][1] += wk * h_hi(oh[k][q].x);
-        o[k][2] += wk * h_lo(oh[k][q].y);
-        o[k][3] += wk * h_hi(oh[k][q].y);
+        o[k][0] += wk * h_lo((uint32_t)ow[k][q]);
+        o[k][1] += wk * h_hi((uint32_t)ow[k][q]);
+        o[k][2] += wk * h_lo((uint32_t)(ow[k][q] >> 32));
+        o[k][3] += wk * h_hi((uint32_t)(ow[k][q] >> 32));
       }
       mrun[k] = mc;
     }
@@ -983,8 +999,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     const int ti = th + TS * k;
     // Output-side arithmetic runs in fp32 on the hardware reciprocal, rsqrt and
     // exp (each within a couple of fp32 ulps); the result is rounded to bf16
-    // (2^-9 relative) once at the end.
-    const float inv = lrun[k] > 0.0f ? vs * __builtin_amdgcn_rcpf(lrun[k]) : 0.0f;
+    // (2^-9 relative) once at the end.  A lost split gives NaN, not a hang.
+    const float inv = lost ? __builtin_nanf("") : (lrun[k] > 0.0f ? vs * __builtin_amdgcn_rcpf(lrun[k]) : 0.0f);
     float y[4];
     float ss = 0.0f;
 #pragma unroll
@@ -1003,7 +1019,6 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
           make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
   }
-  if (tid == 0 && nsp > 1) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int LU, bool HS, int KW, bool SP = false, bool BAL = false>
@@ -1034,6 +1049,11 @@ __global__ void zero_counters_kernel(int32_t* c, int n) {
   if (i < n) c[i] = 0;
 }
 
+__global__ void fill_sentinel_kernel(uint64_t* w, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    w[i] = kPartialSentinel;
+}
+
 }  // namespace
 
 hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_start) {
@@ -1059,6 +1079,15 @@ hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_
     case 4: return launch_served<4>(p, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_fill_sentinel(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n = (int64_t)(bytes / sizeof(uint64_t));
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_sentinel_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<uint64_t*>(p), n);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t stream) {

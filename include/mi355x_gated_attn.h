@@ -123,10 +123,13 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
                            size_t* workspace_bytes, int32_t* num_splits_out);
 
 /*
- * Zero the cross-workgroup counters of a freshly allocated workspace.  Call
- * once per workspace (per ctx plan) before its first step; every completed step
- * leaves the workspace ready for the next one.  Asynchronous on `stream`; a
- * kernel launch, never a memset, so it may also be captured in a HIP graph.
+ * Prepare a freshly allocated workspace for the ctx's plan: zero its
+ * cross-workgroup counters (q_len > 8) and set every word of its split-partial
+ * slots to the empty pattern (q_len <= 8).  Call once per workspace (per ctx
+ * plan) before its first step, and again before a workspace serves another
+ * plan; every completed step leaves the workspace ready for the next one.
+ * Asynchronous on `stream`; kernel launches, never a memset, so it may also be
+ * captured in a HIP graph.
  */
 int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace,
                                      size_t workspace_bytes, void* stream);
@@ -194,9 +197,16 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
  *                  [B*L, Hq, D]; then split partials and B*G int32
  *                  counters (G token groups per request, from the plan; for
  *                  q_len > 8 partials only when split, and one counter per
- *                  (request, 16-token tile, KV head)).
+ *                  (request, 16-token tile, KV head); q_len <= 8 uses no
+ *                  counter: its partial slots are empty between steps).
  * Calls that share a workspace, or write the same cache rows, must be ordered
  * on one stream.  Returns MI355X_GA_OK with no launch when B == 0.
+ * With q_len <= 8 and more than one split, the first split of each request
+ * (and token group) waits for the others' partials: the launch's B*G*S
+ * workgroups (at most a few hundred whenever S > 1) must be able to run
+ * together, as they do on an MI355X unless other work holds every compute
+ * unit; a split that has not arrived after 100 ms makes that group's output
+ * NaN rather than hang the device.
  */
 int mi355x_gated_attn_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positions,
                            const int64_t* cache_loc, const int32_t* cache_seqlens,
