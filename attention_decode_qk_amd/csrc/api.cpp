@@ -43,13 +43,10 @@ int ok() {
   return MI355X_GA_OK;
 }
 
-constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs x 32 CUs
-// Work units per compute unit the automatic plan aims for.  Measured on the
-// B=32, L=1, window-2048 decode (units of 4 waves each): one unit per CU (S=8)
-// 19.9 us per step, two (S=16) 25.0 us -- fewer, longer units shorten the
-// merge of the partials more than they lengthen each unit's key walk.
-int units_per_cu(int q_len) { (void)q_len; return 1; }
+constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs x 32 CUs; the plan aims at one unit per CU
 constexpr int kMaxSplits = 256;
+constexpr int64_t kPartialRowBytes = kHeadDim * 2 + 8;  // f16 o / l + fp32 (m, l)
+constexpr int64_t kSepCombineBytes = 32 << 10;
 constexpr int64_t kShortKeys = 4096;  // key ranges up to this use groups of two tokens
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -67,6 +64,7 @@ struct mi355x_gated_attn_ctx {
   bool head_split = false;
   int32_t key_waves = kAttnWaves;
   bool balanced = false;  // splits per request by key count
+  bool sep_combine = false;  // partials merged by a second launch
   size_t q_bytes = 0, po_off = 0, pml_off = 0, cnt_off = 0, ws_bytes = 0;
   size_t po_bytes = 0, pml_bytes = 0;  // partial o / l and (m, l) region sizes
   int64_t n_counters = 0;              // int32 counters (B x groups)
@@ -258,7 +256,7 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (s == 0) {
     const int64_t min_keys_per_split = (int64_t)key_waves * kKeyBlock;  // a block per wave
     const int64_t by_len = std::max<int64_t>(1, (keys + min_keys_per_split - 1) / min_keys_per_split);
-    const int64_t target = (int64_t)kComputeUnits * units_per_cu(c.q_len);
+    const int64_t target = kComputeUnits;
     const int64_t units = (int64_t)c.batch * groups;  // units per split
     const int64_t by_batch = units > 0 ? (target + units - 1) / units : 1;
     s = (int32_t)std::max<int64_t>(1, std::min<int64_t>({by_len, by_batch, (int64_t)kMaxSplits}));
@@ -286,6 +284,12 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   // units with both KV heads per wave only).  Measured (B = 8, L = 8, 64k-128k
   // keys, S = 16): 94.1 against 84.6 us per step.
   ctx->balanced = !sparse && !head_split && c.window == 0 && c.batch > 1 && c.batch <= 64 && s > 1;
+  // The partials of a request-group are merged by its first split, which reads
+  // the others' (S - 1) * rows * 136 bytes through one compute unit with
+  // device-coherent loads; beyond kSepCombineBytes a second launch merges them
+  // over the whole chip with plain loads instead (one more launch, ~1.6 us).
+  const int64_t lu = tokens_per_unit(c.q_len, groups);
+  ctx->sep_combine = s > 1 && (int64_t)(s - 1) * lu * kQHeads * kPartialRowBytes > kSepCombineBytes;
   ctx->planned = true;
   if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
   if (num_splits_out) *num_splits_out = s;
@@ -420,6 +424,7 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   sp.balanced = ctx->balanced ? 1 : 0;
   sp.head_split = ctx->head_split ? 1 : 0;
   sp.key_waves = ctx->key_waves;
+  sp.sep_combine = ctx->sep_combine ? 1 : 0;
   sp.max_pages = c.max_pages;
   sp.page_size = c.page_size;
   sp.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;
@@ -606,8 +611,9 @@ int mi355x_gated_attn_step_noalloc(mi355x_gated_attn_ctx* ctx, const void* qkv,
   if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
   if (!ctx->planned) return fail(MI355X_GA_INVALID_ARGUMENT, "step before plan");
   if (ctx->cfg.batch == 0) return ok();
-  // Decode partials live in the sentinel slot region, extend partials after it.
-  const bool decode = ctx->cfg.q_len <= kMaxQLen;
+  // Partials exchanged within the decode launch live in the sentinel slot
+  // region; extend partials and separately combined ones after it.
+  const bool decode = ctx->cfg.q_len <= kMaxQLen && !ctx->sep_combine;
   const size_t parts = align_up(ctx->po_bytes, 256) + align_up(ctx->pml_bytes, 256);
   const size_t slot_need = decode ? parts : 0;
   const size_t rest_need = (decode ? 0 : parts) + align_up(ctx->q_bytes, 256);

@@ -68,6 +68,8 @@ struct StepParams {
   int32_t balanced;              // 1: splits per request by key count (batch <= 64), else S each
   int32_t head_split;            // 1: eight waves per unit, one KV head each
   int32_t key_waves;             // waves per KV head taking blocks round-robin (4, or 8 at q_len 1)
+  int32_t sep_combine;           // 1: every unit publishes its partial and a second launch
+                                 // (combine_kernel) merges them and runs the epilogue
   int32_t max_pages;
   int32_t page_size;
   int32_t page_shift;            // log2(page_size) if a power of two, else -1

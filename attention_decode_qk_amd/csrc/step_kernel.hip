@@ -139,6 +139,56 @@ __device__ inline void norm_rope8(const float (&x)[8], bool rope, const float (*
   }
 }
 
+// The balanced deal (batch <= 64; lane l stands for request l): the first of
+// the token group's B * S units that request l gets, R_l = l + floor(X * K_<l
+// / K) with X = B * (S - 1), K_<l the keys of the requests before l and K all
+// of them (R_B = B * S), so that every unit carries about K / (B * S) keys;
+// csl receives request l's cached length.  Every wave of a workgroup computes
+// the same values.
+__device__ inline int balanced_first_unit(const StepParams& p, int L, int lane, int& csl) {
+  const int bs = p.batch * p.splits;
+  csl = lane < p.batch ? p.cache_seqlens[lane] : 0;
+  const int firstl = p.window > 0 ? max(0, csl - L - p.window + 1) : 0;
+  const long long kl = max(0, csl - firstl);
+  long long incl = kl;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const long long ktot = __shfl(incl, 63);
+  const int x = bs - p.batch;
+  // Exact in double (x * keys < 2^53); correctly rounded division is monotonic,
+  // so the boundaries strictly increase and the last one is bs.
+  return ktot > 0 ? lane + (int)floor((double)x * (double)(incl - kl) / (double)ktot) : lane * p.splits;
+}
+
+// The gated epilogue of one thread's 4 columns (c4..c4+3 of a head: 16
+// consecutive lanes hold the head's 64 columns): the attention output o / l
+// (times the value descale vs) rounded to bf16, RMSNorm over the head,
+// times sigmoid(gate); bf16 bits of the 4 results packed in a uint2.  Output-
+// side arithmetic runs in fp32 on the hardware reciprocal, rsqrt and exp (each
+// within a couple of fp32 ulps); the result is rounded to bf16 (2^-9
+// relative) once at the end.  A lost split (lost) gives NaN.
+__device__ inline uint2 gated_epilogue(const float (&o)[4], float l, float vs, uint2 graw, bool lost) {
+  const float inv = lost ? __builtin_nanf("") : (l > 0.0f ? vs * __builtin_amdgcn_rcpf(l) : 0.0f);
+  float y[4];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    y[c] = round_bf16(o[c] * inv);  // the attention result is bf16 before the epilogue
+    ss += y[c] * y[c];
+  }
+  ss = sum16(ss);
+  const float r = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + 1.0e-5f);
+  const float gate[4] = {bf16_value(graw.x & 0xffffu), bf16_value(graw.x >> 16), bf16_value(graw.y & 0xffffu),
+                         bf16_value(graw.y >> 16)};
+  uint32_t ob[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[c])));
+  return make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
+}
+
 template <int LU, bool HS, int KW, bool SP, bool BAL>
 __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(StepParams p) {
   // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
@@ -184,21 +234,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     const int bs = p.batch * p.splits;
     ru = kOneGroup ? blockIdx.x : blockIdx.x % bs;
     tg = kOneGroup ? 0 : blockIdx.x / bs;
-    const int csl = lane < p.batch ? p.cache_seqlens[lane] : 0;
-    const int firstl = p.window > 0 ? max(0, csl - L - p.window + 1) : 0;
-    const long long kl = max(0, csl - firstl);
-    long long incl = kl;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const long long v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
-    }
-    const long long ktot = __shfl(incl, 63);
-    const int x = bs - p.batch;
-    // Exact in double (x * keys < 2^53); correctly rounded division is monotonic,
-    // so the boundaries strictly increase and the last one is bs.
-    const int rl = ktot > 0 ? lane + (int)floor((double)x * (double)(incl - kl) / (double)ktot)
-                            : lane * p.splits;
+    int csl;
+    const int rl = balanced_first_unit(p, L, lane, csl);
     b = __popcll(__ballot(lane >= 1 && lane < p.batch && rl <= ru));
     sbase = __builtin_amdgcn_readlane(rl, b);
     nsp = (b + 1 < p.batch ? __builtin_amdgcn_readlane(rl, b + 1) : bs) - sbase;
@@ -873,9 +910,11 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // Partial rows are ((sbase + kc) * L + token) * 16 + head.
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
   const int64_t base = (int64_t)sbase * stride + (int64_t)t_lo * kQHeads + h;
-  if (nsp > 1 && kc != 0) {
+  if (p.sep_combine || (nsp > 1 && kc != 0)) {
     // A producer: merge the waves and publish the unit's partial, each 8-byte
     // word one device-coherent store (never the sentinel pattern); no wait.
+    // With the separate combine every unit is a producer (combine_kernel
+    // merges the partials after this launch).
     const int64_t prow0 = ((int64_t)ru * L + t_lo) * kQHeads;
     for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
       const int cr = idx >> 4, cc = (idx & 15) * 4;
@@ -997,28 +1036,73 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
   for (int k = 0; k < TPT; ++k) {
     const int ti = th + TS * k;
-    // Output-side arithmetic runs in fp32 on the hardware reciprocal, rsqrt and
-    // exp (each within a couple of fp32 ulps); the result is rounded to bf16
-    // (2^-9 relative) once at the end.  A lost split gives NaN, not a hang.
-    const float inv = lost ? __builtin_nanf("") : (lrun[k] > 0.0f ? vs * __builtin_amdgcn_rcpf(lrun[k]) : 0.0f);
-    float y[4];
-    float ss = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      y[c] = round_bf16(o[k][c] * inv);  // the attention result is bf16 before the epilogue
-      ss += y[c] * y[c];
-    }
-    ss = sum16(ss);
-    const float r = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + 1.0e-5f);
-    const float gate[4] = {bf16_value(graw[k].x & 0xffffu), bf16_value(graw[k].x >> 16),
-                           bf16_value(graw[k].y & 0xffffu), bf16_value(graw[k].y >> 16)};
-    uint32_t ob[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ob[c] = bf16_bits(y[c] * r * __builtin_amdgcn_rcpf(1.0f + __expf(-gate[c])));
+    const uint2 ov = gated_epilogue(o[k], lrun[k], vs, graw[k], lost);
     if (ti < t_n)
-      *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
-          make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
+      *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) = ov;
   }
+}
+
+// The separate combine (q_len <= kMaxQLen, when the plan moves the merge of
+// the partials out of the attention launch): one workgroup per token, thread
+// (h, c4) of head h and columns c4..c4+3.  The token's request has nsp
+// partial rows per (token, head), split kc's at ((sbase + kc) * L + t) * 16 +
+// h, merged by log-sum-exp (split weight l * 2^(m - max), partial o / l) and
+// followed by the gated epilogue, exactly as a combining unit would.  The
+// partials come from the previous launch, so plain loads see them.
+__global__ __launch_bounds__(256) void combine_kernel(StepParams p) {
+  constexpr int KS = 16;  // splits per round of loads
+  const int tok = blockIdx.x;
+  const int L = p.q_len;
+  const int b = tok / L, t = tok - b * L;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int h = tid >> 4, c4 = (tid & 15) * 4;
+  int sbase = b * p.splits, nsp = p.splits;
+  if (p.balanced) {
+    int csl;
+    const int rl = balanced_first_unit(p, L, lane, csl);
+    sbase = __builtin_amdgcn_readlane(rl, b);
+    nsp = (b + 1 < p.batch ? __builtin_amdgcn_readlane(rl, b + 1) : p.batch * p.splits) - sbase;
+  }
+  const float vs = p.scaled ? *p.v_scale : 1.0f;
+  const uint2 graw =
+      *reinterpret_cast<const uint2*>(p.qkv + (int64_t)tok * kWidth + kGateOffset + h * kHeadDim + c4);
+  const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
+  const int64_t base = ((int64_t)sbase * L + t) * kQHeads + h;
+  float mrun = -INFINITY, lrun = 0.0f, o[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsp; s0 += KS) {
+    float2 ml[KS];
+    uint2 oh[KS];
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      ml[q] = make_float2(-INFINITY, 0.0f);
+      oh[q] = make_uint2(0, 0);
+      if (s0 + q < nsp) {
+        const int64_t r = base + (int64_t)(s0 + q) * stride;
+        ml[q] = *reinterpret_cast<const float2*>(p.part_ml + r * 2);
+        oh[q] = *reinterpret_cast<const uint2*>(p.part_o + r * kHeadDim + c4);
+      }
+    }
+    float mc = mrun;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) mc = fmaxf(mc, ml[q].x);
+    const float muse = mc == -INFINITY ? 0.0f : mc;
+    const float a = __builtin_amdgcn_exp2f(mrun - muse);
+    lrun *= a;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] *= a;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      const float wk = __builtin_amdgcn_exp2f(ml[q].x - muse) * ml[q].y;
+      lrun += wk;
+      o[0] += wk * h_lo(oh[q].x);
+      o[1] += wk * h_hi(oh[q].x);
+      o[2] += wk * h_lo(oh[q].y);
+      o[3] += wk * h_hi(oh[q].y);
+    }
+    mrun = mc;
+  }
+  *reinterpret_cast<uint2*>(p.out + (int64_t)tok * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
+      gated_epilogue(o, lrun, vs, graw, false);
 }
 
 template <int LU, bool HS, int KW, bool SP = false, bool BAL = false>
@@ -1026,7 +1110,12 @@ hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
   hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW, SP, BAL>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
                      stream, p);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && p.sep_combine) {
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.batch * p.q_len)), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 template <int LU>
