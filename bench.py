@@ -13,13 +13,17 @@ Cold-cache discipline: the steps round-robin over per-layer pools (own K/V
 caches, own page-table permutation and cache rows, own projection rows, same
 lengths), enough of them that one round touches at least 1 GiB -- the bytes
 the steps read and write, not the pools' size -- four times the 256 MB Infinity
-Cache, as a model's layers would.  --shared-table shares pool 0's page table and cache rows
+Cache, as a model's layers would.  After one sweep over every pool the
+warm-up steps run on pools 0 .. W-1 and the timed steps start at pool W, so a
+timed step never reads a pool touched less than a round of pools earlier
+(config.timed_min_reuse_bytes reports the smallest such distance).  --shared-table shares pool 0's page table and cache rows
 instead, as a serving engine that builds them once per step for every layer
 would (measured within noise of the default).  The layer-
 steps are captured in HIP graphs outside the timed region (one graph of W
 warm-up steps, one of exactly K timed steps) and the timed region is one
 replay of the K-step graph, bracketed by synchronisation and HIP events on the
-replay stream.  For q_len <= 8 the step is a single kernel, so the time per
+replay stream (a short untimed GPU spin before the start event lets the host
+finish submitting the graph, so its submission latency is not counted).  For q_len <= 8 the step is a single kernel, so the time per
 step is also the kernel's average duration (the roofline figure); a second,
 eager pass with the library's event hook is reported as well (it includes
 event overhead).  An extend workload (q_len > 8: swa_extend, full_extend) is
@@ -42,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+SPIN_CYCLES = 5_000_000  # GPU spin ahead of a timed replay (about 2 ms at 2.4 GHz)
 METRIC = "µs per layer-step and KV-read HBM GB/s (% of peak), B=32 L=1 16k ctx"
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "f16": 2500.0}  # MI355X dense matrix-core peaks
 
@@ -234,9 +239,43 @@ def load_traffic(workload: str):
     return d.get("traffic_bytes_per_launch")
 
 
+def reuse_distances(before, timed, step_bytes):
+    """For each timed step, the bytes the steps since its pool's previous use
+    touched (each step touches step_bytes), given the pools run before the timed
+    region; None for a pool never used before."""
+    last = {}
+    seq = list(before) + list(timed)
+    out = []
+    for i, li in enumerate(seq):
+        if i >= len(before):
+            out.append(None if li not in last else (i - last[li] - 1) * step_bytes)
+        last[li] = i
+    return out
+
+
+def host_description():
+    """The benchmark host's CPU: logical CPUs visible, usable by this process,
+    and the model name."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
 def cpu_baseline(x, budget_s: float):
-    """The oracle as it stands, single-threaded on this host, on whole steps of
-    layer pool 0's inputs until the time budget is used (at least one step)."""
+    """The oracle as it stands on this host (at its current thread count), on
+    whole steps of layer pool 0's inputs until the time budget is used (at least
+    one step)."""
     import numpy as np
     import oracle
     cfg = oracle.Config(q_scale=x.w.q_scale, batch=x.w.batch, q_len=x.w.q_len,
@@ -296,8 +335,36 @@ def cpu_baseline_extend(x, budget_s: float):
     est = t_pro + t_rows / n_rows * total_rows
     sample = (f"prologue of all {x.tokens} tokens ({t_pro:.1f} s) + attention and epilogue of "
               f"{n_rows} random (token, head) rows of {total_rows} ({t_rows:.1f} s), scaled to "
-              f"the whole step: {est:.0f} s per step; single-threaded")
+              f"the whole step: {est:.0f} s per step; single-threaded")  # (thread count noted by the caller)
     return est, sample
+
+
+def cpu_baseline_legs(x, kv_bytes, budget_s: float, extend: bool):
+    """The oracle as it stands on this host, twice on the same sample: with its
+    attention loops on every usable CPU (OpenMP over (token, head) pairs: the
+    reported value, cores = the threads used) and on one thread."""
+    import oracle
+    oracle.build()
+    host = host_description()
+    legs = {}
+    n0 = oracle.threads()
+    try:
+        for name, n in (("omp", max(1, host["usable_cpus"] or 1)), ("single_thread", 1)):
+            used = oracle.threads(n)
+            if extend:
+                est, sample = cpu_baseline_extend(x, budget_s / 2)
+                legs[name] = {"value": round(kv_bytes / est / 1e9, 6), "cores": used,
+                              "sample": sample.replace("single-threaded", f"{used} threads")}
+            else:
+                k, dt = cpu_baseline(x, budget_s / 2)
+                legs[name] = {"value": round(k * kv_bytes / dt / 1e9, 4), "cores": used,
+                              "sample": f"{k} whole steps of layer pool 0 ({x.w.name}), "
+                                        f"{used} threads, {dt:.1f} s"}
+    finally:
+        oracle.threads(n0)
+    top = legs["omp"]
+    return {"value": top["value"], "unit": "GB/s", "cores": top["cores"], "kind": "oracle",
+            "sample": top["sample"], "single_thread": legs["single_thread"], "host": host}
 
 
 def qk_norm_bytes(w) -> int:
@@ -340,22 +407,28 @@ def run_qk_norm(args, w, dev):
             call(i, cap)
     torch.cuda.synchronize()
 
-    def capture(n, rotate):
+    def capture(pools):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
-                for k in range(n):
-                    call(k % n_pools if rotate else 0, cap)
+                for i in pools:
+                    call(i, cap)
         return g
 
-    g_warm, g_cold, g_hot = capture(max(1, args.warmup), True), capture(args.steps, True), \
-        capture(args.steps, False)
+    # As for the step: the warm-up on buffer pairs 0 .. W-1, the timed calls from pair W on.
+    n_warm = max(1, args.warmup)
+    warm_pools = [k % n_pools for k in range(n_warm)]
+    cold_pools = [(n_warm + k) % n_pools for k in range(args.steps)]
+    g_warm, g_cold, g_hot = capture(warm_pools), capture(cold_pools), capture([0] * args.steps)
     torch.cuda.synchronize()
+    reuse = [r for r in reuse_distances(list(range(n_pools)) + warm_pools, cold_pools, call_bytes)
+             if r is not None]
 
     def timed(g):
         g_warm.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SPIN_CYCLES)  # as for the step: the host's submission is not timed
         e0.record()
         g.replay()
         e1.record()
@@ -374,7 +447,9 @@ def run_qk_norm(args, w, dev):
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "rows": w.rows, "num_heads": w.num_heads,
                    "head_dim": w.head_dim, "row_stride": w.row_stride, "scale": w.scale,
-                   "buffer_pairs": n_pools, "touched_bytes_per_round": n_pools * call_bytes},
+                   "buffer_pairs": n_pools, "touched_bytes_per_round": n_pools * call_bytes,
+                   "timed_touched_bytes": args.steps * call_bytes,
+                   "timed_min_reuse_bytes": min(reuse) if reuse else None},
         "us_per_call": round(us, 3),
         "warm_single_buffer": {"us_per_call": round(us_warm, 3),
                                "gbs": round(call_bytes / (us_warm * 1e-6) / 1e9, 1)},
@@ -400,7 +475,9 @@ def run_qk_norm(args, w, dev):
         per = 2 * rows * w.num_heads * w.head_dim * 2
         result["cpu_baseline"] = {"value": round(n * per / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
                                   "kind": "oracle",
-                                  "sample": f"{n} calls on the first {rows} rows, single-threaded, {dt:.1f} s"}
+                                  "sample": f"{n} calls on the first {rows} rows, single-threaded "
+                                            f"(the QK-norm oracle has no parallel loop), {dt:.1f} s",
+                                  "host": host_description()}
     print(json.dumps(result), flush=True)
 
 
@@ -577,28 +654,41 @@ def main():
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
 
-    def capture(n_steps, rotate):
+    def capture(pools):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
-                for k in range(n_steps):
-                    run(k % n_layers if rotate else 0, cap)
+                for li in pools:
+                    run(li, cap)
         return g
 
+    # Order of execution: one sweep over every pool, the warm-up graph on pools
+    # 0 .. W-1, then the timed graph starting at pool W, so that no timed step
+    # reads a pool touched since the sweep (until the rotation wraps round, a
+    # whole round of pools later).
+    n_warm = max(1, args.warmup)
+    warm_pools = [k % n_layers for k in range(n_warm)]
+    cold_pools = [(n_warm + k) % n_layers for k in range(args.steps)]
+    sweep = list(range(n_layers))
     with torch.cuda.stream(cap):
-        for li in range(n_layers):
+        for li in sweep:
             run(li, cap)
     torch.cuda.synchronize()
-    g_warm = capture(max(1, args.warmup), True)
-    g_cold = capture(args.steps, True)
-    g_hot = capture(args.steps, False)
+    g_warm = capture(warm_pools)
+    g_cold = capture(cold_pools)
+    g_hot = capture([0] * args.steps)
     torch.cuda.synchronize()
+    reuse = reuse_distances(sweep + warm_pools, cold_pools, step_bytes)
 
     def timed(g):
         g_warm.replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
+        # A short spin on the GPU (untimed, ahead of the start event) keeps the
+        # device busy while the host submits the graph, so the interval holds
+        # the K steps' device time rather than the host's submission latency.
+        torch.cuda._sleep(SPIN_CYCLES)
         e0.record()
         g.replay()
         e1.record()
@@ -663,6 +753,7 @@ def main():
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "algorithmic_bytes": step_bytes,
                     "kernel": "fused_step_kernel", "kernel_source": kernel_source_hash()}
+    timed_reuse = [r for r in reuse if r is not None]
     result = {
         "metric": METRIC,
         "value": round(kv_bytes / (us_step * 1e-6) / 1e9, 1),
@@ -682,6 +773,8 @@ def main():
                    "rope_theta": w.rope_theta, "sm_scale": w.sm_scale, "kv_scale": w.kv_scale,
                    "seq_lens": [w.seq_lo, w.seq_hi], "splits": step.splits,
                    "layer_pools": n_layers, "touched_bytes_per_round": n_layers * step_bytes,
+                   "timed_touched_bytes": args.steps * step_bytes,
+                   "timed_min_reuse_bytes": min(timed_reuse) if timed_reuse else None,
                    "pool_bytes_allocated": n_layers * pool_bytes,
                    "page_table": "shared by the layers" if args.shared_table else "per layer"},
         "us_per_layer_step": round(us_step, 3),
@@ -707,17 +800,8 @@ def main():
         result["config"]["prefill_topk"] = w.prefill_topk
     if not args.no_cpu_baseline and (ragged is not None or sprefill is not None):
         pass  # the sampled oracle baselines are written for uniform batches
-    elif not args.no_cpu_baseline and extend:
-        est, sample = cpu_baseline_extend(x0, args.cpu_seconds)
-        result["cpu_baseline"] = {"value": round(kv_bytes / est / 1e9, 6), "unit": "GB/s",
-                                  "cores": 1, "kind": "oracle", "sample": sample}
     elif not args.no_cpu_baseline:
-        n, dt = cpu_baseline(x0, args.cpu_seconds)
-        result["cpu_baseline"] = {
-            "value": round(n * kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{n} whole steps of layer pool 0 ({w.name}), single-threaded, {dt:.1f} s",
-        }
+        result["cpu_baseline"] = cpu_baseline_legs(x0, kv_bytes, args.cpu_seconds, extend)
     print(json.dumps(result), flush=True)
     step.close()
 

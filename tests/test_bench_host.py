@@ -150,3 +150,23 @@ def test_sparse_prefill_accounting_counts_the_listed_keys():
                     keys += len([k for k in range(32 * j, 32 * j + 32) if k < cs])
     assert kv == keys * 64 * 2
     assert step_b > kv
+
+
+def test_timed_steps_never_reread_a_recently_touched_pool():
+    """After the sweep over every pool and the warm-up on pools 0 .. W-1, the
+    timed steps start at pool W: each timed step's pool was last touched a whole
+    round of pools earlier (n - 1 steps), for the driver's 20 timed steps after
+    5 warm-up ones as for the default 400 after 40."""
+    import bench
+    step = 17_261_056
+    n = bench.layer_pool_count(step, 89_500_000, float(1 << 30))
+    assert n * step >= 1 << 30
+    for warm, steps in ((5, 20), (40, 400), (1, 1)):
+        warm_pools = [k % n for k in range(warm)]
+        cold = [(warm + k) % n for k in range(steps)]
+        r = bench.reuse_distances(list(range(n)) + warm_pools, cold, step)
+        assert all(x is not None for x in r)
+        assert min(r) == (n - 1) * step, (warm, steps, min(r))
+    # the old order (timed from pool 0 right after a warm-up on pools 0..4) re-read them
+    r = bench.reuse_distances(list(range(n)) + [0, 1, 2, 3, 4], list(range(20)), step)
+    assert min(r) == 4 * step
