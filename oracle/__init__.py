@@ -100,6 +100,9 @@ def lib():
                                       ctypes.c_int32, P, P, ctypes.c_float, ctypes.c_float, P, P, P]
         L.orc_qk_norm.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_float, ctypes.c_float, P]
+        L.orc_page_table.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_int32, P, P, P]
+        L.orc_page_table.restype = ctypes.c_int
         L.orc_threads.argtypes = [ctypes.c_int]
         L.orc_threads.restype = ctypes.c_int
         _lib = L
@@ -241,6 +244,24 @@ def step_meta(cfg: Config, seq_lens: np.ndarray, page_table: np.ndarray):
     _check(lib().orc_step_meta(ctypes.byref(cfg.c()), _p(seq), _p(pt), _p(pos), _p(loc), _p(cs)),
            "step_meta")
     return pos, loc, cs
+
+
+def page_table(req_to_token: np.ndarray, slot_ids: np.ndarray, kv_lens: np.ndarray,
+               page_size: int, max_pages: int):
+    """Page "msa.py" _build_page_table (see orc_page_table): returns (padded page
+    table int32 [B, max_pages], packed kv_indices int32, kv_indptr int32 [B+1])."""
+    r2t = np.ascontiguousarray(req_to_token, np.int32)
+    sid = np.ascontiguousarray(slot_ids, np.int32)
+    kvl = np.ascontiguousarray(kv_lens, np.int32)
+    B = len(sid)
+    n = np.where(kvl > 0, (kvl.astype(np.int64) + page_size - 1) // page_size, 0)
+    table = np.empty((B, max_pages), np.int32)
+    packed = np.empty(max(int(n.sum()), 1), np.int32)
+    indptr = np.empty(B + 1, np.int32)
+    _check(lib().orc_page_table(_p(r2t), r2t.shape[1], r2t.shape[0], _p(sid), _p(kvl), B,
+                                int(page_size), int(max_pages), _p(table), _p(packed),
+                                _p(indptr)), "page_table")
+    return table, packed[:int(n.sum())], indptr
 
 
 def step(cfg: Config, qkv, positions, cache_loc, cache_seqlens, page_table, k_cache, v_cache,

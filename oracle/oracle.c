@@ -613,7 +613,10 @@ int orc_step(const orc_config* cfg, const uint16_t* qkv, const int64_t* position
 /* cache_seqlens = seq_lens + L.  Page "msa.py" (update_msa_decode_cg_meta): */
 /* graph replay pads the batch with seq_len == 0 slots, masked by a zero key */
 /* count.                                                                    */
-/* READING: a slot with seq_lens[b] <= 0 is padding: its tokens get position */
+/* READING: in a decode or verify step (q_len <= 8) a slot with seq_lens[b]  */
+/* <= 0 is padding (a decode request always has cached tokens); in an extend */
+/* step (q_len > 8) seq_lens[b] == 0 is a new request with an empty prefix   */
+/* and only seq_lens[b] < 0 is padding.  A padded slot's tokens get position */
 /* 0 and cache row -1 (nothing is stored) and the slot key count 0 (no key,  */
 /* output 0).  A position whose page-table entry lies beyond max_pages or is */
 /* negative also gets cache row -1.                                          */
@@ -624,7 +627,7 @@ int orc_step_meta(const orc_config* cfg, const int32_t* seq_lens, const int32_t*
   const int64_t P = cfg->page_size;
   for (int64_t b = 0; b < cfg->batch; ++b) {
     const int64_t len = seq_lens[b];
-    const int pad = len <= 0;
+    const int pad = cfg->q_len <= 8 ? len <= 0 : len < 0;
     cache_seqlens[b] = pad ? 0 : (int32_t)(len + cfg->q_len);
     for (int64_t i = 0; i < cfg->q_len; ++i) {
       const int64_t t = b * cfg->q_len + i;
@@ -640,6 +643,54 @@ int orc_step_meta(const orc_config* cfg, const int32_t* seq_lens, const int32_t*
       if (page < cfg->max_pages) entry = page_table[b * cfg->max_pages + page];
       cache_loc[t] = entry < 0 ? -1 : entry * P + p % P;
     }
+  }
+  return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The physical page table of a step from the allocator's map (page          */
+/* "msa.py", _build_page_table): req_to_token[r, p] is the physical slot of  */
+/* logical position p of request row r; pages hold page_size contiguous      */
+/* slots, so the physical page of logical page i of request b is             */
+/* req_to_token[slot_ids[b], i * P] / P, for i < ceil(kv_lens[b] / P).       */
+/*   page_table  int32 [B, max_pages] (NULL: not built): those pages, then   */
+/*               -1 to the end of the row (page 1's layout)                  */
+/*   kv_indices  int32 [sum of page counts] (NULL: not built): the same      */
+/*               pages packed request after request (page 2's kv_indices),   */
+/*               request b's from kv_indptr[b]                               */
+/*   kv_indptr   int32 [B + 1] (needed with kv_indices): exclusive prefix    */
+/*               sums of the page counts                                     */
+/* READING: kv_lens[b] <= 0 gives no page (a padded slot); a negative map    */
+/* entry is no slot and gives -1.  A slot id outside 0..max_reqs-1, a page   */
+/* whose first position lies past the map's row, or more pages than          */
+/* max_pages for the padded table is a caller error (ORC_BAD_ARG).           */
+/* ------------------------------------------------------------------------ */
+int orc_page_table(const int32_t* req_to_token, int64_t req_stride, int64_t max_reqs,
+                   const int32_t* slot_ids, const int32_t* kv_lens, int32_t batch,
+                   int32_t page_size, int32_t max_pages, int32_t* page_table,
+                   int32_t* kv_indices, int32_t* kv_indptr) {
+  if (batch < 0 || page_size < 1 || req_stride < 1 || max_reqs < 1) return ORC_BAD_ARG;
+  if (page_table && max_pages < 1) return ORC_BAD_ARG;
+  if (kv_indices && !kv_indptr) return ORC_BAD_ARG;
+  int64_t packed = 0;
+  if (kv_indptr) kv_indptr[0] = 0;
+  for (int64_t b = 0; b < batch; ++b) {
+    const int64_t r = slot_ids[b];
+    if (r < 0 || r >= max_reqs) return ORC_BAD_ARG;
+    const int64_t len = kv_lens[b];
+    const int64_t n = len > 0 ? (len + page_size - 1) / page_size : 0;
+    if (n > 0 && (n - 1) * page_size >= req_stride) return ORC_BAD_ARG;
+    if (page_table && n > max_pages) return ORC_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t slot = req_to_token[r * req_stride + i * page_size];
+      const int32_t page = slot < 0 ? -1 : (int32_t)(slot / page_size);
+      if (page_table) page_table[b * max_pages + i] = page;
+      if (kv_indices) kv_indices[packed + i] = page;
+    }
+    if (page_table)
+      for (int64_t i = n; i < max_pages; ++i) page_table[b * max_pages + i] = -1;
+    packed += n;
+    if (kv_indptr) kv_indptr[b + 1] = (int32_t)packed;
   }
   return ORC_OK;
 }
