@@ -27,7 +27,7 @@ EXPORTED = ["mi355x_gated_attn_supports", "mi355x_gated_attn_prepare", "mi355x_g
             "mi355x_gated_attn_timing_read", "mi355x_gated_attn_step_meta",
             "mi355x_qk_norm_supports", "mi355x_qk_norm", "mi355x_gated_attn_sparse_step",
             "mi355x_gated_attn_ragged_step", "mi355x_gated_attn_sparse_prefill_step",
-            "mi355x_gated_attn_step_noalloc"]
+            "mi355x_gated_attn_step_noalloc", "mi355x_gated_attn_page_table"]
 
 MI355X_QKN_BF16 = 0
 MI355X_QKN_FP16 = 1
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.mi355x_gated_attn_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_step_noalloc.argtypes = [P] * 13
         L.mi355x_gated_attn_step_meta.argtypes = [P] * 7
+        L.mi355x_gated_attn_page_table.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64] + [P] * 6
         L.mi355x_gated_attn_sparse_step.argtypes = [P] * 13 + [ctypes.c_size_t, P]
         L.mi355x_gated_attn_sparse_prefill_step.argtypes = [P] * 5 + [ctypes.c_int32] + \
             [P] * 9 + [ctypes.c_size_t, P]
@@ -365,6 +366,35 @@ def mi355x_gated_attn_step_meta(ctx, seq_lens, page_table, positions, cache_loc,
     _check(lib().mi355x_gated_attn_step_meta(ctx, _ptr(seq_lens), _ptr(page_table), _ptr(positions),
                                              _ptr(cache_loc), _ptr(cache_seqlens),
                                              ctypes.c_void_p(handle)))
+
+
+def mi355x_gated_attn_page_table(ctx, req_to_token, slot_ids, kv_lens, page_table=None,
+                                 kv_indices=None, kv_indptr=None, stream=None):
+    """Build the step's physical page table on the device (page "msa.py"
+    _build_page_table): int32 req_to_token [max_reqs, req_stride], slot_ids
+    [B] and kv_lens [B] in; page_table [B, max_pages] (padded with -1) and/or
+    kv_indices (packed) with kv_indptr [B+1] out."""
+    import torch
+    c, dev = _ctx_entry(ctx)
+    if c.batch == 0:
+        return
+    i32 = _dt("int32")
+    if req_to_token is None or req_to_token.dim() != 2:
+        raise ValueError("req_to_token must be a 2-D int32 device tensor [max_reqs, req_stride]")
+    specs = [("req_to_token", req_to_token, i32, None, None, True),
+             ("slot_ids", slot_ids, i32, c.batch, None, True),
+             ("kv_lens", kv_lens, i32, c.batch, None, True),
+             ("page_table", page_table, i32, c.batch * c.max_pages, None, False),
+             ("kv_indices", kv_indices, i32, None, None, False),
+             ("kv_indptr", kv_indptr, i32, c.batch + 1, None, kv_indices is not None)]
+    _check_tensors(specs, dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(req_to_token.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+    _check(lib().mi355x_gated_attn_page_table(
+        ctx, _ptr(req_to_token), req_to_token.shape[1], req_to_token.shape[0], _ptr(slot_ids),
+        _ptr(kv_lens), _ptr(page_table), _ptr(kv_indices), _ptr(kv_indptr),
+        ctypes.c_void_p(handle)))
 
 
 def mi355x_gated_attn_workspace_init(ctx, workspace, stream=None):

@@ -342,6 +342,41 @@ int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_l
   return ok();
 }
 
+int mi355x_gated_attn_page_table(mi355x_gated_attn_ctx* ctx, const int32_t* req_to_token,
+                                 int64_t req_stride, int64_t max_reqs, const int32_t* slot_ids,
+                                 const int32_t* kv_lens, int32_t* page_table, int32_t* kv_indices,
+                                 int32_t* kv_indptr, void* stream) {
+  if (!ctx) return fail(MI355X_GA_INVALID_ARGUMENT, "ctx is NULL");
+  const auto& c = ctx->cfg;
+  if (c.batch == 0) return ok();
+  if (!req_to_token || !slot_ids || !kv_lens)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "req_to_token, slot_ids and kv_lens are required");
+  if (!page_table && !kv_indices)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "neither page_table nor kv_indices is given");
+  if (kv_indices && !kv_indptr)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "kv_indices needs kv_indptr");
+  if (req_stride < 1 || max_reqs < 1)
+    return fail(MI355X_GA_INVALID_ARGUMENT, "req_stride and max_reqs must be >= 1");
+  int rc = check_device(ctx);
+  if (rc) return rc;
+  PageTableParams q{};
+  q.req_to_token = req_to_token;
+  q.req_stride = req_stride;
+  q.max_reqs = max_reqs;
+  q.slot_ids = slot_ids;
+  q.kv_lens = kv_lens;
+  q.batch = c.batch;
+  q.page_size = c.page_size;
+  q.page_shift = (c.page_size & (c.page_size - 1)) == 0 ? __builtin_ctz((unsigned)c.page_size) : -1;
+  q.max_pages = c.max_pages;
+  q.page_table = page_table;
+  q.kv_indices = kv_indices;
+  q.kv_indptr = kv_indices ? kv_indptr : nullptr;
+  const hipError_t e = launch_page_table(q, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(MI355X_GA_HIP_ERROR, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"
 
 namespace {

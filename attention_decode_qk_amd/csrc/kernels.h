@@ -129,6 +129,23 @@ struct MetaParams {
   int32_t page_shift;            // log2(page_size) if a power of two, else -1
 };
 hipError_t launch_step_meta(const MetaParams& m, hipStream_t stream);
+
+// The step's physical page table from the allocator's map (meta_kernel.hip).
+struct PageTableParams {
+  const int32_t* req_to_token;   // [max_reqs, req_stride] physical slot per logical position
+  int64_t req_stride;
+  int64_t max_reqs;
+  const int32_t* slot_ids;       // [B] map row of each request
+  const int32_t* kv_lens;        // [B] logical positions to cover
+  int32_t batch;
+  int32_t page_size;
+  int32_t page_shift;            // log2(page_size) if a power of two, else -1
+  int32_t max_pages;
+  int32_t* page_table;           // [B, max_pages] padded with -1, or null
+  int32_t* kv_indices;           // packed pages, or null
+  int32_t* kv_indptr;            // [B+1] exclusive prefix sums (written when kv_indices is)
+};
+hipError_t launch_page_table(const PageTableParams& q, hipStream_t stream);
 hipError_t launch_zero_counters(int32_t* counters, int n, hipStream_t stream);
 // Set every 8-byte word of [p, p + bytes) to the decode step's empty-slot
 // sentinel (all bits set); bytes is a multiple of 8.

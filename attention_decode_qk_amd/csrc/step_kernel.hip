@@ -253,7 +253,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   }
   const int t_lo = tg * LU;              // the group's first token (request-local)
   const int t_n = min(LU, L - t_lo);     // its tokens, >= 1
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: block indices and branches stay scalar
   const int kw = wave % KW;            // this wave's place among its head's waves
   const int g0 = HS ? wave / KW : 0;   // first KV head this wave works on
   const int j = lane & 15;

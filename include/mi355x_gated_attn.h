@@ -144,7 +144,9 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
  * capturable; the calling thread's current device must be the ctx's device.
  *
  *   seq_lens       int32 [B]    cached tokens per request; a slot with
- *                  seq_lens[b] <= 0 is padding
+ *                  seq_lens[b] <= 0 is padding when q_len <= 8 (a decode
+ *                  request always has cached tokens), seq_lens[b] < 0 when
+ *                  q_len > 8 (0 is a new request with an empty prefix)
  *   page_table     int32 [B, max_pages]  physical page of each logical page,
  *                  already covering the step's new positions (-1 unused)
  *   positions      int64 [B*L]  out: seq_lens[b] + i (0 in a padded slot)
@@ -160,6 +162,38 @@ int mi355x_gated_attn_workspace_init(mi355x_gated_attn_ctx* ctx, void* workspace
 int mi355x_gated_attn_step_meta(mi355x_gated_attn_ctx* ctx, const int32_t* seq_lens,
                                 const int32_t* page_table, int64_t* positions, int64_t* cache_loc,
                                 int32_t* cache_seqlens, void* stream);
+
+/*
+ * The step's physical page table from the allocator's map, built on the device
+ * once per step for every layer (page "msa.py", _build_page_table: a page holds
+ * page_size contiguous slots, so the physical page of logical page i of request
+ * b is req_to_token[slot_ids[b], i * P] / P, for i < ceil(kv_lens[b] / P); the
+ * page replaces its host-side .item() by a device scan, so the call needs no
+ * host synchronisation and may be captured in a HIP graph).
+ *
+ *   req_to_token  int32 [max_reqs, req_stride]  physical slot of each logical
+ *                 position of each allocator row (caller-owned, read only)
+ *   slot_ids      int32 [B]  allocator row of each request (clamped to
+ *                 0..max_reqs-1)
+ *   kv_lens       int32 [B]  logical positions to cover per request (for a
+ *                 step: its cache_seqlens, which include the new tokens); <= 0
+ *                 gives no page (a padded slot)
+ *   page_table    int32 [B, max_pages] out, or NULL: those pages, -1 after
+ *                 them (page 1's layout, the step's page_table argument)
+ *   kv_indices    int32 out, or NULL: the same pages packed request after
+ *                 request (page 2's kv_indices); request b's start at
+ *   kv_indptr     int32 [B+1] out (needed with kv_indices): exclusive prefix
+ *                 sums of the page counts
+ * A negative map entry gives -1.  Pages starting past a map row or beyond
+ * max_pages are a caller error: the kernels clamp the count to stay in bounds.
+ * B, P and max_pages come from the ctx's config (only `prepare` is needed).
+ * Returns MI355X_GA_OK with no launch when B == 0; INVALID_ARGUMENT for a NULL
+ * required pointer, no output, or req_stride / max_reqs < 1.
+ */
+int mi355x_gated_attn_page_table(mi355x_gated_attn_ctx* ctx, const int32_t* req_to_token,
+                                 int64_t req_stride, int64_t max_reqs, const int32_t* slot_ids,
+                                 const int32_t* kv_lens, int32_t* page_table, int32_t* kv_indices,
+                                 int32_t* kv_indptr, void* stream);
 
 /*
  * One layer-step, asynchronous on `stream` (a hipStream_t; NULL = the null

@@ -621,3 +621,28 @@ def test_noalloc_step_rejects_plans_beyond_its_static_scratch(L):
         assert L.mi355x_gated_attn_step_noalloc(small, *([None] * 12)) == ga.MI355X_GA_OK
     finally:
         ga.mi355x_gated_attn_destroy(small)
+
+
+def test_page_table_validates_before_any_launch(L):
+    ctx = ga.mi355x_gated_attn_prepare(cfg(batch=3, max_pages=10))
+    P = ctypes.c_void_p
+    try:
+        f = L.mi355x_gated_attn_page_table
+        good = [P(0x1000), 16, 4, P(0x2000), P(0x3000), P(0x4000), None, None]
+        assert f(ctx, *good[:5], None, None, None, None) == ga.MI355X_GA_INVALID_ARGUMENT
+        assert "neither" in ga.mi355x_gated_attn_last_error()
+        assert f(ctx, None, 16, 4, P(0x2000), P(0x3000), P(0x4000), None, None, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+        assert f(ctx, P(0x1000), 0, 4, P(0x2000), P(0x3000), P(0x4000), None, None, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+        assert f(ctx, P(0x1000), 16, 4, P(0x2000), P(0x3000), None, P(0x5000), None, None) == \
+            ga.MI355X_GA_INVALID_ARGUMENT
+        assert "kv_indptr" in ga.mi355x_gated_attn_last_error()
+        assert f(None, *good, None) == ga.MI355X_GA_INVALID_ARGUMENT
+    finally:
+        ga.mi355x_gated_attn_destroy(ctx)
+    empty = ga.mi355x_gated_attn_prepare(cfg(batch=0))
+    try:
+        assert L.mi355x_gated_attn_page_table(empty, None, 1, 1, *([None] * 6)) == ga.MI355X_GA_OK
+    finally:
+        ga.mi355x_gated_attn_destroy(empty)
