@@ -13,7 +13,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmi355x_gated_attn.so")
+# MI355X_GA_LIB may name another build of the same library (the host-sanitized
+# one of the sanitizer tests); by default the in-tree product library.
+LIB_PATH = os.environ.get("MI355X_GA_LIB") or os.path.join(HERE, "libmi355x_gated_attn.so")
 
 MI355X_GA_OK = 0
 MI355X_GA_UNSUPPORTED = 1
