@@ -81,11 +81,12 @@ typedef struct mi355x_gated_attn_config {
 typedef struct mi355x_gated_attn_ctx mi355x_gated_attn_ctx;
 
 /*
- * Whether this build serves cfg: returns MI355X_GA_OK, MI355X_GA_UNSUPPORTED
- * (head_dim != 64, Hq != 16, Hkv != 2, q_len outside 1..65536, B * q_len
- * beyond 2^31 - 1 for q_len > 8) or
- * MI355X_GA_INVALID_ARGUMENT (negative or zero sizes, window < 0,
- * rope_theta < 0, non-finite or non-positive scales).  Pure host code.
+ * Whether this build serves cfg (the query page "qk_norm" gives its kernel,
+ * supports_qk_norm: a shape a kernel does not serve is reported, not
+ * attempted): returns MI355X_GA_OK, MI355X_GA_UNSUPPORTED (head_dim != 64,
+ * Hq != 16, Hkv != 2, q_len outside 1..65536, B * q_len beyond 2^31 - 1 for
+ * q_len > 8) or MI355X_GA_INVALID_ARGUMENT (negative or zero sizes, window <
+ * 0, rope_theta < 0, non-finite or non-positive scales).  Pure host code.
  */
 int mi355x_gated_attn_supports(const mi355x_gated_attn_config* cfg);
 
@@ -276,10 +277,21 @@ int mi355x_gated_attn_step_noalloc(mi355x_gated_attn_ctx* ctx, const void* qkv,
                                    const float* k_scale, const float* v_scale, void* out,
                                    void* stream);
 
-/* Release a context (NULL is ignored).  Does not synchronise. */
+/*
+ * Release a context made by mi355x_gated_attn_prepare (NULL is ignored): its
+ * host memory and the timing hook's events.  Does not synchronise; steps
+ * already enqueued keep running (they read nothing from the ctx).
+ */
 void mi355x_gated_attn_destroy(mi355x_gated_attn_ctx* ctx);
 
-/* The calling thread's last error message ("" if none). */
+/*
+ * The calling thread's last error message ("" after a call that succeeded).
+ * Every failure is a returned status with this text, never a crash or an
+ * exception across the ABI: page "msa.py" makes an unavailable kernel a
+ * raised, catchable error (MSAUnavailableError) that callers test for, and
+ * this library reports every unserved shape, bad argument and HIP failure the
+ * same way.
+ */
 const char* mi355x_gated_attn_last_error(void);
 
 /*
