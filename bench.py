@@ -212,6 +212,29 @@ def algorithmic_bytes(w, x):
     return kv, kv + 4 * pages + x.tokens * per_token
 
 
+def step_accounting(w, x0):
+    """(KV bytes, algorithmic bytes) of one step of workload w on its seeded
+    inputs x0: the ragged and block-sparse prefill batches count only what
+    they keep."""
+    import synth
+    if w.prefill_block > 0:
+        sp0 = synth.sparse_prefill(x0, w.prefill_block, w.prefill_topk, seed=w.seed + 2)
+        return sparse_prefill_accounting(w, x0, sp0)
+    if w.ragged_lo > 0:
+        return ragged_accounting(w, x0, synth.ragged_lens(w))[:2]
+    return algorithmic_bytes(w, x0)
+
+
+def extend_attention_bytes(w, step_bytes: int, tokens: int) -> int:
+    """The extend path's attention launch alone: the step's KV and page-table
+    bytes, and per token its e4m3 query rows, gate columns and output row (the
+    prologue, a launch of its own, reads the projection row and stores q and the
+    K/V rows)."""
+    step_token = w.width * 2 + 2 * w.num_kv_heads * w.head_dim + w.num_q_heads * w.head_dim * 2 + 16
+    attn_token = w.num_q_heads * w.head_dim * (1 + 2 + 2)
+    return step_bytes - tokens * (step_token - attn_token)
+
+
 POOL_MEMORY_LIMIT = 64 << 30  # device bytes the layer pools may take
 
 
@@ -481,6 +504,218 @@ def run_qk_norm(args, w, dev):
     print(json.dumps(result), flush=True)
 
 
+# ---- profile summaries (profiles/*.md) from rocprofv3's CSV output ----------
+
+PROFILES_DIR = os.path.join(ROOT, "profiles")
+KERNEL_NAMES = {"fused_step": "fused_step_kernel", "extend_attn": "extend_attn_kernel",
+                "qk_norm": "qk_norm_kernel"}
+
+
+def _short_kernel(name: str) -> str:
+    name = re.sub(r"^void ", "", name).replace("mi355x_ga::(anonymous namespace)::", "")
+    return re.sub(r"\(.*$", "", name)
+
+
+def _find_csv(directory: str, suffix: str) -> str:
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {directory}")
+    return files[0]
+
+
+def summarize_trace(workload: str, trace_dir: str, title: str, command: str) -> str:
+    """profiles/<kernel>_<workload>_kernel_trace.md from a rocprofv3
+    --kernel-trace --stats run: calls and average / min / max duration of each
+    of the library's kernels."""
+    import csv
+    rows = list(csv.DictReader(open(_find_csv(trace_dir, "kernel_stats.csv"))))
+    out = os.path.join(PROFILES_DIR, f"{_kernel_prefix(workload)}_{workload}_kernel_trace.md")
+    lines = [f"# Kernel trace: {title}", "", "Command (on the MI355X box, from /tmp):", "", "```",
+             command, "```", "",
+             f"Kernel sources hash (as `bench.py` computes it): "
+             f"`{kernel_source_hash(workload_sources(workload))}`", "",
+             "| kernel | calls | avg µs | min µs | max µs |", "|---|---|---|---|---|"]
+    for r in rows:
+        if "mi355x_ga::" not in r["Name"]:
+            continue
+        lines.append(f"| {_short_kernel(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} |")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
+def _counter_mean(directory: str, counter: str, kernel: str):
+    import csv
+    import glob
+    vals, full = [], None
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and kernel in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+                full = r["Kernel_Name"]
+    if not vals:
+        raise SystemExit(f"no {counter} for {kernel} under {directory}")
+    return sum(vals) / len(vals), len(vals), full
+
+
+def summarize_counters(workload: str, dirs, title: str, commands, algorithmic: int) -> str:
+    """profiles/<kernel>_<workload>_counters.md from four rocprofv3 --pmc runs
+    (FETCH_SIZE and WRITE_SIZE of the workload, then of a 1 GiB device copy):
+    HBM bytes per launch, each counter scaled by what it reads for the copy."""
+    pref = _kernel_prefix(workload)
+    kname = KERNEL_NAMES[pref]
+    fetch, nf, full = _counter_mean(dirs[0], "FETCH_SIZE", kname)
+    write, _, _ = _counter_mean(dirs[1], "WRITE_SIZE", kname)
+    cf, _, _ = _counter_mean(dirs[2], "FETCH_SIZE", "copyBuffer")
+    cw, _, _ = _counter_mean(dirs[3], "WRITE_SIZE", "copyBuffer")
+    copy = 1 << 30
+    fs, ws = copy / (cf * 1024), copy / (cw * 1024)
+    fb, wb = round(fetch * 1024 * fs), round(write * 1024 * ws)
+    kshort = _short_kernel(full) if pref == "fused_step" else kname
+    d = {"kernel": kshort, "kernel_source_sha256": kernel_source_hash(workload_sources(workload)),
+         "fetch_kib_per_dispatch": round(fetch, 3), "write_kib_per_dispatch": round(write, 3),
+         "copy_fetch_kib": round(cf, 3), "copy_write_kib": round(cw, 3),
+         "fetch_scale": round(fs, 5), "write_scale": round(ws, 5), "fetch_bytes": fb,
+         "write_bytes": wb, "traffic_bytes_per_launch": fb + wb,
+         "algorithmic_bytes_per_launch": algorithmic}
+    out = os.path.join(PROFILES_DIR, f"{pref}_{workload}_counters.md")
+    lines = [f"# HBM counters: {kshort}, {title}", "",
+             "Commands (on the MI355X box, from /tmp), one counter per run:", "", "```", *commands,
+             "```", "",
+             f"- FETCH_SIZE per dispatch: {fetch:.1f} KiB (mean of {nf} dispatches)",
+             f"- WRITE_SIZE per dispatch: {write:.1f} KiB",
+             f"- Calibration: a 1 GiB device copy (`bench.py --calibrate-copy`, rocclr copyBuffer) "
+             f"reads FETCH_SIZE {cf:.1f} KiB and WRITE_SIZE {cw:.1f} KiB per dispatch, so the scale "
+             f"factors are {fs:.4f} (fetch) and {ws:.4f} (write).",
+             f"- Scaled: {fb / 1e6:.3f} MB read + {wb / 1e6:.3f} MB written = {(fb + wb) / 1e6:.3f} MB "
+             f"per launch, against {algorithmic / 1e6:.3f} MB algorithmic (ratio "
+             f"{(fb + wb) / algorithmic:.3f}).", "", "traffic_json: " + json.dumps(d)]
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
+def _old_title(path: str):
+    """The workload description on the first line of an existing summary."""
+    if os.path.exists(path):
+        m = re.match(r"# (?:Kernel trace|HBM counters): (?:.*?, )?(\w+ \(.*\))$",
+                     open(path).readline().strip())
+        if m:
+            return m.group(1)
+    return None
+
+
+SQ_PASSES = (
+    "SQ_WAVES SQ_WAVE_CYCLES SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_INSTS_MFMA "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY",
+    "SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_SALU SQ_INSTS_VMEM_RD SQ_ACTIVE_INST_ANY SQ_BUSY_CYCLES "
+    "SQ_INSTS_LDS SQ_ACTIVE_INST_SCA SQ_INSTS_BRANCH",
+    "GRBM_GUI_ACTIVE GRBM_COUNT",
+)
+
+
+def summarize_sq(workloads, root: str) -> str:
+    """profiles/fused_step_sq_counters.md: per-wave instruction, wait and
+    matrix-core counts of the step kernel from three --pmc passes per workload
+    (root/sq_<workload>_<pass>), the kernel's duration from its trace summary."""
+    import csv
+    import glob
+    rows, cmds = [], []
+    for w in workloads:
+        vals, meta = {}, None
+        for i in (1, 2, 3):
+            for f in glob.glob(os.path.join(root, f"sq_{w}_{i}", "**", "*counter_collection.csv"),
+                               recursive=True):
+                for r in csv.DictReader(open(f)):
+                    if "fused_step_kernel" in r["Kernel_Name"]:
+                        vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                        meta = r
+        if meta is None:
+            raise SystemExit(f"no SQ counters for {w} under {root}")
+        m = {k: sum(v) / len(v) for k, v in vals.items()}
+        wv = m["SQ_WAVES"]
+
+        def per(k):
+            return m[k] / wv
+        trace = open(os.path.join(PROFILES_DIR, f"fused_step_{w}_kernel_trace.md")).read()
+        us = float(re.search(r"^\| fused_step_kernel[^|]*\| \d+ \| ([\d.]+) \|", trace, re.M).group(1))
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024  # per SIMD
+        frac = busy / (us * 1e-6 * 2.4e9)
+        util = 100 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] * 1024)
+        rows.append(
+            f"| {w} | `{_short_kernel(meta['Kernel_Name'])}` | {meta['Workgroup_Size']} | "
+            f"{meta['VGPR_Count']}+{meta['Accum_VGPR_Count']} | {int(wv)} | {per('SQ_INSTS_VALU'):.0f} | "
+            f"{per('SQ_INSTS_MFMA'):.0f} | {per('SQ_INSTS_VALU_TRANS_F32'):.0f} | "
+            f"{per('SQ_INSTS_VMEM_RD'):.0f} | {per('SQ_WAVE_CYCLES'):.0f} | "
+            f"{per('SQ_ACTIVE_INST_VALU'):.0f} ({100 * m['SQ_ACTIVE_INST_VALU'] / m['SQ_WAVE_CYCLES']:.0f}%) | "
+            f"{per('SQ_WAIT_INST_ANY'):.0f} | {per('SQ_WAIT_ANY'):.0f} "
+            f"({100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:.0f}%) | {busy:.0f} | "
+            f"{100 * frac:.1f}% of {us:.1f} µs | {util:.2f}% |")
+        for i, pas in enumerate(SQ_PASSES, 1):
+            cmds.append(f"rocprofv3 --pmc {pas} --output-format csv -d $R/gpurun_out/sq_{w}_{i} -o sq -- "
+                        f"python3 $R/bench.py --workload {w} --steps 10 --warmup 2 --no-cpu-baseline")
+    out = os.path.join(PROFILES_DIR, "fused_step_sq_counters.md")
+    lines = [
+        "# SQ instruction, wait and matrix-core counters: fused step kernel", "",
+        "Commands (on the MI355X box, from /tmp; three passes per workload, within the per-block "
+        "counter limits):", "", "```", *cmds, "```", "",
+        f"Kernel sources hash (as `bench.py` computes it): `{kernel_source_hash()}`", "",
+        "Per wave, mean over the dispatches of the step kernel (wave-cycle counters are in units of 4 "
+        "cycles). MFMA busy: `SQ_VALU_MFMA_BUSY_CYCLES` is counted per SIMD; summed over the dispatch "
+        "it is divided by the 1,024 SIMDs, then by the kernel-trace average duration at 2.4 GHz "
+        "(second-last column). The last column is rocprofv3's own `MfmaUtil` expression (busy cycles / "
+        "(GRBM_GUI_ACTIVE x SIMDs)), whose GRBM_GUI_ACTIVE, taken in its own pass, spans the profiler's "
+        "serialised dispatch window and so is far longer than the kernel.", "",
+        "| workload | kernel | threads | VGPRs+AGPRs | waves | VALU | MFMA | transcendental | vector loads "
+        "| wave quad-cycles | VALU-active | waiting on a dependency | waiting (any) | MFMA busy cycles per "
+        "SIMD | MFMA busy / kernel time | MfmaUtil |",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|", *rows, ""]
+    open(out, "w").write("\n".join(lines) + "\n")
+    return out
+
+
+def summarize(args):
+    """--summarize trace|counters|sq: write profiles/*.md for the workload(s)
+    from rocprofv3's CSV output under --profile-root (trace_<w>,
+    pmc_<counter>_<w>, pmc_<counter>_copy, sq_<w>_<pass>), recording the
+    commands that made them."""
+    import synth
+    root = args.profile_root
+    R = "$R"
+    if args.summarize == "sq":
+        print("wrote", summarize_sq(args.workload.split(","), root))
+        return
+    w = args.workload
+    pref = _kernel_prefix(w)
+    if args.summarize == "trace":
+        out = os.path.join(PROFILES_DIR, f"{pref}_{w}_kernel_trace.md")
+        cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {R}/gpurun_out/trace_{w} "
+               f"-o {w} -- python3 {R}/bench.py --workload {w} --steps 100 --warmup 10 "
+               f"--no-cpu-baseline")
+        title = args.title or _old_title(out) or w
+        print("wrote", summarize_trace(w, os.path.join(root, f"trace_{w}"), title, cmd))
+        return
+    out = os.path.join(PROFILES_DIR, f"{pref}_{w}_counters.md")
+    cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {R}/gpurun_out/pmc_{c}_{w} -o bench -- "
+            f"python3 {R}/bench.py --workload {w} --steps 20 --warmup 2 --no-cpu-baseline"
+            for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    cmds += [f"rocprofv3 --pmc {c} --output-format csv -d {R}/gpurun_out/pmc_{c}_copy -o copy -- "
+             f"python3 {R}/bench.py --calibrate-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+    if w in synth.QK_NORM_WORKLOADS:
+        alg = qk_norm_bytes(synth.QK_NORM_WORKLOADS[w])
+    else:
+        wl = synth.WORKLOADS[w]
+        x0 = synth.make_inputs(wl)
+        alg = step_accounting(wl, x0)[1]
+        if pref == "extend_attn":
+            tokens = int(synth.ragged_lens(wl).sum()) if wl.ragged_lo > 0 else x0.tokens
+            alg = extend_attention_bytes(wl, alg, tokens)
+    dirs = [os.path.join(root, d) for d in (f"pmc_FETCH_SIZE_{w}", f"pmc_WRITE_SIZE_{w}",
+                                            "pmc_FETCH_SIZE_copy", "pmc_WRITE_SIZE_copy")]
+    title = args.title or _old_title(out) or w
+    print("wrote", summarize_counters(w, dirs, title, cmds, alg))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -496,7 +731,20 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force a split count (0 = plan)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--summarize", choices=("trace", "counters", "sq"), default=None,
+                    help="write profiles/*.md for --workload (comma list for sq) from rocprofv3 "
+                         "CSV output under --profile-root; needs no GPU")
+    ap.add_argument("--profile-root", default=os.path.join(ROOT, "gpurun_out"),
+                    help="--summarize: where the rocprofv3 runs wrote their directories")
+    ap.add_argument("--title", default="", help="--summarize: the workload's description")
+    ap.add_argument("--profiles-dir", default=os.path.join(ROOT, "profiles"), help="--summarize: where to write")
     args = ap.parse_args()
+
+    if args.summarize:
+        global PROFILES_DIR
+        PROFILES_DIR = args.profiles_dir
+        summarize(args)
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the step is "
@@ -746,6 +994,8 @@ def main():
                     "algorithmic_flops": {"qk_fp8": f8, "pv_f16": f16},
                     "peak_rule": "QK^T at the fp8 dense peak (5.0 PFLOP/s) and PV at the f16 "
                                  "one (2.5), back to back",
+                    "algorithmic_bytes": extend_attention_bytes(
+                        w, step_bytes, int(ragged["total"]) if ragged is not None else x0.tokens),
                     "kernel": "extend_attn_kernel", "kernel_us": round(kernel_us, 3),
                     "kernel_source": kernel_source_hash(EXTEND_SOURCES)}
     else:

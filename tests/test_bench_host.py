@@ -170,3 +170,48 @@ def test_timed_steps_never_reread_a_recently_touched_pool():
     # the old order (timed from pool 0 right after a warm-up on pools 0..4) re-read them
     r = bench.reuse_distances(list(range(n)) + [0, 1, 2, 3, 4], list(range(20)), step)
     assert min(r) == 4 * step
+
+
+def _write_csv(path, header, rows):
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def test_summarize_writes_trace_and_counter_summaries(tmp_path):
+    """--summarize turns rocprofv3 CSV output into the profiles' summaries:
+    the kernel table and a traffic line that bench.py reads back, scaled by the
+    copy calibration (a copy that counts twice its bytes halves the reading)."""
+    import json
+    import re
+    import subprocess
+    import sys
+    root, out = tmp_path / "runs", tmp_path / "profiles"
+    out.mkdir()
+    kname = "void mi355x_ga::(anonymous namespace)::fused_step_kernel<1, 1, 0>(mi355x_ga::StepParams)"
+    _write_csv(root / "trace_swa_decode" / "box" / "swa_decode_kernel_stats.csv",
+               ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs"],
+               [[kname, 110, 1100000, 10000, 99.0, 9500, 12000], ["copyBuffer", 3, 1, 1, 1.0, 1, 1]])
+    counters = {"FETCH_SIZE": 1000.0, "WRITE_SIZE": 10.0}
+    for c, v in counters.items():
+        _write_csv(root / f"pmc_{c}_swa_decode" / "box" / "bench_counter_collection.csv",
+                   ["Counter_Name", "Kernel_Name", "Counter_Value"], [[c, kname, v], [c, kname, v]])
+        copy_kib = (2 if c == "FETCH_SIZE" else 1) * (1 << 20)
+        _write_csv(root / f"pmc_{c}_copy" / "box" / "copy_counter_collection.csv",
+                   ["Counter_Name", "Kernel_Name", "Counter_Value"], [[c, "copyBuffer", copy_kib]])
+    for mode in ("trace", "counters"):
+        subprocess.run([sys.executable, bench.__file__, "--summarize", mode, "--workload", "swa_decode",
+                        "--profile-root", str(root), "--profiles-dir", str(out), "--title", "t"],
+                       check=True, capture_output=True)
+    trace = (out / "fused_step_swa_decode_kernel_trace.md").read_text()
+    assert "| fused_step_kernel<1, 1, 0> | 110 | 10.000 | 9.500 | 12.000 |" in trace
+    assert "copyBuffer" not in trace
+    text = (out / "fused_step_swa_decode_counters.md").read_text()
+    d = json.loads(re.search(r"^traffic_json:\s*(\{.*\})\s*$", text, re.M).group(1))
+    assert d["fetch_bytes"] == 1000 * 1024 // 2 and d["write_bytes"] == 10 * 1024
+    wl = synth.WORKLOADS["swa_decode"]
+    assert d["algorithmic_bytes_per_launch"] == bench.step_accounting(wl, synth.make_inputs(wl))[1]
+    assert d["kernel_source_sha256"] == bench.kernel_source_hash()
