@@ -965,18 +965,22 @@ def main():
 
     # The on-device step metadata (built once per step for all layers): K
     # launches in one graph, round-robin over the layer pools' page tables.
-    m_pos = torch.empty(x0.tokens, dtype=torch.int64, device=dev)
-    m_loc = torch.empty(x0.tokens, dtype=torch.int64, device=dev)
-    m_cs = torch.empty(w.batch, dtype=torch.int32, device=dev)
-    g_meta = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(cap):
-        step.meta(seq, layers[0]["page_table"], m_pos, m_loc, m_cs, cap)
+    # The block-sparse prefill's queries carry their own rows and positions
+    # (token_req), so it has no such metadata.
+    meta_us = None
+    if sprefill is None:
+        m_pos = torch.empty(x0.tokens, dtype=torch.int64, device=dev)
+        m_loc = torch.empty(x0.tokens, dtype=torch.int64, device=dev)
+        m_cs = torch.empty(w.batch, dtype=torch.int32, device=dev)
+        g_meta = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            step.meta(seq, layers[0]["page_table"], m_pos, m_loc, m_cs, cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g_meta, stream=cap):
+                for k in range(args.steps):
+                    step.meta(seq, layers[k % n_layers]["page_table"], m_pos, m_loc, m_cs, cap)
         torch.cuda.synchronize()
-        with torch.cuda.graph(g_meta, stream=cap):
-            for k in range(args.steps):
-                step.meta(seq, layers[k % n_layers]["page_table"], m_pos, m_loc, m_cs, cap)
-    torch.cuda.synchronize()
-    meta_us = 1000.0 * timed(g_meta) / args.steps
+        meta_us = 1000.0 * timed(g_meta) / args.steps
 
     # The step is one kernel, so the graph-timed time per step is that kernel's
     # average duration over the timed region (rocprofv3's kernel trace agrees).
@@ -1032,7 +1036,7 @@ def main():
         "kv_gbs_pct_of_peak": round(100.0 * kv_bytes / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
         "kernel_us": round(us_step, 3),
         "eager_event_kernel_us": round(kernel_us, 3),
-        "step_meta_us": round(meta_us, 3),
+        "step_meta_us": None if meta_us is None else round(meta_us, 3),
         "warm_single_pool": {"us_per_layer_step": round(us_warm, 3),
                              "kv_gbs": round(kv_bytes / (us_warm * 1e-6) / 1e9, 1)},
         "roofline": roofline,
