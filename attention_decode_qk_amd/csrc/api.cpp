@@ -47,7 +47,7 @@ constexpr int kComputeUnits = 256;   // MI355X: 8 XCDs x 32 CUs; the plan aims a
 constexpr int kMaxSplits = 256;
 constexpr int64_t kPartialRowBytes = kHeadDim * 2 + 8;  // f16 o / l + fp32 (m, l)
 constexpr int64_t kSepCombineBytes = 32 << 10;
-constexpr int64_t kShortKeys = 4096;  // key ranges up to this use groups of two tokens
+constexpr int64_t kShortKeys = 4096;  // key ranges up to this: pairs (L <= 4), one KV head per wave
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -232,12 +232,14 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (c.window > 0) keys = std::min<int64_t>(keys, (int64_t)c.window + c.q_len - 1);
   // Page-list-driven decode walks topk * block_size list positions per KV head.
   if (sparse) keys = (int64_t)c.sparse_topk * c.sparse_block;
-  // Token groups: for short key ranges (a sliding window) the step is bound by
-  // its fixed latencies, and groups of two tokens shorten the per-unit prologue
-  // and the combine; long ranges are bound by the key loop, where groups of four
-  // amortise each block's V operand over more rows.  Measured (B = 32, L = 8,
-  // W = 2048): 20.5 us with groups of two, 22.7 with four; (B = 8, L = 8, 64k-128k
-  // keys): 116 us with two, 97 with four.
+  // Token groups: a unit's prologue (q of its tokens, every unit of a group
+  // computing the same) grows with its tokens and each group walks the keys
+  // again; with every combine spread over the splits (one token per combining
+  // unit), groups of four win for L > 4 both over a sliding window (B = 32,
+  // L = 8, W = 2048: 19.1 us with two groups of four at S = 4, 19.45 with four
+  // pairs at S = 2, 20.0 with one group of eight at S = 8, whose prologue alone
+  // took 5 us) and over long ranges (B = 8, L = 8, 64k-128k keys: 97 against
+  // 116 us with pairs); pairs keep L <= 4 over short ranges.
   const int groups = token_groups(c.q_len, keys <= kShortKeys);
   // Eight waves per unit (one KV head each, two waves per SIMD) pay where the
   // key loop is short and compute-heavy (q_len > 1 over a short key range:
@@ -284,12 +286,15 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   // units with both KV heads per wave only).  Measured (B = 8, L = 8, 64k-128k
   // keys, S = 16): 94.1 against 84.6 us per step.
   ctx->balanced = !sparse && !head_split && c.window == 0 && c.batch > 1 && c.batch <= 64 && s > 1;
-  // The partials of a request-group are merged by its first split, which reads
-  // the others' (S - 1) * rows * 136 bytes through one compute unit with
-  // device-coherent loads; beyond kSepCombineBytes a second launch merges them
-  // over the whole chip with plain loads instead (one more launch, ~1.6 us).
+  // Token t of a request-group is merged by split t mod S, which reads the
+  // other splits' (S - 1) * 16 partial rows of 136 bytes per token it merges
+  // through one compute unit with device-coherent loads; beyond
+  // kSepCombineBytes per unit a second launch merges them over the whole chip
+  // with plain loads instead (one more launch, ~1.6 us).
   const int64_t lu = tokens_per_unit(c.q_len, groups);
-  ctx->sep_combine = s > 1 && (int64_t)(s - 1) * lu * kQHeads * kPartialRowBytes > kSepCombineBytes;
+  const int64_t merged_per_unit = (lu + s - 1) / s;  // tokens a combining unit merges
+  ctx->sep_combine =
+      s > 1 && (int64_t)(s - 1) * merged_per_unit * kQHeads * kPartialRowBytes > kSepCombineBytes;
   ctx->planned = true;
   if (workspace_bytes) *workspace_bytes = ctx->ws_bytes;
   if (num_splits_out) *num_splits_out = s;

@@ -19,18 +19,19 @@ constexpr int kWidth = (2 * kQHeads + 2 * kKvHeads) * kHeadDim;  // 2304 project
 constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
 
 // Work unit = (request, token group, split): a workgroup of kAttnWaves waves
-// walks the split's key chunk in blocks of kKeyBlock keys, one block per wave
-// at a time, for the query rows of the group's tokens.  A request's q_len
-// tokens form G groups of consecutive tokens, G = ceil(q_len / 4) or, for short
-// key ranges, ceil(q_len / 2) (the plan's choice); a unit carries
-// ceil(q_len / G) tokens.
+// (or twice that, one KV head each) walks the split's key chunk in blocks of
+// kKeyBlock keys, one block per wave at a time, for the query rows of the
+// group's tokens.  A request's q_len tokens form G groups of consecutive
+// tokens (the plan's choice): G = ceil(q_len / 2) over a short key range up to
+// q_len 4, else G = ceil(q_len / 4); a unit carries ceil(q_len / G) tokens.
 constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
 constexpr int kMaxTokensPerUnit = 4;
 constexpr int kMaxSparseTopk = 256;  // list slots per (KV head, request) of page-list-driven decode
 constexpr int kMaxExtendLen = 65536;  // longest extend / prefill block (q_len > kMaxQLen) served
 constexpr int token_groups(int q_len, bool short_keys) {
-  return short_keys ? (q_len + 1) / 2 : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit;
+  return short_keys && q_len <= kMaxTokensPerUnit ? (q_len + 1) / 2
+                                                  : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit;
 }
 constexpr int tokens_per_unit(int q_len, int groups) { return (q_len + groups - 1) / groups; }
 // The longest q_len served by units of lu tokens under either grouping (0 if none).

@@ -5,14 +5,15 @@
 // frequencies), kernel_fn's flash_attn_with_kvcache call (paged causal window
 // attention over the e4m3 cache, split-KV) and its rms_norm_gate epilogue.
 //
-// One workgroup (4 waves) per work unit (request b, token group tg, split s).  A
-// request's L new tokens form one group (L <= 4) or two groups of at most four
-// consecutive tokens; a unit covers all 16 query heads of its group's tokens,
-// i.e. both KV heads, so every 128-byte cache row it fetches (one key, both
-// heads) is used whole.  Two groups halve the rows a unit carries, and with them
-// the partials its group's combine reads, for the price of reading each key
-// chunk twice (workgroups are dealt to the 8 XCDs round-robin, so the two units
-// of a chunk share an XCD and its L2 when batch x splits is a multiple of 8).
+// One workgroup per work unit (request b, token group tg, split s).  A
+// request's L new tokens form groups of at most two or four consecutive tokens
+// (the plan's choice).  Four waves each cover both KV heads of the group's
+// rows, so every 128-byte cache row a wave fetches (one key, both heads) is
+// used whole; or, for multi-token groups over a short key range, eight waves
+// each cover one KV head.  Groups of fewer tokens shorten a unit's prologue at
+// the price of reading each key chunk once per group (workgroups are dealt to
+// the 8 XCDs round-robin, so the units of a chunk share an XCD and its L2 when
+// batch x splits is a multiple of 8).
 //
 //  A. Geometry and early loads: cache_seqlens[b] gives the request's key range
 //     and this unit's chunk; the projection rows, positions and the page-table
@@ -28,10 +29,11 @@
 //     by more than 2^8); P in f16; PV as O^T = V^T P^T on
 //     v_mfma_f32_16x16x32_f16 with V transposed in registers and widened
 //     exactly to f16.
-//  C. The waves merge through LDS.  A request-group's split 0 is its combiner;
-//     the other splits publish their partial (o / l in f16, m and l in fp32),
-//     each 8-byte word one device-coherent store, and leave without waiting.
-//  D. The combiner keeps its own partial in registers, polls the others' words
+//  C. The waves merge through LDS.  Token t of a group is combined by split
+//     t mod S of its request; the other splits publish their partial rows of t
+//     (o / l in f16, m and l in fp32), each 8-byte word one device-coherent
+//     store, and do not wait for them.
+//  D. A combiner keeps its own partial in registers, polls the others' words
 //     until none holds the empty-slot sentinel, merges them (log-sum-exp),
 //     rounds the attention output to bf16, applies RMSNorm x sigmoid(gate),
 //     writes bf16 out and sets the consumed words back to the sentinel.
@@ -212,13 +214,16 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   __shared__ __align__(16) uint8_t s_newk[kMaxQLen][kRowBytes];
   __shared__ __align__(16) uint8_t s_newv[kMaxQLen][kRowBytes];
   __shared__ float s_cs[kMaxQLen][kHeadDim / 2][2];
-  __shared__ __align__(16) float s_mo[KW][kRows][kHeadDim];
+  // Wave partials for the merge: rows KV-head-major (row g * LU * 8 + r of
+  // head g's row r), padded by 4 floats so that a wave's 16 consecutive rows
+  // start on distinct banks.
+  __shared__ __align__(16) float s_mo[KW][kRows][kHeadDim + 4];
   __shared__ __align__(16) float s_ml[KW][kRows][2];
   // SP (page-list-driven decode): the request's block lists, one per KV head.
   __shared__ int s_blk[SP ? kKvHeads : 1][SP ? kMaxSparseTopk : 1];
 
-  // A unit size that serves a single q_len (LU = 1: q_len 1) serves it as one group.
-  constexpr bool kOneGroup = kMaxL == LU;
+  // Units of one token serve q_len 1 only, as one group.
+  constexpr bool kOneGroup = LU == 1;
   const int L = kOneGroup ? LU : p.q_len;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -253,7 +258,12 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   }
   const int t_lo = tg * LU;              // the group's first token (request-local)
   const int t_n = min(LU, L - t_lo);     // its tokens, >= 1
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: block indices and branches stay scalar
+  // The wave index as a scalar keeps the block indices and branches of the
+  // windowed kernels scalar (B = 32, L = 1, W = 2048: 10.39 against 10.53 us);
+  // the balanced kernels' long key loops run faster with it in a vector
+  // register (B = 64, L = 1, 32k keys: 101.1 against 119.6 us; B = 8, L = 8,
+  // 64k-128k keys: 82.3 against 89.6 us).
+  const int wave = BAL ? tid >> 6 : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kw = wave % KW;            // this wave's place among its head's waves
   const int g0 = HS ? wave / KW : 0;   // first KV head this wave works on
   const int j = lane & 15;
@@ -854,9 +864,10 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 
   // ---------------- C. merge the waves, publish the partial ----------------
   // Every wave parks (m, l, o) of its valid rows in the LDS slot of its place
-  // among its head's waves (compact row ti*16 + h for the group's token ti);
-  // after one barrier all threads merge 4 columns of a row each and publish the
-  // unit's partial.
+  // among its head's waves; after one barrier all threads merge 4 columns of a
+  // row each and publish the unit's partial.
+  // LDS row of the group's token ti, query head h (compact row ti * 16 + h).
+  auto lds_row = [](int cr) { return ((cr & 15) >> 3) * (LU * kGroup) + (cr >> 4) * kGroup + (cr & 7); };
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
@@ -864,7 +875,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       const int r = 16 * rb + j;
       const int ti = r >> 3;
       if (ti >= t_n) continue;
-      const int cr = ti * kQHeads + (g0 + g) * kGroup + (r & 7);
+      const int cr = (g0 + g) * (LU * kGroup) + r;
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii)
         *reinterpret_cast<float4*>(&s_mo[kw][cr][16 * q4 + 4 * ii]) =
@@ -878,7 +889,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
-      const float2 ml = *reinterpret_cast<const float2*>(&s_ml[w][cr][0]);
+      const float2 ml = *reinterpret_cast<const float2*>(&s_ml[w][lds_row(cr)][0]);
       mw[w] = ml.x;
       lw[w] = ml.y;
       mx = fmaxf(mx, ml.x);
@@ -889,7 +900,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
     for (int w = 0; w < KW; ++w) {
       const float a = __builtin_amdgcn_exp2f(mw[w] - muse);
-      const float4 v = *reinterpret_cast<const float4*>(&s_mo[w][cr][c4]);
+      const float4 v = *reinterpret_cast<const float4*>(&s_mo[w][lds_row(cr)][c4]);
       lsum += a * lw[w];
       o.x += a * v.x;
       o.y += a * v.y;
@@ -900,24 +911,28 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     l_out = lsum;
     o_out = o;
   };
+  // Token ti of the group is merged by split ti % nsp of its request (its
+  // combiner), so a group's combines are spread over its splits; every other
+  // split publishes its partial rows of that token.
   // The combine's thread mapping: thread (th, h, c4) takes columns c4..c4+3 of
-  // head h for the group's tokens th, th + TS, ... (TS = threads / 256).
-  constexpr int TS = kThreads / 256;            // token stride between thread groups
-  constexpr int TPT = (LU + TS - 1) / TS;       // token slots per thread
+  // head h for the combiner's tokens kc + nsp * (th + TS * k), k = 0, 1, ...
+  // (TS = threads / 256), one token per thread at a time.
+  constexpr int TS = kThreads / 256;            // thread groups, 256 threads each
   const int c4 = (tid & 15) * 4;
   const int h = (tid >> 4) & (kQHeads - 1);
   const int th = tid >> 8;
   // Partial rows are ((sbase + kc) * L + token) * 16 + head.
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
   const int64_t base = (int64_t)sbase * stride + (int64_t)t_lo * kQHeads + h;
-  if (p.sep_combine || (nsp > 1 && kc != 0)) {
-    // A producer: merge the waves and publish the unit's partial, each 8-byte
-    // word one device-coherent store (never the sentinel pattern); no wait.
-    // With the separate combine every unit is a producer (combine_kernel
-    // merges the partials after this launch).
+  if (p.sep_combine || nsp > 1) {
+    // A producer of the tokens it does not merge: merge the waves and publish
+    // the unit's partial rows, each 8-byte word one device-coherent store
+    // (never the sentinel pattern); no wait.  With the separate combine every
+    // unit publishes every token (combine_kernel merges after this launch).
     const int64_t prow0 = ((int64_t)ru * L + t_lo) * kQHeads;
     for (int idx = tid; idx < t_n * kQHeads * 16; idx += kThreads) {
       const int cr = idx >> 4, cc = (idx & 15) * 4;
+      if (!p.sep_combine && (cr >> 4) % nsp == kc) continue;  // merged here
       float mx, lsum;
       float4 o;
       merge(cr, cc, mx, lsum, o);
@@ -926,119 +941,97 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       publish_h4(p.part_o + (prow0 + cr) * kHeadDim + cc, o.x * rl, o.y * rl, o.z * rl, o.w * rl);
       if (cc == 0) publish_ml(p.part_ml + (prow0 + cr) * 2, mx, lsum);
     }
-    return;
+    if (p.sep_combine || kc >= t_n) return;
   }
 
-  // ---------------- D. combine + gated epilogue (split 0 of the group) ----------------
+  // ---------------- D. combine + gated epilogue (the token's combiner) ----------------
   // The unit's own partial comes from its waves' LDS slots; the other splits'
-  // are polled until none of their words holds the sentinel (a producer
-  // publishes without waiting, so the first poll usually finds them), KS
-  // splits at a time for all the thread's tokens, then merged.  The consumed
+  // (kc + 1, kc + 2, ... modulo nsp) are polled until none of their words
+  // holds the sentinel (a producer publishes without waiting, so the first
+  // poll usually finds them), KS splits at a time, then merged.  The consumed
   // words are set back to the sentinel for the next step.
-  constexpr int KS = TPT >= 4 ? 4 : (TPT == 3 ? 5 : (TPT == 2 ? 8 : 16));
-  uint2 graw[TPT];
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int ti = th + TS * k;
-    graw[k] = make_uint2(0, 0);
-    if (ti < t_n)
-      graw[k] = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + t_lo + ti) * kWidth + kGateOffset +
-                                                 h * kHeadDim + c4);
-  }
-  float mrun[TPT], lrun[TPT], o[TPT][4];
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int ti = th + TS * k;
-    mrun[k] = -INFINITY;
-    lrun[k] = 0.0f;
-    float4 ov = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ti < t_n) merge(ti * kQHeads + h, c4, mrun[k], lrun[k], ov);
-    o[k][0] = ov.x;
-    o[k][1] = ov.y;
-    o[k][2] = ov.z;
-    o[k][3] = ov.w;
-  }
+  constexpr int KS = 16;
   bool lost = false;  // a split never arrived within the wait bound
   const uint64_t t_wait0 = wall_clock64();
-  for (int s0 = 1; nsp > 1 && s0 < nsp; s0 += KS) {
-    uint64_t mlw[TPT][KS], ow[TPT][KS];
-    auto ml_at = [&](int q, int k) { return p.part_ml + (base + (int64_t)(s0 + q) * stride + (th + TS * k) * kQHeads) * 2; };
-    auto o_at = [&](int q, int k) { return p.part_o + (base + (int64_t)(s0 + q) * stride + (th + TS * k) * kQHeads) * kHeadDim + c4; };
-    auto used = [&](int q, int k) { return th + TS * k < t_n && s0 + q < nsp; };
-#pragma unroll
-    for (int q = 0; q < KS; ++q)
-#pragma unroll
-      for (int k = 0; k < TPT; ++k) {
-        mlw[k][q] = kEmptyPartialMl;
-        ow[k][q] = 0;
-        if (used(q, k)) {
-          mlw[k][q] = poll_word(ml_at(q, k));
-          ow[k][q] = poll_word(o_at(q, k));
-        }
-      }
-    // Every lane waits for its own words; the wait is bounded.
-    for (;;) {
-      bool pending = false;
-#pragma unroll
-      for (int q = 0; q < KS; ++q)
-#pragma unroll
-        for (int k = 0; k < TPT; ++k) pending |= mlw[k][q] == kPartialSentinel || ow[k][q] == kPartialSentinel;
-      if (!pending) break;
-      if (wall_clock64() - t_wait0 > kPartialWaitTicks) {
-        lost = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-      for (int q = 0; q < KS; ++q)
-#pragma unroll
-        for (int k = 0; k < TPT; ++k) {
-          if (mlw[k][q] == kPartialSentinel) mlw[k][q] = poll_word(ml_at(q, k));
-          if (ow[k][q] == kPartialSentinel) ow[k][q] = poll_word(o_at(q, k));
-        }
+  for (int k = 0; kc + nsp * TS * k < t_n; ++k) {
+    const int ti = kc + nsp * (th + TS * k);
+    if (ti >= t_n) break;  // whole waves: th is uniform in a wave
+    const uint2 graw = *reinterpret_cast<const uint2*>(p.qkv + (tok0 + t_lo + ti) * kWidth + kGateOffset +
+                                                        h * kHeadDim + c4);
+    float mrun, lrun, o[4];
+    {
+      float4 ov;
+      merge(ti * kQHeads + h, c4, mrun, lrun, ov);
+      o[0] = ov.x;
+      o[1] = ov.y;
+      o[2] = ov.z;
+      o[3] = ov.w;
     }
-    // The words are consumed: back to the sentinel for the next step.
+    for (int s0 = 1; s0 < nsp; s0 += KS) {
+      uint64_t mlw[KS], ow[KS];
+      auto split_of = [&](int q) {  // the (s0 + q)-th split after this one
+        const int sq = kc + s0 + q;
+        return sq >= nsp ? sq - nsp : sq;
+      };
+      auto ml_at = [&](int q) { return p.part_ml + (base + (int64_t)split_of(q) * stride + ti * kQHeads) * 2; };
+      auto o_at = [&](int q) { return p.part_o + (base + (int64_t)split_of(q) * stride + ti * kQHeads) * kHeadDim + c4; };
+      auto used = [&](int q) { return s0 + q < nsp; };
 #pragma unroll
-    for (int q = 0; q < KS; ++q)
-#pragma unroll
-      for (int k = 0; k < TPT; ++k)
-        if (used(q, k)) {
-          reset_word(ml_at(q, k));
-          reset_word(o_at(q, k));
+      for (int q = 0; q < KS; ++q) {
+        mlw[q] = kEmptyPartialMl;
+        ow[q] = 0;
+        if (used(q)) {
+          mlw[q] = poll_word(ml_at(q));
+          ow[q] = poll_word(o_at(q));
         }
+      }
+      // Every lane waits for its own words; the wait is bounded.
+      for (;;) {
+        bool pending = false;
 #pragma unroll
-    for (int k = 0; k < TPT; ++k) {
-      float mc = mrun[k];
+        for (int q = 0; q < KS; ++q) pending |= mlw[q] == kPartialSentinel || ow[q] == kPartialSentinel;
+        if (!pending) break;
+        if (wall_clock64() - t_wait0 > kPartialWaitTicks) {
+          lost = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-      for (int q = 0; q < KS; ++q) mc = fmaxf(mc, __uint_as_float((uint32_t)mlw[k][q]));
+        for (int q = 0; q < KS; ++q) {
+          if (mlw[q] == kPartialSentinel) mlw[q] = poll_word(ml_at(q));
+          if (ow[q] == kPartialSentinel) ow[q] = poll_word(o_at(q));
+        }
+      }
+      // The words are consumed: back to the sentinel for the next step.
+#pragma unroll
+      for (int q = 0; q < KS; ++q)
+        if (used(q)) {
+          reset_word(ml_at(q));
+          reset_word(o_at(q));
+        }
+      float mc = mrun;
+#pragma unroll
+      for (int q = 0; q < KS; ++q) mc = fmaxf(mc, __uint_as_float((uint32_t)mlw[q]));
       const float muse = mc == -INFINITY ? 0.0f : mc;
-      const float a = __builtin_amdgcn_exp2f(mrun[k] - muse);
-      lrun[k] *= a;
+      const float a = __builtin_amdgcn_exp2f(mrun - muse);
+      lrun *= a;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) o[k][c] *= a;
+      for (int c = 0; c < 4; ++c) o[c] *= a;
 #pragma unroll
       for (int q = 0; q < KS; ++q) {
         // A split's weight is its l times 2^(m - max); its partial is o / l.
-        const float wk = __builtin_amdgcn_exp2f(__uint_as_float((uint32_t)mlw[k][q]) - muse) *
-                         __uint_as_float((uint32_t)(mlw[k][q] >> 32));
-        lrun[k] += wk;
-        o[k][0] += wk * h_lo((uint32_t)ow[k][q]);
-        o[k][1] += wk * h_hi((uint32_t)ow[k][q]);
-        o[k][2] += wk * h_lo((uint32_t)(ow[k][q] >> 32));
-        o[k][3] += wk * h_hi((uint32_t)(ow[k][q] >> 32));
+        const float wk = __builtin_amdgcn_exp2f(__uint_as_float((uint32_t)mlw[q]) - muse) *
+                         __uint_as_float((uint32_t)(mlw[q] >> 32));
+        lrun += wk;
+        o[0] += wk * h_lo((uint32_t)ow[q]);
+        o[1] += wk * h_hi((uint32_t)ow[q]);
+        o[2] += wk * h_lo((uint32_t)(ow[q] >> 32));
+        o[3] += wk * h_hi((uint32_t)(ow[q] >> 32));
       }
-      mrun[k] = mc;
+      mrun = mc;
     }
-  }
-  // The tokens' epilogues are independent chains (reductions, rsqrt, gate):
-  // computed for every slot without branches so they interleave; only the
-  // stores of the group's real tokens are kept.
-#pragma unroll
-  for (int k = 0; k < TPT; ++k) {
-    const int ti = th + TS * k;
-    const uint2 ov = gated_epilogue(o[k], lrun[k], vs, graw[k], lost);
-    if (ti < t_n)
-      *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) = ov;
+    *reinterpret_cast<uint2*>(p.out + (tok0 + t_lo + ti) * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
+        gated_epilogue(o, lrun, vs, graw, lost);
   }
 }
 
@@ -1160,8 +1153,7 @@ hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_
   if (p.q_len < 1 || p.q_len > kMaxQLen ||
       (p.tgroups != token_groups(p.q_len, false) && p.tgroups != token_groups(p.q_len, true)))
     return hipErrorInvalidValue;
-  const int lu = tokens_per_unit(p.q_len, p.tgroups);
-  switch (lu) {
+  switch (tokens_per_unit(p.q_len, p.tgroups)) {
     case 1: return launch_served<1>(p, stream);
     case 2: return launch_served<2>(p, stream);
     case 3: return launch_served<3>(p, stream);
