@@ -234,21 +234,27 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   if (sparse) keys = (int64_t)c.sparse_topk * c.sparse_block;
   // Token groups: a unit's prologue (q of its tokens, every unit of a group
   // computing the same) grows with its tokens and each group walks the keys
-  // again; with every combine spread over the splits (one token per combining
-  // unit), groups of four win for L > 4 both over a sliding window (B = 32,
-  // L = 8, W = 2048: 19.1 us with two groups of four at S = 4, 19.45 with four
-  // pairs at S = 2, 20.0 with one group of eight at S = 8, whose prologue alone
-  // took 5 us) and over long ranges (B = 8, L = 8, 64k-128k keys: 97 against
-  // 116 us with pairs); pairs keep L <= 4 over short ranges.
-  const int groups = token_groups(c.q_len, keys <= kShortKeys);
+  // again (the combine is spread over the splits, one token per combining
+  // unit, whatever the grouping).  Over a sliding window (B = 32, L = 8,
+  // W = 2048) two groups of four at S = 4 take 19.1 us, four pairs at S = 2
+  // 19.45, one group of eight at S = 8 20.0 (its prologue alone 5 us); over
+  // long ranges the key loop dominates and one group reads every key once
+  // (B = 8, L = 8, 64k-128k keys, balanced: one group of eight at S = 32,
+  // 75.0 us; two groups of four at S = 16, 83.2; four pairs, 116).  Pairs keep
+  // L <= 4 over short ranges.
+  const bool short_keys = keys <= kShortKeys;
+  const int groups = token_groups(c.q_len, short_keys);
+  const int unit_size = unit_tokens(c.q_len, groups);
   // Eight waves per unit (one KV head each, two waves per SIMD) pay where the
   // key loop is short and compute-heavy (q_len > 1 over a short key range:
-  // 19.2 against 20.7 us at B = 32, L = 8, W = 2048).  Elsewhere the two halves
-  // of a cache row, fetched by different waves, cost HBM efficiency (B = 64,
-  // L = 1, 32k keys: 160 against 113 us; B = 32, L = 1, W = 2048: 13.0 against
-  // 12.5 us), so four waves keep both heads.
+  // 19.2 against 20.7 us at B = 32, L = 8, W = 2048), and a unit of a whole
+  // verify block needs them (its rows would not fit the registers of four
+  // waves).  Elsewhere the two halves of a cache row, fetched by different
+  // waves, cost HBM efficiency (B = 64, L = 1, 32k keys: 160 against 113 us;
+  // B = 32, L = 1, W = 2048: 13.0 against 12.5 us), so four waves keep both
+  // heads.
   // (Page-list-driven decode: each KV head has its own list, so one head per wave.)
-  const bool head_split = sparse || (keys <= kShortKeys && c.q_len > 1);
+  const bool head_split = sparse || (short_keys && c.q_len > 1) || unit_size == kMaxQLen;
   // Decode over long key ranges keeps more K/V blocks in flight with eight
   // waves per unit, both heads each (B = 64, 32k keys: 106 against 113 us); over
   // a window the extra merge and barrier cost more (B = 32, W = 2048: 15.7
@@ -283,9 +289,11 @@ int mi355x_gated_attn_plan(mi355x_gated_attn_ctx* ctx, int32_t max_context, int3
   // uniform S splits each leave the step as long as its longest request; the
   // kernel then deals the B * S units out in proportion to each request's keys
   // (every unit reads the batch's cached lengths, one per lane: B <= 64; the
-  // units with both KV heads per wave only).  Measured (B = 8, L = 8, 64k-128k
-  // keys, S = 16): 94.1 against 84.6 us per step.
-  ctx->balanced = !sparse && !head_split && c.window == 0 && c.batch > 1 && c.batch <= 64 && s > 1;
+  // units with both KV heads per wave, and those of a whole verify block).
+  // Measured (B = 8, L = 8, 64k-128k keys, two groups of four, S = 16): 94.1
+  // against 84.6 us per step.
+  ctx->balanced = !sparse && (!head_split || unit_size == kMaxQLen) && c.window == 0 && c.batch > 1 &&
+                  c.batch <= 64 && s > 1;
   // Token t of a request-group is merged by split t mod S, which reads the
   // other splits' (S - 1) * 16 partial rows of 136 bytes per token it merges
   // through one compute unit with device-coherent loads; beyond

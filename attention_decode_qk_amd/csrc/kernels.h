@@ -22,20 +22,29 @@ constexpr int kGateOffset = (kQHeads + 2 * kKvHeads) * kHeadDim; // 1280
 // (or twice that, one KV head each) walks the split's key chunk in blocks of
 // kKeyBlock keys, one block per wave at a time, for the query rows of the
 // group's tokens.  A request's q_len tokens form G groups of consecutive
-// tokens (the plan's choice): G = ceil(q_len / 2) over a short key range up to
-// q_len 4, else G = ceil(q_len / 4); a unit carries ceil(q_len / G) tokens.
+// tokens (the plan's choice): over a short key range G = ceil(q_len / 2) up to
+// q_len 4 and ceil(q_len / 4) beyond; over a long one a single group.  A unit
+// carries ceil(q_len / G) tokens, served by the kernel of unit size
+// unit_tokens(q_len, G): 1..4, or kMaxQLen for one group of five to eight.
 constexpr int kAttnWaves = 4;
 constexpr int kKeyBlock = 32;
 constexpr int kMaxTokensPerUnit = 4;
 constexpr int kMaxSparseTopk = 256;  // list slots per (KV head, request) of page-list-driven decode
 constexpr int kMaxExtendLen = 65536;  // longest extend / prefill block (q_len > kMaxQLen) served
 constexpr int token_groups(int q_len, bool short_keys) {
-  return short_keys && q_len <= kMaxTokensPerUnit ? (q_len + 1) / 2
-                                                  : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit;
+  return !short_keys ? 1
+                     : (q_len <= kMaxTokensPerUnit ? (q_len + 1) / 2
+                                                   : (q_len + kMaxTokensPerUnit - 1) / kMaxTokensPerUnit);
 }
 constexpr int tokens_per_unit(int q_len, int groups) { return (q_len + groups - 1) / groups; }
+// Kernel unit size for q_len tokens in `groups` groups: 1..4, or kMaxQLen for
+// one group of five to eight tokens.
+constexpr int unit_tokens(int q_len, int groups) {
+  return tokens_per_unit(q_len, groups) > kMaxTokensPerUnit ? kMaxQLen : tokens_per_unit(q_len, groups);
+}
 // The longest q_len served by units of lu tokens under either grouping (0 if none).
 constexpr int max_q_len_for(int lu) {
+  if (lu == kMaxQLen) return kMaxQLen;
   int m = 0;
   for (int l = 1; l <= kMaxQLen; ++l)
     if (tokens_per_unit(l, token_groups(l, false)) == lu || tokens_per_unit(l, token_groups(l, true)) == lu)

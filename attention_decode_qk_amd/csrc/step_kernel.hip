@@ -6,14 +6,15 @@
 // attention over the e4m3 cache, split-KV) and its rms_norm_gate epilogue.
 //
 // One workgroup per work unit (request b, token group tg, split s).  A
-// request's L new tokens form groups of at most two or four consecutive tokens
-// (the plan's choice).  Four waves each cover both KV heads of the group's
-// rows, so every 128-byte cache row a wave fetches (one key, both heads) is
-// used whole; or, for multi-token groups over a short key range, eight waves
-// each cover one KV head.  Groups of fewer tokens shorten a unit's prologue at
-// the price of reading each key chunk once per group (workgroups are dealt to
-// the 8 XCDs round-robin, so the units of a chunk share an XCD and its L2 when
-// batch x splits is a multiple of 8).
+// request's L new tokens form one group or groups of at most two or four
+// consecutive tokens (the plan's choice).  Four waves each cover both KV heads
+// of the group's rows, so every 128-byte cache row a wave fetches (one key,
+// both heads) is used whole; or, for multi-token groups over a short key range
+// and for one group of five to eight tokens, eight waves each cover one KV
+// head.  Groups of fewer tokens shorten a unit's prologue at the price of
+// reading each key chunk once per group (workgroups are dealt to the 8 XCDs
+// round-robin, so the units of a chunk share an XCD and its L2 when batch x
+// splits is a multiple of 8).
 //
 //  A. Geometry and early loads: cache_seqlens[b] gives the request's key range
 //     and this unit's chunk; the projection rows, positions and the page-table
@@ -756,24 +757,50 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   using One = std::integral_constant<int, 1>;
   using Two = std::integral_constant<int, 2>;
 
-  // One block on its own: its scores, running max, P and PV.
-  auto one_block = [&](KvBlock<NG>& buf, const int kb) {
+  // One block on its own: its scores, running max, P and PV; `next` runs once
+  // the block's operands are out of `buf` (it may load the next block there).
+  auto one_block = [&](KvBlock<NG>& buf, const int kb, auto next) {
     substitute(buf, kb);
     float z[1][NG][NRB][8];
     qk(buf, z[0]);
     v8h va[1][NG][4];
     v_operand(buf, va[0]);
+    next();
     mask(kb, z[0]);
 #pragma unroll
     for (int g = 0; g < NG; ++g) softmax_pv(g, z, va, One{});
   };
+  auto nothing = [] {};
+  // Units of a whole verify block (four 16-row blocks per wave) take their
+  // blocks one at a time: a pair's scores and operands would not fit the
+  // registers of two waves per SIMD.
+  constexpr bool kSingle = NRB >= 4;
 
   if (kLateB && nb <= 2) {
     // A short chunk (at most one pair per wave): block A is processed while
     // block B's rows are still arriving.
     const int kb0 = start + kw * kKeyBlock;
-    if (nb > 0) one_block(bufA, kb0);
-    if (nb > 1) one_block(bufB, kb0 + KW * kKeyBlock);
+    if (nb > 0) one_block(bufA, kb0, nothing);
+    if (nb > 1) one_block(bufB, kb0 + KW * kKeyBlock, nothing);
+  } else if constexpr (kSingle) {
+    // Blocks A and B alternate; each block's successor (two blocks on) is
+    // requested as soon as its operands are out of the buffer.
+    for (int bi = 0; bi < nb; bi += 2) {
+      const int kb0 = start + (kw + KW * bi) * kKeyBlock;
+      one_block(bufA, kb0, [&] {
+        if (bi + 2 < nb) {
+          bufA = load_block(pa, bi + 2);
+          pa = load_pte(bi + 4);
+        }
+      });
+      if (bi + 1 < nb)
+        one_block(bufB, kb0 + KW * kKeyBlock, [&] {
+          if (bi + 3 < nb) {
+            bufB = load_block(pb, bi + 3);
+            pb = load_pte(bi + 5);
+          }
+        });
+    }
   } else {
     // Blocks are taken in pairs: the scores and V^T operands of both, then the
     // next pair's loads are issued, then per KV head one running-max decision for
@@ -1113,7 +1140,12 @@ hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
 
 template <int LU>
 hipError_t launch_served(const StepParams& p, hipStream_t stream) {
-  if constexpr (max_q_len_for(LU) >= LU) {
+  if constexpr (LU == kMaxQLen) {
+    // A whole verify block per unit: one KV head per wave only.
+    if (!p.head_split) return hipErrorInvalidValue;
+    return p.balanced ? launch_lu<LU, true, kAttnWaves, false, true>(p, stream)
+                      : launch_lu<LU, true, kAttnWaves>(p, stream);
+  } else if constexpr (max_q_len_for(LU) >= LU) {
     if (p.head_split) return launch_lu<LU, true, kAttnWaves>(p, stream);
     // Balanced splits (the plan sets them only with both KV heads per wave).
     if constexpr (LU == 1)
@@ -1153,11 +1185,12 @@ hipError_t launch_step(const StepParams& p, hipStream_t stream, hipEvent_t attn_
   if (p.q_len < 1 || p.q_len > kMaxQLen ||
       (p.tgroups != token_groups(p.q_len, false) && p.tgroups != token_groups(p.q_len, true)))
     return hipErrorInvalidValue;
-  switch (tokens_per_unit(p.q_len, p.tgroups)) {
+  switch (unit_tokens(p.q_len, p.tgroups)) {
     case 1: return launch_served<1>(p, stream);
     case 2: return launch_served<2>(p, stream);
     case 3: return launch_served<3>(p, stream);
     case 4: return launch_served<4>(p, stream);
+    case kMaxQLen: return launch_served<kMaxQLen>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

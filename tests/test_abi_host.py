@@ -116,7 +116,8 @@ def test_auto_split_count_fills_the_chip(L):
             keys = min(ctxlen, W + Lq - 1) if W else ctxlen
             assert s <= max(1, -(-keys // 128))
             assert s <= 256
-            groups = B * (-(-Lq // 2) if keys <= 4096 and Lq <= 4 else -(-Lq // 4))  # work units per split
+            per_req = (-(-Lq // 2) if Lq <= 4 else -(-Lq // 4)) if keys <= 4096 else 1
+            groups = B * per_req  # work units per split
             assert groups * s <= 256 + groups
         finally:
             ga.mi355x_gated_attn_destroy(ctx)
@@ -211,12 +212,13 @@ def test_timing_hook_without_steps(L):
 
 def test_plan_rejects_a_launch_beyond_the_grid_limit(L):
     """B * token groups * splits workgroups must fit one launch (2^31 - 1);
-    q_len 8 makes two groups over any key range, q_len 3 two over a short one."""
+    q_len 8 makes one group over a long key range and two over a short one,
+    q_len 3 one and two."""
     ctx = ga.mi355x_gated_attn_prepare(cfg(batch=1 << 28, q_len=8, window=0))
     try:
-        ga.mi355x_gated_attn_plan(ctx, 100000, 3)  # 2^28 * 2 * 3 < 2^31
-        ga.mi355x_gated_attn_plan(ctx, 1000, 3)
-        for max_context, splits in ((100000, 4), (1000, 4)):  # 2^28 * 2 * 4 = 2^31
+        ga.mi355x_gated_attn_plan(ctx, 100000, 7)  # 2^28 * 1 * 7 < 2^31
+        ga.mi355x_gated_attn_plan(ctx, 1000, 3)  # 2^28 * 2 * 3 < 2^31
+        for max_context, splits in ((100000, 8), (1000, 4)):  # 2^28 * 8 = 2^28 * 2 * 4 = 2^31
             with pytest.raises(ga.GatedAttnError) as e:
                 ga.mi355x_gated_attn_plan(ctx, max_context, splits)
             assert e.value.status == ga.MI355X_GA_UNSUPPORTED
@@ -234,11 +236,11 @@ def test_plan_rejects_a_launch_beyond_the_grid_limit(L):
 
 
 def test_short_key_ranges_use_groups_of_two_tokens(L):
-    """Up to q_len 4 a short key range takes pairs of tokens, longer blocks and
-    long ranges groups of four; the counters region holds one int32 per
-    (request, token group)."""
-    for Lq, max_context, groups in ((8, 100000, 2), (8, 4096, 2), (3, 1000, 2), (3, 100000, 1),
-                                    (1, 1000, 1), (4, 4000, 2), (4, 5000, 1), (5, 4000, 2), (5, 5000, 2)):
+    """Up to q_len 4 a short key range takes pairs of tokens, longer blocks
+    groups of four; a long range one group; the counters region holds one
+    int32 per (request, token group)."""
+    for Lq, max_context, groups in ((8, 100000, 1), (8, 4096, 2), (3, 1000, 2), (3, 100000, 1),
+                                    (1, 1000, 1), (4, 4000, 2), (4, 5000, 1), (5, 4000, 2), (5, 5000, 1)):
         c = cfg(batch=7, q_len=Lq, window=0)
         ctx = ga.mi355x_gated_attn_prepare(c)
         try:
