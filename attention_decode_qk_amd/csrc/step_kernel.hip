@@ -1072,19 +1072,23 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 }
 
 // The separate combine (q_len <= kMaxQLen, when the plan moves the merge of
-// the partials out of the attention launch): one workgroup per token, thread
-// (h, c4) of head h and columns c4..c4+3.  The token's request has nsp
-// partial rows per (token, head), split kc's at ((sbase + kc) * L + t) * 16 +
-// h, merged by log-sum-exp (split weight l * 2^(m - max), partial o / l) and
-// followed by the gated epilogue, exactly as a combining unit would.  The
-// partials come from the previous launch, so plain loads see them.
-__global__ __launch_bounds__(256) void combine_kernel(StepParams p) {
-  constexpr int KS = 16;  // splits per round of loads
-  const int tok = blockIdx.x;
+// the partials out of the attention launch): one 64-thread workgroup per
+// (token, head), lane (q, c4) merging columns c4..c4+3 over the splits
+// q, q + 4, q + 8, ... of the token's request (up to 8 loads in flight per
+// round), the four lanes of a column then merging their states with lane
+// swaps.  The request has nsp partial rows per (token, head), split kc's at
+// ((sbase + kc) * L + t) * 16 + h, merged by log-sum-exp (split weight
+// l * 2^(m - max), partial o / l) and followed by the gated epilogue, exactly
+// as a combining unit would.  The partials come from the previous launch, so
+// plain loads see them.
+__global__ __launch_bounds__(64) void combine_kernel(StepParams p) {
+  constexpr int KQ = 4;   // split classes (lanes per column)
+  constexpr int KS = 8;   // splits per lane per round of loads
+  const int tok = (int)(blockIdx.x >> 4), h = (int)(blockIdx.x & 15);
   const int L = p.q_len;
   const int b = tok / L, t = tok - b * L;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int h = tid >> 4, c4 = (tid & 15) * 4;
+  const int lane = threadIdx.x;
+  const int c4 = (lane & 15) * 4, q = lane >> 4;
   int sbase = b * p.splits, nsp = p.splits;
   if (p.balanced) {
     int csl;
@@ -1098,40 +1102,56 @@ __global__ __launch_bounds__(256) void combine_kernel(StepParams p) {
   const int64_t stride = (int64_t)L * kQHeads;  // partial rows per split
   const int64_t base = ((int64_t)sbase * L + t) * kQHeads + h;
   float mrun = -INFINITY, lrun = 0.0f, o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nsp; s0 += KS) {
+  for (int s0 = q; s0 < nsp; s0 += KQ * KS) {
     float2 ml[KS];
     uint2 oh[KS];
 #pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      ml[q] = make_float2(-INFINITY, 0.0f);
-      oh[q] = make_uint2(0, 0);
-      if (s0 + q < nsp) {
-        const int64_t r = base + (int64_t)(s0 + q) * stride;
-        ml[q] = *reinterpret_cast<const float2*>(p.part_ml + r * 2);
-        oh[q] = *reinterpret_cast<const uint2*>(p.part_o + r * kHeadDim + c4);
+    for (int k = 0; k < KS; ++k) {
+      const int s = s0 + KQ * k;
+      ml[k] = make_float2(-INFINITY, 0.0f);
+      oh[k] = make_uint2(0, 0);
+      if (s < nsp) {
+        const int64_t r = base + (int64_t)s * stride;
+        ml[k] = *reinterpret_cast<const float2*>(p.part_ml + r * 2);
+        oh[k] = *reinterpret_cast<const uint2*>(p.part_o + r * kHeadDim + c4);
       }
     }
     float mc = mrun;
 #pragma unroll
-    for (int q = 0; q < KS; ++q) mc = fmaxf(mc, ml[q].x);
+    for (int k = 0; k < KS; ++k) mc = fmaxf(mc, ml[k].x);
     const float muse = mc == -INFINITY ? 0.0f : mc;
     const float a = __builtin_amdgcn_exp2f(mrun - muse);
     lrun *= a;
 #pragma unroll
     for (int c = 0; c < 4; ++c) o[c] *= a;
 #pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      const float wk = __builtin_amdgcn_exp2f(ml[q].x - muse) * ml[q].y;
+    for (int k = 0; k < KS; ++k) {
+      const float wk = __builtin_amdgcn_exp2f(ml[k].x - muse) * ml[k].y;
       lrun += wk;
-      o[0] += wk * h_lo(oh[q].x);
-      o[1] += wk * h_hi(oh[q].x);
-      o[2] += wk * h_lo(oh[q].y);
-      o[3] += wk * h_hi(oh[q].y);
+      o[0] += wk * h_lo(oh[k].x);
+      o[1] += wk * h_hi(oh[k].x);
+      o[2] += wk * h_lo(oh[k].y);
+      o[3] += wk * h_hi(oh[k].y);
     }
     mrun = mc;
   }
-  *reinterpret_cast<uint2*>(p.out + (int64_t)tok * (kQHeads * kHeadDim) + h * kHeadDim + c4) =
-      gated_epilogue(o, lrun, vs, graw, false);
+  // The four split classes of a column (lanes 16 apart): two swap rounds.
+#pragma unroll
+  for (int d = 16; d < 64; d <<= 1) {
+    const float mo = __shfl_xor(mrun, d), lo = __shfl_xor(lrun, d);
+    float oo[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) oo[c] = __shfl_xor(o[c], d);
+    const float mc = fmaxf(mrun, mo);
+    const float muse = mc == -INFINITY ? 0.0f : mc;
+    const float a0 = __builtin_amdgcn_exp2f(mrun - muse), a1 = __builtin_amdgcn_exp2f(mo - muse);
+    lrun = lrun * a0 + lo * a1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = o[c] * a0 + oo[c] * a1;
+    mrun = mc;
+  }
+  const uint2 ov = gated_epilogue(o, lrun, vs, graw, false);
+  if (q == 0) *reinterpret_cast<uint2*>(p.out + (int64_t)tok * (kQHeads * kHeadDim) + h * kHeadDim + c4) = ov;
 }
 
 template <int LU, bool HS, int KW, bool SP = false, bool BAL = false>
@@ -1141,7 +1161,7 @@ hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.sep_combine) {
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.batch * p.q_len)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)(p.batch * p.q_len * kQHeads)), dim3(64), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
