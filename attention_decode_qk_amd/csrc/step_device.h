@@ -120,12 +120,13 @@ __device__ inline float sum16(float s) {
   return s + dpp<kDppMirror>(s);
 }
 
-// Maximum of three values in one v_max3_f32, without the quieting moves the
-// compiler puts before fmaxf on values it cannot prove canonical (MFMA results).
+// Maximum of three values in one v_maximum3_f32: without the quieting moves the
+// compiler puts before fmaxf on values it cannot prove canonical (MFMA
+// results), and visible to the compiler, which then keeps the wait states a
+// matrix-core result needs before a vector read (it adds none ahead of inline
+// assembly).  NaN-propagating; the scores it serves hold none.
 __device__ inline float fmax3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
 // Maximum / sum of lane j over the four 16-lane rows: the 16-row swap pairs
