@@ -14,6 +14,9 @@
 namespace mi355x_ga {
 namespace {
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
 // ---------------- Extend / prefill: q_len > kMaxQLen ----------------
 // Two launches.  The prologue normalises, rotates and encodes every new token
 // (q to the workspace, K/V rows to the cache); the launch boundary orders all
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const int unit = (b * n_tiles + tile) * kKvHeads + g;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
   const int kg = wave >> 2, wq = wave & 3;  // key group; the wave's rows within the tile
-  const int j = lane & 15, q4 = lane >> 4;
+
   const int cs = p.cache_seqlens[b];
   // Ragged batches: request b's segment is tokens cu[b] .. cu[b+1]-1 (clamped
   // to q_len and to the step's tokens); a tile past its segment has no rows
@@ -234,21 +237,24 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const float vs = p.scaled ? *p.v_scale : 1.0f;
   const float scale = p.sm_scale_log2 * kscale;
 
-  // q operands of the wave's two 16-row blocks: row r = 32 wq + 16 rb + j is
-  // token r / 8 of the tile, q head 8 g + r % 8 (both key groups hold the same rows).
-  long qop[2][2];
-  int prow[2], plo[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int r = 32 * wq + 16 * rb + j;
+  // The wave's 32 rows, one per lane pair: lane l holds row n = l % 32 (tile
+  // row r = 32 wq + n: token r / 8 of the tile, q head 8 g + r % 8; both key
+  // groups hold the same rows) and, as the QK^T operand, its 32 q bytes of
+  // head-dim half l / 32.
+  const int n32 = lane & 31, hf = lane >> 5;
+  v8i qB;
+  int prow, plo;
+  {
+    const int r = 32 * wq + n32;
     const int ti = r >> 3;
     const bool valid = ti < n_tok;
-    const uint4 qv = *reinterpret_cast<const uint4*>(
-        p.q_out + ((tok0 + min(ti, n_tok - 1)) * kQHeads + kGroup * g + (r & 7)) * kHeadDim + 16 * q4);
-    qop[rb][0] = valid ? as_long(qv.x, qv.y) : 0;
-    qop[rb][1] = valid ? as_long(qv.z, qv.w) : 0;
-    prow[rb] = valid ? p_first + ti : -1;  // an invalid row sees no key
-    plo[rb] = p.window > 0 ? p_first + ti - p.window + 1 : 0;
+    const uint4* qs = reinterpret_cast<const uint4*>(
+        p.q_out + ((tok0 + min(ti, n_tok - 1)) * kQHeads + kGroup * g + (r & 7)) * kHeadDim + 32 * hf);
+    const uint4 q0 = qs[0], q1 = qs[1];
+    qB = valid ? v8i{(int)q0.x, (int)q0.y, (int)q0.z, (int)q0.w, (int)q1.x, (int)q1.y, (int)q1.z, (int)q1.w}
+               : v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    prow = valid ? p_first + ti : -1;  // an invalid row sees no key
+    plo = p.window > 0 ? p_first + ti - p.window + 1 : 0;
   }
 
   // Staging: thread -> (K for waves 0-3 / V for waves 4-7, key of the 64-key
@@ -287,84 +293,81 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     }
   };
 
-  // Per row: the running max (log2 units), the output accumulators and the
-  // sum of P, the latter on the matrix cores (an all-ones operand against P:
-  // every lane of a row gets the row's sum of the f16 weights PV uses).
-  // The lazy test compares the raw score max against thr = (mrow + 2^8 bound)
-  // / scale (scale > 0), and the exponent offset nm = -mrow (0 before any key);
-  // both change only with mrow.
-  float mrow[2] = {-INFINITY, -INFINITY}, thr[2] = {-INFINITY, -INFINITY}, nm[2] = {0.0f, 0.0f};
+  // Per row (both lanes of the row hold the same values): the running max
+  // (log2 units), the lazy test's raw threshold thr = (mrow + 2^8 bound) /
+  // scale (scale > 0) and the exponent offset nm = -mrow (0 before any key),
+  // which change only with mrow; per lane: the output accumulators (its row,
+  // 16 dims of each 32-dim half) and the sum of the f16 weights of its keys.
+  float mrow = -INFINITY, thr = -INFINITY, nm = 0.0f, lpart = 0.0f;
   const float inv_scale = 1.0f / scale;
-  v4f acc[2][4], lsum[2];
-#pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    lsum[rb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  }
-  v8h ones = {1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16, 1.0f16};
+  v16f acc[2] = {};
+  const v2h ones2 = {1.0f16, 1.0f16};
 
-  // One 32-key block of the wave's key group from stage buffer buf.
+  // One 32-key block of the wave's key group from stage buffer buf, as 32 x 32
+  // matrix-core tiles: QK^T on one v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3,
+  // unit scales), PV on four v_mfma_f32_32x32x16_f16.  Lane l's scores are
+  // row l % 32's keys 8 (i / 4) + 4 (l / 32) + i % 4, i = 0..15; its f16
+  // weights are directly the PV operand for the key order {0-3, 8-11 | 4-7,
+  // 12-15} (and + 16), which the V^T operand follows.
   auto compute = [&](const int buf, const int blk) {
     const int kbase = lo + blk * kKeyBlock;
     // Interior: every key <= the first row's position (so <= hi) and inside the
     // last real row's window.
     const bool edge = !(kbase + kKeyBlock - 1 <= p_first && (p.window == 0 || kbase >= hi - p.window + 1));
-    // V^T operand: column c of the lane's four is dim 4 j + c; slots 0-3 are
-    // keys 4 q4 .. 4 q4 + 3 and slots 4-7 keys 16 + 4 q4 .., as in P below.
-    v8h va[4];
+    const uint4* kr = reinterpret_cast<const uint4*>(&s_k[buf][kKeyBlock * kg + n32][32 * hf]);
+    const uint4 k0 = kr[0], k1 = kr[1];
+    const v8i kA = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
+    v16f z = {};
+    z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kA, qB, z, 0, 0, 0, 127, 0, 127);
+    // Causal and window mask of the row, on edge blocks only (an interior
+    // block is visible to every real row; padding rows are never stored).
+    if (edge) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint8_t* row = &s_vt[buf][kg][vt_row(4 * j + c)];
-      const uint2 a0 = *reinterpret_cast<const uint2*>(row + 8 * q4);
-      const uint2 a1 = *reinterpret_cast<const uint2*>(row + 2 * 16 + 8 * q4);
-      va[c] = __builtin_bit_cast(v8h, make_uint4(a0.x, a0.y, a1.x, a1.y));
+      for (int i = 0; i < 16; ++i) {
+        const int key = kbase + 8 * (i >> 2) + 4 * hf + (i & 3);
+        z[i] = (key <= prow && key >= plo) ? z[i] : -INFINITY;
+      }
     }
-    uint4 kv[2];
+    float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], z[8]));
+    m = fmax3(m, fmax3(z[9], z[10], z[11]), fmax3(z[12], z[13], z[14]));
+    m = __builtin_elementwise_maximum(m, z[15]);
+    // The K operand stays live past the product (to here, after its result is
+    // read): a 16-pass MFMA must not write registers it is still reading, and
+    // the allocator would otherwise give the result kA's registers (the zero
+    // accumulator being an inline constant).
+    asm volatile("" ::"v"(kA), "v"(m));
+    if (__any(m > thr)) {
+      const float mx = fmaxf(m, __shfl_xor(m, 32)) * scale;  // the row's other half
+      const float mold = mrow;
+      const float mnew = mx > mold + kLazyRescale ? mx : mold;
+      const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
+      lpart *= alpha;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-      kv[t] = *reinterpret_cast<const uint4*>(&s_k[buf][kKeyBlock * kg + 16 * t + j][16 * q4]);
+      for (int d = 0; d < 2; ++d) acc[d] *= alpha;
+      mrow = mnew;
+      nm = mnew == -INFINITY ? 0.0f : -mnew;
+      thr = mnew == -INFINITY ? -INFINITY : (mnew + kLazyRescale) * inv_scale;
+    }
+    v8h pv[2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      // Raw q.k: lane (q4, j) gets keys 16t + 4q4 + i (slot 4t + i) of row j.
-      float z[8];
+    for (int i = 0; i < 16; ++i) pv[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[i], scale, nm));
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        v4f c = {0.f, 0.f, 0.f, 0.f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(kv[t].x, kv[t].y), qop[rb][0], c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(as_long(kv[t].z, kv[t].w), qop[rb][1], c, 0, 0, 0);
+    for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) z[t * 4 + ii] = c[ii];
+      for (int i = 0; i < 4; ++i)
+        lpart = __builtin_amdgcn_fdot2(v2h{pv[kh][2 * i], pv[kh][2 * i + 1]}, ones2, lpart, false);
+    // V^T operand of dims 32 d + l % 32: keys 16 kh + 4 (l / 32) + {0..3} and
+    // 16 kh + 8 + 4 (l / 32) + {0..3}, two 8-byte runs of the transposed row.
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint8_t* row = &s_vt[buf][kg][vt_row(32 * d + n32)];
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const uint2 a0 = *reinterpret_cast<const uint2*>(row + 32 * kh + 8 * hf);
+        const uint2 a1 = *reinterpret_cast<const uint2*>(row + 32 * kh + 16 + 8 * hf);
+        const v8h va = __builtin_bit_cast(v8h, make_uint4(a0.x, a0.y, a1.x, a1.y));
+        acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pv[kh], acc[d], 0, 0, 0);
       }
-      // Causal and window mask of the row, on edge blocks only (an interior
-      // block is visible to every real row; padding rows are never stored).
-      if (edge) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
-          z[k] = (key <= prow[rb] && key >= plo[rb]) ? z[k] : -INFINITY;
-        }
-      }
-      float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], -INFINITY));
-      if (__any(m > thr[rb])) {
-        const float mx = rows_max(m * scale);
-        const float mold = mrow[rb];
-        const float mnew = mx > mold + kLazyRescale ? mx : mold;
-        const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
-        lsum[rb] *= alpha;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[rb][c] *= alpha;
-        mrow[rb] = mnew;
-        nm[rb] = mnew == -INFINITY ? 0.0f : -mnew;
-        thr[rb] = mnew == -INFINITY ? -INFINITY : (mnew + kLazyRescale) * inv_scale;
-      }
-      v8h pv;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) pv[k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[k], scale, nm[rb]));
-      lsum[rb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pv, lsum[rb], 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        acc[rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va[c], pv, acc[rb][c], 0, 0, 0);
     }
   };
 
@@ -381,11 +384,10 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   int eB = st_entry(min(3, last));
   // The q operands are taken here, once (issued first, they are in by now):
   // a first use inside the loop would make every iteration wait for all loads.
-  asm volatile("" ::"v"(qop[0][0]), "v"(qop[0][1]), "v"(qop[1][0]), "v"(qop[1][1]));
+  asm volatile("" ::"v"(qB));
 
   auto stage_step = [&](const int s, uint4& data, int& e_next) {
     const int buf = s & 1;
-    asm volatile("" : "+v"(ones));  // kept in registers, not rebuilt per block
     if (st_v)
       stage_v(buf, data);
     else
@@ -410,41 +412,39 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // Merge: group 1 leaves its rows' raw accumulators and (m, l) in LDS (the
   // staging buffers are free once every wave is past the loop); group 0 adds
   // them at a common reference max and leaves o / l (times the V descale when
-  // the unit is whole) and its (m, l).
-  const float l_own[2] = {lsum[0][0], lsum[1][0]};
+  // the unit is whole) and its (m, l).  A row's sum is its two lanes' parts;
+  // lane l holds dims 32 d + 8 (i / 4) + 4 (l / 32) + {0..3} of row l % 32.
+  const float l_own = lpart + __shfl_xor(lpart, 32);
+  const int rr = 32 * wq + n32;
   lds_barrier();
   if (kg == 1) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = 32 * wq + 16 * rb + j;
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii)
-        *reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]) =
-            make_float4(acc[rb][0][ii], acc[rb][1][ii], acc[rb][2][ii], acc[rb][3][ii]);
-      if (q4 == 0) s_ml[r] = make_float2(mrow[rb], l_own[rb]);
-    }
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<float4*>(&s_o[rr][32 * d + 8 * i4 + 4 * hf]) =
+            make_float4(acc[d][4 * i4], acc[d][4 * i4 + 1], acc[d][4 * i4 + 2], acc[d][4 * i4 + 3]);
+    if (hf == 0) s_ml[rr] = make_float2(mrow, l_own);
   }
   lds_barrier();
   if (kg == 0) {
+    const float2 ml = s_ml[rr];
+    const float mt = fmaxf(mrow, ml.x);
+    const float mref = mt == -INFINITY ? 0.0f : mt;
+    const float a0 = __builtin_amdgcn_exp2f(mrow - mref), a1 = __builtin_amdgcn_exp2f(ml.x - mref);
+    const float l = l_own * a0 + ml.y * a1;
+    const float inv = l > 0.0f ? (S == 1 ? vs : 1.0f) * __builtin_amdgcn_rcpf(l) : 0.0f;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = 32 * wq + 16 * rb + j;
-      const float2 ml = s_ml[r];
-      const float mt = fmaxf(mrow[rb], ml.x);
-      const float mref = mt == -INFINITY ? 0.0f : mt;
-      const float a0 = __builtin_amdgcn_exp2f(mrow[rb] - mref), a1 = __builtin_amdgcn_exp2f(ml.x - mref);
-      const float l = l_own[rb] * a0 + ml.y * a1;
-      const float inv = l > 0.0f ? (S == 1 ? vs : 1.0f) * __builtin_amdgcn_rcpf(l) : 0.0f;
+    for (int d = 0; d < 2; ++d)
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        float4* o = reinterpret_cast<float4*>(&s_o[r][16 * q4 + 4 * ii]);
+      for (int i4 = 0; i4 < 4; ++i4) {
+        float4* o = reinterpret_cast<float4*>(&s_o[rr][32 * d + 8 * i4 + 4 * hf]);
         const float4 u = *o;
-        *o = make_float4((acc[rb][0][ii] * a0 + u.x * a1) * inv, (acc[rb][1][ii] * a0 + u.y * a1) * inv,
-                         (acc[rb][2][ii] * a0 + u.z * a1) * inv, (acc[rb][3][ii] * a0 + u.w * a1) * inv);
+        *o = make_float4((acc[d][4 * i4] * a0 + u.x * a1) * inv, (acc[d][4 * i4 + 1] * a0 + u.y * a1) * inv,
+                         (acc[d][4 * i4 + 2] * a0 + u.z * a1) * inv, (acc[d][4 * i4 + 3] * a0 + u.w * a1) * inv);
       }
-      // Every lane of the row has read s_ml[r] (one wave, in order) before this.
-      if (q4 == 0) s_ml[r] = make_float2(mt, l);
-    }
+    // Both lanes of the row have read s_ml[rr] (one wave, in order) before this.
+    if (hf == 0) s_ml[rr] = make_float2(mt, l);
   }
   lds_barrier();
 
