@@ -30,8 +30,9 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // 32-key blocks) in LDS, group 0 takes the first block and group 1 the
 // second, and at the end group 0 merges group 1's (max, sum, output) through
 // LDS.  Staging is one 16-byte load per thread: waves 0-3 stage K rows as they
-// are (the fp8 QK^T operand), waves 4-7 widen V to f16 exactly and store it
-// transposed ([dim][key]), so the PV operand is two plain LDS loads per MFMA.
+// are (the fp8 QK^T operand), waves 4-7 widen V to f16 exactly and store its
+// rows as they are ([key][dim]); the PV operand (V^T: four consecutive keys of
+// one dim per lane and half) comes from two transposing LDS reads per MFMA.
 // fp8 QK^T and f16 PV on the matrix cores, base-2 online softmax in fp32 with
 // a lazily moved running max; the unit ends with the gated epilogue of its rows.
 constexpr int kExtTile = 16;                    // new tokens per attention unit
@@ -39,12 +40,13 @@ constexpr int kExtRows = kExtTile * kGroup;     // 128 query rows
 constexpr int kExtWaves = 8;                    // two key groups of four waves
 constexpr int kExtStageKeys = 2 * kKeyBlock;    // keys staged per barrier (one block per group)
 constexpr int kExtKStride = kHeadDim + 16;      // LDS bytes per staged K row (fp8; bank spread)
-constexpr int kExtVStride = 2 * kKeyBlock + 8;  // LDS bytes per staged V^T row (f16 x 32 keys + pad)
-// One block's V^T rows (+ the row-group skew), sized so the second block starts
-// 16 banks after the first (4672 B = 1168 dwords = 16 mod 32).
-constexpr int kExtVBlock = kHeadDim * kExtVStride + 64;
+// LDS bytes per staged V row (f16 x 64 dims + pad): the four keys one
+// transposing read covers start 8 banks apart, so its 16 lanes' 8-byte pieces
+// fill all 32 banks once.
+constexpr int kExtVStride = 2 * kHeadDim + 32;
+constexpr int kExtVBlock = kKeyBlock * kExtVStride;                   // one block's 32 rows
 constexpr int kExtKBytes = 2 * kExtStageKeys * kExtKStride;           // double-buffered K
-constexpr int kExtVBytes = 2 * 2 * kExtVBlock;                        // double-buffered V^T, 2 blocks
+constexpr int kExtVBytes = 2 * 2 * kExtVBlock;                        // double-buffered V, 2 blocks
 constexpr int kExtOBytes = kExtRows * (kHeadDim + 4) * 4 + kExtRows * 8;  // merge / epilogue rows + (m, l)
 constexpr int kExtSmem = (kExtKBytes + kExtVBytes) > kExtOBytes ? (kExtKBytes + kExtVBytes) : kExtOBytes;
 constexpr int kXcds = 8;                        // MI355X: accelerator complex dies, one L2 each
@@ -145,7 +147,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // Staging buffers during the key loop; merge rows and (m, l) after it.
   __shared__ __align__(16) uint8_t smem[kExtSmem];
   auto s_k = reinterpret_cast<uint8_t(*)[kExtStageKeys][kExtKStride]>(smem);                  // [2][64][80]
-  auto s_vt = reinterpret_cast<uint8_t(*)[2][kExtVBlock]>(smem + kExtKBytes);                 // [2][2][4736]
+  auto s_v = reinterpret_cast<uint8_t(*)[2][kExtVBlock]>(smem + kExtKBytes);                  // [2][2][5120]
   auto s_o = reinterpret_cast<float(*)[kHeadDim + 4]>(smem);                                  // [128][68]
   auto s_ml = reinterpret_cast<float2*>(smem + kExtRows * (kHeadDim + 4) * 4);                // [128]
 
@@ -260,14 +262,10 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // Staging: thread -> (K for waves 0-3 / V for waves 4-7, key of the 64-key
   // stage, 16-byte quarter of the head's row).  A K wave's lanes take 16 keys'
   // rows, four lanes per key; V wave 4 + c takes quarter c of all 64 keys, one
-  // key per lane, so each transposed store writes one dim row of both blocks.
+  // key per lane.
   const int st_v = wave >> 2;
   const int st_key = st_v ? lane : (tid >> 2) & (kExtStageKeys - 1);
   const int st_c = st_v ? wave & 3 : tid & 3;
-  // V^T row r of a block (72-byte rows, 8 bytes of skew per 16-row group): the
-  // 16 rows 4 j + c an MFMA operand load reads (j = 0..15) then cover all 32
-  // banks with their 8-byte pieces.
-  auto vt_row = [](int r) { return r * kExtVStride + ((r >> 4) & 3) * 8; };
   // Keys past hi reload key hi (masked); with no key at all (hi < lo, hi maybe
   // negative) key 0, in bounds and unused.
   auto st_keyof = [&](int s) { return max(min(lo + (s_first + s) * kExtStageKeys + st_key, hi), 0); };
@@ -278,19 +276,32 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     return *reinterpret_cast<const uint4*>(src);
   };
   // V: 16 e4m3 values (dims 16 c .. 16 c + 15 of one key) widened to f16
-  // exactly and stored down the key's column of the transposed block.
+  // exactly, 32 bytes of the key's row.
   auto stage_v = [&](const int buf, const uint4 d) {
-    uint8_t* col = &s_vt[buf][st_key >> 5][vt_row(16 * st_c) + 2 * (st_key & (kKeyBlock - 1))];
     const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+    uint32_t h[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const v2h lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, false);
-      const v2h hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, true);
-      *reinterpret_cast<_Float16*>(col + (4 * k + 0) * kExtVStride) = lo2[0];
-      *reinterpret_cast<_Float16*>(col + (4 * k + 1) * kExtVStride) = lo2[1];
-      *reinterpret_cast<_Float16*>(col + (4 * k + 2) * kExtVStride) = hi2[0];
-      *reinterpret_cast<_Float16*>(col + (4 * k + 3) * kExtVStride) = hi2[1];
+      h[2 * k] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, false));
+      h[2 * k + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w[k], 1.0f, true));
     }
+    uint4* dst = reinterpret_cast<uint4*>(
+        &s_v[buf][st_key >> 5][(st_key & (kKeyBlock - 1)) * kExtVStride + 32 * st_c]);
+    dst[0] = make_uint4(h[0], h[1], h[2], h[3]);
+    dst[1] = make_uint4(h[4], h[5], h[6], h[7]);
+  };
+  // Transposing read of the PV operand (ds_read_b64_tr_b16): within each
+  // 16-lane group, lane 4 j + q names 8 bytes (four f16) and lane i receives
+  // element i % 4 of the piece lane 4 j + i / 4 named, for j = 0..3.  Lane i
+  // of a group naming key kb + i / 4, dims D0 + 4 (i % 4) .. + 3 thus
+  // receives keys kb .. kb + 3 of dim D0 + i.  Lane l's group covers dims
+  // 32 d + 16 ((l / 16) % 2) + {0..15} and key offset 4 (l / 32) (its half hf).
+  const int tr_off = ((lane & 15) >> 2) * kExtVStride + 2 * (16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto tr_read = [&](const uint8_t* blk, int key0, int dim0) {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4s*)(blk + key0 * kExtVStride + 2 * dim0 + tr_off));
+    return __builtin_bit_cast(uint2, r);
   };
 
   // Per row (both lanes of the row hold the same values): the running max
@@ -357,14 +368,13 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
       for (int i = 0; i < 4; ++i)
         lpart = __builtin_amdgcn_fdot2(v2h{pv[kh][2 * i], pv[kh][2 * i + 1]}, ones2, lpart, false);
     // V^T operand of dims 32 d + l % 32: keys 16 kh + 4 (l / 32) + {0..3} and
-    // 16 kh + 8 + 4 (l / 32) + {0..3}, two 8-byte runs of the transposed row.
+    // 16 kh + 8 + 4 (l / 32) + {0..3}, one transposing read each.
 #pragma unroll
     for (int d = 0; d < 2; ++d) {
-      const uint8_t* row = &s_vt[buf][kg][vt_row(32 * d + n32)];
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const uint2 a0 = *reinterpret_cast<const uint2*>(row + 32 * kh + 8 * hf);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(row + 32 * kh + 16 + 8 * hf);
+        const uint2 a0 = tr_read(s_v[buf][kg], 16 * kh + 4 * hf, 32 * d);
+        const uint2 a1 = tr_read(s_v[buf][kg], 16 * kh + 8 + 4 * hf, 32 * d);
         const v8h va = __builtin_bit_cast(v8h, make_uint4(a0.x, a0.y, a1.x, a1.y));
         acc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pv[kh], acc[d], 0, 0, 0);
       }
