@@ -238,6 +238,10 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const float kscale = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
   const float scale = p.sm_scale_log2 * kscale;
+  // The matrix cores' block scales (E8M0 127 = 2^0), one opaque register held
+  // for the whole kernel, so no product's result is ever allocated over it.
+  int unit_scale;
+  asm volatile("v_mov_b32 %0, 127" : "=v"(unit_scale));
 
   // The wave's 32 rows, one per lane pair: lane l holds row n = l % 32 (tile
   // row r = 32 wq + n: token r / 8 of the tile, q head 8 g + r % 8; both key
@@ -246,10 +250,11 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   const int n32 = lane & 31, hf = lane >> 5;
   v8i qB;
   int prow, plo;
+  bool valid;
   {
     const int r = 32 * wq + n32;
     const int ti = r >> 3;
-    const bool valid = ti < n_tok;
+    valid = ti < n_tok;
     const uint4* qs = reinterpret_cast<const uint4*>(
         p.q_out + ((tok0 + min(ti, n_tok - 1)) * kQHeads + kGroup * g + (r & 7)) * kHeadDim + 32 * hf);
     const uint4 q0 = qs[0], q1 = qs[1];
@@ -304,13 +309,14 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     return __builtin_bit_cast(uint2, r);
   };
 
-  // Per row (both lanes of the row hold the same values): the running max
-  // (log2 units), the lazy test's raw threshold thr = (mrow + 2^8 bound) /
-  // scale (scale > 0) and the exponent offset nm = -mrow (0 before any key),
-  // which change only with mrow; per lane: the output accumulators (its row,
-  // 16 dims of each 32-dim half) and the sum of the f16 weights of its keys.
-  float mrow = -INFINITY, thr = -INFINITY, nm = 0.0f, lpart = 0.0f;
-  const float inv_scale = 1.0f / scale;
+  // Per row (both lanes of the row hold the same values): the reference max
+  // mref (log2 units; P = 2^(score * scale - mref)) and nm = -mref; `seen`
+  // once the reference comes from the row's own keys (before, it is 0 and every
+  // block takes the exact path below; padding rows never see a key and keep
+  // it).  Per lane: the output accumulators (its row, 16 dims of each 32-dim
+  // half) and the sum of the f16 weights of its keys.
+  float mref = 0.0f, nm = 0.0f, lpart = 0.0f;
+  bool seen = !valid;
   v16f acc[2] = {};
   const v2h ones2 = {1.0f16, 1.0f16};
 
@@ -320,6 +326,13 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // row l % 32's keys 8 (i / 4) + 4 (l / 32) + i % 4, i = 0..15; its f16
   // weights are directly the PV operand for the key order {0-3, 8-11 | 4-7,
   // 12-15} (and + 16), which the V^T operand follows.
+  //
+  // Lazy reference: a lane whose 16 weights sum to at most 16 * 2^8 has none
+  // above 2^8, so the block stays within the bound and no maximum is taken.  A
+  // larger sum (or a row without a reference yet) sends the wave to the exact
+  // path: the row's block maximum, and when it passes the bound (or gives the
+  // row its first reference) the reference moves to it and the row's
+  // accumulators and sum are rescaled before the weights are recomputed.
   auto compute = [&](const int buf, const int blk) {
     const int kbase = lo + blk * kKeyBlock;
     // Interior: every key <= the first row's position (so <= hi) and inside the
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     const uint4 k0 = kr[0], k1 = kr[1];
     const v8i kA = {(int)k0.x, (int)k0.y, (int)k0.z, (int)k0.w, (int)k1.x, (int)k1.y, (int)k1.z, (int)k1.w};
     v16f z = {};
-    z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kA, qB, z, 0, 0, 0, 127, 0, 127);
+    z = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kA, qB, z, 0, 0, 0, unit_scale, 0, unit_scale);
     // Causal and window mask of the row, on edge blocks only (an interior
     // block is visible to every real row; padding rows are never stored).
     if (edge) {
@@ -339,34 +352,42 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
         z[i] = (key <= prow && key >= plo) ? z[i] : -INFINITY;
       }
     }
-    float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], z[8]));
-    m = fmax3(m, fmax3(z[9], z[10], z[11]), fmax3(z[12], z[13], z[14]));
-    m = __builtin_elementwise_maximum(m, z[15]);
+    v8h pv[2];
+    float bs;
+    auto weights = [&]() {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        pv[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[i], scale, nm));
+      bs = 0.0f;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          bs = __builtin_amdgcn_fdot2(v2h{pv[kh][2 * i], pv[kh][2 * i + 1]}, ones2, bs, false);
+    };
+    weights();
     // The K operand stays live past the product (to here, after its result is
     // read): a 16-pass MFMA must not write registers it is still reading, and
     // the allocator would otherwise give the result kA's registers (the zero
     // accumulator being an inline constant).
-    asm volatile("" ::"v"(kA), "v"(m));
-    if (__any(m > thr)) {
-      const float mx = fmaxf(m, __shfl_xor(m, 32)) * scale;  // the row's other half
-      const float mold = mrow;
-      const float mnew = mx > mold + kLazyRescale ? mx : mold;
-      const float alpha = __builtin_amdgcn_exp2f(mold - (mnew == -INFINITY ? 0.0f : mnew));
+    asm volatile("" ::"v"(kA), "v"(bs));
+    if (__any(!(bs <= 16.0f * (float)(1 << (int)kLazyRescale)) || !seen)) {
+      float m = fmax3(fmax3(z[0], z[1], z[2]), fmax3(z[3], z[4], z[5]), fmax3(z[6], z[7], z[8]));
+      m = fmax3(m, fmax3(z[9], z[10], z[11]), fmax3(z[12], z[13], z[14]));
+      m = __builtin_elementwise_maximum(m, z[15]);
+      m = __builtin_elementwise_maximum(m, __shfl_xor(m, 32)) * scale;  // the row's other half
+      const bool mv = m > -INFINITY && (m - mref > kLazyRescale || !seen);
+      const float sh = mv ? m - mref : 0.0f;
+      mref += sh;
+      nm = -mref;
+      seen = seen || mv;
+      const float alpha = __builtin_amdgcn_exp2f(-sh);
       lpart *= alpha;
 #pragma unroll
       for (int d = 0; d < 2; ++d) acc[d] *= alpha;
-      mrow = mnew;
-      nm = mnew == -INFINITY ? 0.0f : -mnew;
-      thr = mnew == -INFINITY ? -INFINITY : (mnew + kLazyRescale) * inv_scale;
+      weights();
     }
-    v8h pv[2];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pv[i >> 3][i & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z[i], scale, nm));
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        lpart = __builtin_amdgcn_fdot2(v2h{pv[kh][2 * i], pv[kh][2 * i + 1]}, ones2, lpart, false);
+    lpart += bs;
     // V^T operand of dims 32 d + l % 32: keys 16 kh + 4 (l / 32) + {0..3} and
     // 16 kh + 8 + 4 (l / 32) + {0..3}, one transposing read each.
 #pragma unroll
@@ -425,6 +446,8 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // the unit is whole) and its (m, l).  A row's sum is its two lanes' parts;
   // lane l holds dims 32 d + 8 (i / 4) + 4 (l / 32) + {0..3} of row l % 32.
   const float l_own = lpart + __shfl_xor(lpart, 32);
+  // A row without a reference of its own has no weight (l = 0, max -inf).
+  const float mrow = seen ? mref : -INFINITY;
   const int rr = 32 * wq + n32;
   lds_barrier();
   if (kg == 1) {
@@ -440,8 +463,8 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   if (kg == 0) {
     const float2 ml = s_ml[rr];
     const float mt = fmaxf(mrow, ml.x);
-    const float mref = mt == -INFINITY ? 0.0f : mt;
-    const float a0 = __builtin_amdgcn_exp2f(mrow - mref), a1 = __builtin_amdgcn_exp2f(ml.x - mref);
+    const float mc = mt == -INFINITY ? 0.0f : mt;
+    const float a0 = __builtin_amdgcn_exp2f(mrow - mc), a1 = __builtin_amdgcn_exp2f(ml.x - mc);
     const float l = l_own * a0 + ml.y * a1;
     const float inv = l > 0.0f ? (S == 1 ? vs : 1.0f) * __builtin_amdgcn_rcpf(l) : 0.0f;
 #pragma unroll
