@@ -327,12 +327,13 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // weights are directly the PV operand for the key order {0-3, 8-11 | 4-7,
   // 12-15} (and + 16), which the V^T operand follows.
   //
-  // Lazy reference: a lane whose 16 weights sum to at most 16 * 2^8 has none
-  // above 2^8, so the block stays within the bound and no maximum is taken.  A
-  // larger sum (or a row without a reference yet) sends the wave to the exact
-  // path: the row's block maximum, and when it passes the bound (or gives the
+  // Lazy reference: a lane whose 16 weights sum to at most 16 * 2^8 keeps the
+  // reference (its weights stay below 2^12, exact enough in f16 and far from
+  // overflow) and no maximum is taken.  A larger sum (or a row without a
+  // reference yet) sends the wave to the exact path: the row's block maximum,
+  // and when it passes the reference by more than the lazy bound (or gives the
   // row its first reference) the reference moves to it and the row's
-  // accumulators and sum are rescaled before the weights are recomputed.
+  // accumulators and sum are rescaled before the weights are formed again.
   auto compute = [&](const int buf, const int blk) {
     const int kbase = lo + blk * kKeyBlock;
     // Interior: every key <= the first row's position (so <= hi) and inside the
