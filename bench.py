@@ -982,8 +982,10 @@ def main():
         torch.cuda.synchronize()
         meta_us = 1000.0 * timed(g_meta) / args.steps
 
-    # The step is one kernel, so the graph-timed time per step is that kernel's
-    # average duration over the timed region (rocprofv3's kernel trace agrees).
+    # A decode or verify step is one kernel, or two where the plan merges the
+    # splits in a second launch (combine_kernel, the long-context verify): the
+    # roofline takes the graph-timed time of the whole step either way, so a
+    # second launch never flatters it (rocprofv3's kernel trace lists both).
     # An extend step is two launches: its roofline takes the attention kernel's
     # event-timed duration (the hook brackets that launch alone).
     extend = w.q_len > 8 and sprefill is None
