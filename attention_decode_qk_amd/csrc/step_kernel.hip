@@ -974,8 +974,17 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       merge(cr, cc, mx, lsum, o);
       // o / l is a weighted mean of V codes (|.| <= 448): f16 holds it.
       const float rl = lsum > 0.0f ? __builtin_amdgcn_rcpf(lsum) : 0.0f;
-      publish_h4(p.part_o + (prow0 + cr) * kHeadDim + cc, o.x * rl, o.y * rl, o.z * rl, o.w * rl);
-      if (cc == 0) publish_ml(p.part_ml + (prow0 + cr) * 2, mx, lsum);
+      if (p.sep_combine) {
+        // Read by the next launch: plain stores (the kernel boundary makes
+        // them visible), no write-through.
+        const v2h lo = {(_Float16)(o.x * rl), (_Float16)(o.y * rl)}, hi = {(_Float16)(o.z * rl), (_Float16)(o.w * rl)};
+        *reinterpret_cast<uint2*>(p.part_o + (prow0 + cr) * kHeadDim + cc) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+        if (cc == 0) *reinterpret_cast<float2*>(p.part_ml + (prow0 + cr) * 2) = make_float2(mx, lsum);
+      } else {
+        publish_h4(p.part_o + (prow0 + cr) * kHeadDim + cc, o.x * rl, o.y * rl, o.z * rl, o.w * rl);
+        if (cc == 0) publish_ml(p.part_ml + (prow0 + cr) * 2, mx, lsum);
+      }
     }
     if (p.sep_combine || kc >= t_n) return;
   }
