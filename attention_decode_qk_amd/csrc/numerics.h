@@ -11,12 +11,14 @@ namespace mi355x_ga {
 
 __device__ inline float bf16_value(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// fp32 -> nearest-even bf16 bit pattern (NaN -> quiet NaN).
+// fp32 -> nearest-even bf16 bit pattern (NaN -> the positive quiet NaN 0x7fc0),
+// on the gfx950 converter (v_cvt_pk_bf16_f32).  Checked against the integer
+// rounding (add 0x7fff plus the kept lowest bit, truncate) over all 2^32 fp32
+// patterns: equal on every non-NaN input, subnormals and infinities included;
+// a NaN keeps its own sign and payload there, hence the select.
 __device__ inline uint32_t bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const uint32_t h = __builtin_bit_cast(unsigned short, (__bf16)f);
+  return __builtin_isnan(f) ? 0x7fc0u : h;
 }
 
 // fp32 -> nearest-even bf16, returned as the fp32 value it represents.
