@@ -129,6 +129,19 @@ __device__ inline float fmax3(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
+// `acc` plus the sum of the f16 weights of n blocks (the values the PV products
+// take), two per v_dot2_f32_f16 against ones: half the instructions of fp32
+// adds, and the row's sum then matches the weights its output is formed from.
+template <int N>
+__device__ inline float row_weights(const v8h (&pv)[N], float acc) {
+  const v2h ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int q = 0; q < N; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_fdot2(v2h{pv[q][2 * i], pv[q][2 * i + 1]}, ones, acc, false);
+  return acc;
+}
+
 // Maximum / sum of lane j over the four 16-lane rows: the 16-row swap pairs
 // rows (0,1) and (2,3), the 32-row swap then pairs the halves.
 __device__ inline float rows_max(float x) {

@@ -687,7 +687,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const bool vis = key < end && key >= rlo[rb] && key <= rhi[rb];
+        const bool vis = (key < end) & (key >= rlo[rb]) & (key <= rhi[rb]);
 #pragma unroll
         for (int g = 0; g < NG; ++g) z[g][rb][k] = vis ? z[g][rb][k] : -INFINITY;
       }
@@ -737,16 +737,12 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     for (int rb = 0; rb < NRB; ++rb) {
       const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
       v8h pv[NB];
-      float psum = 0.0f;
 #pragma unroll
       for (int k = 0; k < 8; ++k)
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(zs[q][g][rb][k], scale, nmuse));
-          psum += e;
-          pv[q][k] = (_Float16)e;
-        }
-      lrow[g][rb] += psum;
+        for (int q = 0; q < NB; ++q)
+          pv[q][k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(zs[q][g][rb][k], scale, nmuse));
+      lrow[g][rb] = row_weights(pv, lrow[g][rb]);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -765,6 +761,12 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     qk(buf, z[0]);
     v8h va[1][NG][4];
     v_operand(buf, va[0]);
+    // The operand is formed before `next` refills `buf`, so that the new rows
+    // land in the registers the old ones leave (else every block pays copies).
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(va[0][g][c]) : "memory");
     next();
     mask(kb, z[0]);
 #pragma unroll
@@ -871,17 +873,14 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
           const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
-          v8h p0v, p1v;
-          float psum = 0.0f;
+          v8h pp[2];
   #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(z0[g][rb][k], scale, nmuse));
-            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(z1[g][rb][k], scale, nmuse));
-            psum += e0 + e1;
-            p0v[k] = (_Float16)e0;
-            p1v[k] = (_Float16)e1;
+            pp[0][k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z0[g][rb][k], scale, nmuse));
+            pp[1][k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(z1[g][rb][k], scale, nmuse));
           }
-          lrow[g][rb] += psum;
+          lrow[g][rb] = row_weights(pp, lrow[g][rb]);
+          const v8h p0v = pp[0], p1v = pp[1];
   #pragma unroll
           for (int c = 0; c < 4; ++c) {
             acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va0[g][c], p0v, acc[g][rb][c], 0, 0, 0);
