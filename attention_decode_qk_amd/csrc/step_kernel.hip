@@ -551,12 +551,17 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   const float scale = p.sm_scale_log2 * ks;
 
   float mrow[NG][NRB], lrow[NG][NRB];
+  // Single-block walks (four row blocks): the exponent's offset, -mrow once a
+  // row has a reference; before that 2^30 for a valid row, so that any visible
+  // key's weight overflows and asks for the maximum, and 0 for a padding row.
+  float nmr[NG][NRB];
   v4f acc[NG][NRB][4];
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       mrow[g][rb] = -INFINITY;
+      nmr[g][rb] = ((16 * rb + j) >> 3) < t_n ? 0x1p30f : 0.0f;
       lrow[g][rb] = 0.0f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[g][rb][c] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -703,10 +708,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // raw q.k for NB blocks (the lazy max decision covers them all).
   auto softmax_pv = [&](int g, auto& zs, auto& vas, auto nblocks) {
     constexpr int NB = decltype(nblocks)::value;
-    float lmx[NRB];     // this lane's scaled maximum over its keys of the blocks
-    bool grow = false;  // some lane's maximum passes its row's lazy bound
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
+    // This lane's scaled maximum over its keys of the blocks in row block rb.
+    auto lane_max = [&](int rb) {
       float m = -INFINITY;
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
@@ -714,13 +717,11 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
         m = fmax3(m, fmax3(u[0], u[1], u[2]), fmax3(u[3], u[4], u[5]));
         m = fmax3(m, u[6], u[7]);
       }
-      lmx[rb] = m * scale;
-      grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
-    }
-    // A row's maximum moves only when its full maximum (over the four lane
-    // groups) passes the bound, which no lane's own maximum does in the common
-    // case: then nothing moves and the cross-lane reduction is skipped.
-    if (__any(grow)) {
+      return m * scale;
+    };
+    // Rows whose full maximum (over the four lane groups) passes their
+    // reference by more than kLazyRescale move it there; acc and l rescale.
+    auto move_refs = [&](const float (&lmx)[NRB]) {
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
         const float mx = rows_max(lmx[rb]);
@@ -731,23 +732,75 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
         for (int c = 0; c < 4; ++c) acc[g][rb][c] *= alpha;
         mrow[g][rb] = mnew;
+        if (mnew != -INFINITY) nmr[g][rb] = -mnew;
       }
-    }
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const float nmuse = mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb];
-      v8h pv[NB];
+    };
+    // f16 weights of row block rb against the row's reference (exponent offset nmuse).
+    auto weights = [&](int rb, float nmuse, v8h (&pv)[NB]) {
 #pragma unroll
       for (int k = 0; k < 8; ++k)
 #pragma unroll
         for (int q = 0; q < NB; ++q)
           pv[q][k] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(zs[q][g][rb][k], scale, nmuse));
-      lrow[g][rb] = row_weights(pv, lrow[g][rb]);
+    };
+    auto products = [&](int rb, const v8h (&pv)[NB]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int q = 0; q < NB; ++q)
           acc[g][rb][c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vas[q][g][c], pv[q], acc[g][rb][c], 0, 0, 0);
+    };
+    if constexpr (NRB >= 4) {
+      // Long walks of single blocks: the weights are formed against the rows'
+      // references first and the maximum is taken only when some lane's sum
+      // passes NB * 8 * 2^8 (a weight may have passed 2^8; a valid row without
+      // a reference overflows, see nmr); a row's weights therefore stay below
+      // 2^11 (f16 holds them to its 11-bit precision), and the maximum's
+      // instructions leave the common block.
+      v8h pv[NRB][NB];
+      float bs[NRB];
+      bool redo = false;
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        weights(rb, nmr[g][rb], pv[rb]);
+        bs[rb] = row_weights(pv[rb], 0.0f);
+        redo |= !(bs[rb] <= NB * 8 * 256.0f);
+      }
+      if (__any(redo)) {
+        float lmx[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) lmx[rb] = lane_max(rb);
+        move_refs(lmx);
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          weights(rb, nmr[g][rb], pv[rb]);
+          bs[rb] = row_weights(pv[rb], 0.0f);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        lrow[g][rb] += bs[rb];
+        products(rb, pv[rb]);
+      }
+    } else {
+      float lmx[NRB];     // this lane's scaled maximum over its keys of the blocks
+      bool grow = false;  // some lane's maximum passes its row's lazy bound
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        lmx[rb] = lane_max(rb);
+        grow |= lmx[rb] > mrow[g][rb] + kLazyRescale;
+      }
+      // A row's maximum moves only when its full maximum passes the bound,
+      // which no lane's own maximum does in the common case: then nothing
+      // moves and the cross-lane reduction is skipped.
+      if (__any(grow)) move_refs(lmx);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        v8h pv[NB];
+        weights(rb, mrow[g][rb] == -INFINITY ? 0.0f : -mrow[g][rb], pv);
+        lrow[g][rb] = row_weights(pv, lrow[g][rb]);
+        products(rb, pv);
+      }
     }
   };
   using One = std::integral_constant<int, 1>;
