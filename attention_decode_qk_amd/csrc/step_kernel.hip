@@ -295,11 +295,17 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // SP: the unit's chunk is a range of virtual key indices v in [0, topk * BS):
   // list slot v / BS, offset v % BS within that block.
   const int first = SP ? 0 : (p.window > 0 ? max(0, p0 - p.window + 1) : 0);
-  const int n = SP ? p.sparse_topk * p.sparse_block : max(0, last - first + 1);
+  // Units of three or more tokens over a window split only the cached keys
+  // (first .. p0 - 1); the request's new keys, whose codes the prologue leaves
+  // in LDS, are one more block for the last split (kNewApart).  A window of W
+  // then splits as W - 1 keys instead of W + L - 1: B 32, L 8, W 2048 gives 64
+  // blocks, four per wave, where 65 left one wave of most units a fifth.
+  constexpr bool kNewApart = LU > 2 && !BAL && !SP;
+  const int n = SP ? p.sparse_topk * p.sparse_block : max(0, (kNewApart ? p0 - 1 : last) - first + 1);
   int chunk = (n + nsp - 1) / nsp;
   chunk = (chunk + kKeyBlock - 1) / kKeyBlock * kKeyBlock;
   const int start = first + kc * chunk;
-  const int end = min(start + chunk, SP ? n : last + 1);
+  const int end = min(start + chunk, SP ? n : (kNewApart ? p0 : last + 1));
   const int nblk = end > start ? (end - start + kKeyBlock - 1) / kKeyBlock : 0;
   const int nb = nblk > kw ? (nblk - kw + KW - 1) / KW : 0;  // this wave's
   const int pt_row = SP && p.token_req ? min(max(p.token_req[b], 0), p.pt_rows - 1) : b;
@@ -405,6 +411,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // any chunk (a padded slot) goes to chunk 0.
   auto chunk_has = [&](int i) {
     if constexpr (SP) return true;  // the new key may sit in any chunk's blocks
+    if constexpr (kNewApart) return kc == nsp - 1;
     const int key = p0 + i;
     return (key >= start && key < end) || (key < first && kc == 0);
   };
@@ -596,6 +603,11 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       return;
     }
     if (kbase + kKeyBlock - 1 < p0) return;
+    // kNewApart: cached blocks stop before p0 (their keys past it are masked and
+    // loaded from clamped cached rows); only the new-key block, at p0, takes the
+    // codes, which only the last split computes.
+    if constexpr (kNewApart)
+      if (kbase < p0) return;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int key = kbase + 16 * t + j;
@@ -667,13 +679,13 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
         }
   };
 
-  // Invisible keys (outside the chunk or a row's window) get a -inf score.
-  auto mask = [&](const int kbase, float (&z)[NG][NRB][8]) {
+  // Invisible keys (at or past kend, outside a row's window) get a -inf score.
+  auto mask = [&](const int kbase, float (&z)[NG][NRB][8], const int kend) {
     if constexpr (SP) {
       // A block past the chunk is invisible; otherwise its keys are visible when
       // their slot is used and they lie below the cached length (q_len 1).
-      const int slot = min(kbase, end - 1) / p.sparse_block;
-      const int bid = kbase < end ? s_blk[g0][slot] : -1;
+      const int slot = min(kbase, kend - 1) / p.sparse_block;
+      const int bid = kbase < kend ? s_blk[g0][slot] : -1;
       const int k0 = bid * p.sparse_block + (kbase - slot * p.sparse_block);
       if (bid >= 0 && k0 + kKeyBlock - 1 < cs) return;
 #pragma unroll
@@ -692,7 +704,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       const int key = kbase + 16 * (k >> 2) + 4 * q4 + (k & 3);
 #pragma unroll
       for (int rb = 0; rb < NRB; ++rb) {
-        const bool vis = (key < end) & (key >= rlo[rb]) & (key <= rhi[rb]);
+        const bool vis = (key < kend) & (key >= rlo[rb]) & (key <= rhi[rb]);
 #pragma unroll
         for (int g = 0; g < NG; ++g) z[g][rb][k] = vis ? z[g][rb][k] : -INFINITY;
       }
@@ -808,7 +820,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 
   // One block on its own: its scores, running max, P and PV; `next` runs once
   // the block's operands are out of `buf` (it may load the next block there).
-  auto one_block = [&](KvBlock<NG>& buf, const int kb, auto next) {
+  auto one_block = [&](KvBlock<NG>& buf, const int kb, const int kend, auto next) {
     substitute(buf, kb);
     float z[1][NG][NRB][8];
     qk(buf, z[0]);
@@ -821,7 +833,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
 #pragma unroll
       for (int c = 0; c < 4; ++c) asm volatile("" ::"v"(va[0][g][c]) : "memory");
     next();
-    mask(kb, z[0]);
+    mask(kb, z[0], kend);
 #pragma unroll
     for (int g = 0; g < NG; ++g) softmax_pv(g, z, va, One{});
   };
@@ -831,12 +843,24 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // registers of two waves per SIMD.
   constexpr bool kSingle = NRB >= 4;
 
+  // kNewApart: the request's new keys p0 .. cs - 1 as one block, K and V from
+  // the prologue's LDS codes (substitute fills every key of a block at p0),
+  // masked by the rows' own ranges; the last split's last wave of each head
+  // takes it, so it is counted once.  It goes first, while the wave's first
+  // cached blocks are still arriving (B 32, L 8, W 2048: 16.7 us, against
+  // 17.8 with it after the cached blocks).
+  if constexpr (kNewApart)
+    if (kc == nsp - 1 && kw == KW - 1 && cs > max(p0, 0)) {
+      KvBlock<NG> nbk{};
+      one_block(nbk, p0, cs, nothing);
+    }
+
   if (kLateB && nb <= 2) {
     // A short chunk (at most one pair per wave): block A is processed while
     // block B's rows are still arriving.
     const int kb0 = start + kw * kKeyBlock;
-    if (nb > 0) one_block(bufA, kb0, nothing);
-    if (nb > 1) one_block(bufB, kb0 + KW * kKeyBlock, nothing);
+    if (nb > 0) one_block(bufA, kb0, end, nothing);
+    if (nb > 1) one_block(bufB, kb0 + KW * kKeyBlock, end, nothing);
   } else if constexpr (kSingle) {
     // Blocks A and B alternate; each block's successor (two blocks on) is
     // requested as soon as its operands are out of the buffer.  The two waves
@@ -851,14 +875,14 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       const int kb0 = start + (kw + KW * bi) * kKeyBlock;
       if ((bi & 3) == 0) __builtin_amdgcn_s_barrier();
       if (bi < nb)
-        one_block(bufA, kb0, [&] {
+        one_block(bufA, kb0, end, [&] {
           if (bi + 2 < nb) {
             bufA = load_block(pa, bi + 2);
             pa = load_pte(bi + 4);
           }
         });
       if (bi + 1 < nb)
-        one_block(bufB, kb0 + KW * kKeyBlock, [&] {
+        one_block(bufB, kb0 + KW * kKeyBlock, end, [&] {
           if (bi + 3 < nb) {
             bufB = load_block(pb, bi + 3);
             pb = load_pte(bi + 5);
@@ -870,9 +894,14 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     // next pair's loads are issued, then per KV head one running-max decision for
     // the pair and P / PV for both.  Scores stay raw (q.k): the scale (> 0) goes
     // into the exponent's fma, so the maximum is taken on raw scores.
-    for (int bi = 0; bi < nb; bi += 2) {
-      const bool has_b = bi + 1 < nb;
-      // An absent second block sits past the chunk: every key masked, no codes substituted.
+    // Units of three or more tokens take an odd last block on its own (below);
+    // the one- and two-token kernels pair it with an empty second block, past
+    // the chunk (every key masked, no codes substituted), which measured faster
+    // for them.
+    constexpr bool kOddAlone = !kLateB;
+    int bi = 0;
+    for (; kOddAlone ? bi + 1 < nb : bi < nb; bi += 2) {
+      const bool has_b = kOddAlone || bi + 1 < nb;
       const int kb0 = start + (kw + KW * bi) * kKeyBlock;
       const int kb1 = has_b ? kb0 + KW * kKeyBlock : end;
       substitute(bufA, kb0);
@@ -892,8 +921,8 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
         pa = load_pte(bi + 4);
         pb = load_pte(bi + 5);
       }
-      mask(kb0, z0);
-      mask(kb1, z1);
+      mask(kb0, z0, end);
+      mask(kb1, z1, end);
   #pragma unroll
       for (int g = 0; g < NG; ++g) {
         float lmx[NRB];     // this lane's scaled maximum over its 16 keys of the pair
@@ -942,6 +971,12 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
         }
       }
     }
+    // An odd block count leaves one block (already in bufA), taken on its own
+    // rather than as a pair with an empty second block: with 65 blocks over
+    // 16 waves (a window of 2048 plus the verify block's keys) one wave of most
+    // units holds five (B 32, L 8, W 2048: 18.5 -> 17.5 us).
+    if constexpr (kOddAlone)
+      if (bi < nb) one_block(bufA, start + (kw + KW * bi) * kKeyBlock, end, nothing);
   }
 
   // Row sums: each lane summed its own keys; add the four lane groups of a row.
