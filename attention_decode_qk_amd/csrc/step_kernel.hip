@@ -109,6 +109,49 @@ __device__ inline KvBlock<NG> load_kv(const StepParams& p, int2 entry, int kk, i
   return d;
 }
 
+// load_kv for a block that lies in one page (32-aligned blocks, power-of-two
+// pages of 32 keys or more): the page's base row in scalar registers (`entry`
+// and `kb`, the block's first key, are wave-uniform), each lane's rows at fixed
+// offsets from it (the loads' immediates), so no per-lane page lookups or row
+// addresses.  All 32 rows lie in the block's page, so they are in bounds; in a
+// block that runs past the chunk's end the rows of the keys beyond it may hold
+// anything: their scores are masked, and the kernel zeroes their V bytes where
+// the block is consumed (zero_v_past), so that no NaN code reaches the PV
+// products (load_kv clamps such keys to end - 1 instead).
+template <int NG>
+__device__ inline KvBlock<NG> load_kv_page(const StepParams& p, int entry, int kb, int g0, int j, int q4) {
+  const int e = __builtin_amdgcn_readfirstlane(entry);  // uniform: keep the base scalar
+  const int phys = (uint32_t)e < (uint32_t)p.num_pages ? e : 0;  // invalid input: stay in bounds
+  const int64_t row0 = ((int64_t)phys << p.page_shift) + (kb & ((1 << p.page_shift) - 1));
+  const uint8_t* kbase = p.k_cache + row0 * kRowBytes + g0 * kHeadDim;
+  const uint8_t* vbase = p.v_cache + row0 * kRowBytes + g0 * kHeadDim;
+  const uint32_t ok = (uint32_t)(j * kRowBytes + 16 * q4);
+  const uint32_t ov = (uint32_t)(4 * q4 * kRowBytes + 4 * j);
+  KvBlock<NG> d;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      d.k[t][g] = *reinterpret_cast<const uint4*>(kbase + ok + (16 * t * kRowBytes + g * kHeadDim));
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      d.v[g][r] =
+          *reinterpret_cast<const uint32_t*>(vbase + ov + ((16 * (r >> 2) + (r & 3)) * kRowBytes + g * kHeadDim));
+  return d;
+}
+
+// V bytes of the keys past offset `lim` of a block loaded by load_kv_page set
+// to zero (lim < 0: every key).
+template <int NG>
+__device__ inline void zero_v_past(KvBlock<NG>& d, int lim, int q4) {
+#pragma unroll
+  for (int r = 0; r < 8; ++r)
+#pragma unroll
+    for (int g = 0; g < NG; ++g) d.v[g][r] = 16 * (r >> 2) + 4 * q4 + (r & 3) <= lim ? d.v[g][r] : 0u;
+}
+
 // Norm (+ RoPE) of one 8-column slice of a head row, page order, every fp32 step
 // rounded once (no contraction): fp64-exact sum of squares over the 8 lanes of
 // the row, exact rsqrt, fp32 product (times `scale`, exact when 1), bf16; RoPE
@@ -192,14 +235,17 @@ __device__ inline uint2 gated_epilogue(const float (&o)[4], float l, float vs, u
   return make_uint2(ob[0] | (ob[1] << 16), ob[2] | (ob[3] << 16));
 }
 
-template <int LU, bool HS, int KW, bool SP, bool BAL>
+template <int LU, bool HS, int KW, bool SP, bool BAL, bool PG>
 __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(StepParams p) {
   // LU: tokens per unit.  A request's L tokens form p.tgroups groups of at most
   // LU consecutive tokens; the unit (request b, token group tg, key chunk kc)
   // attends its group's query rows over chunk kc of the request's keys.
   // KW waves per KV head take the chunk's 32-key blocks round-robin.  HS (head
   // split): 2*KW waves, each working on one KV head's rows; otherwise KW waves
-  // working on both heads.
+  // working on both heads.  PG (balanced units of a whole verify block, pages
+  // of a power of two >= 32 keys): every block starts at a multiple of 32 keys
+  // (no window, chunks of whole blocks), so it lies in one page, and its rows
+  // come from one scalar page-table load (load_kv_page).
   constexpr int NG = HS ? 1 : kKvHeads;           // KV heads a wave works on
   constexpr int kWaves = HS ? 2 * KW : KW;
   constexpr int kThreads = 64 * kWaves;
@@ -208,6 +254,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   constexpr int kMaxL = max_q_len_for(LU);
   static_assert(kMaxL >= LU, "no q_len is served by this unit size");
   static_assert(!SP || (HS && LU == 1), "page-list-driven decode: q_len 1, one KV head per wave");
+  static_assert(!PG || (BAL && HS && NRB >= 4), "page-blocks: balanced whole-block units only");
   constexpr int kMaxItems = kQItems + kMaxL * 2 * kKvHeads * 8;  // + K/V rows of every token
   constexpr int kItemIters = (kMaxItems + kThreads - 1) / kThreads;
   constexpr int kRows = LU * kQHeads;           // partial rows of a unit
@@ -341,8 +388,20 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   };
   auto k_key = [&](int i) { return SP ? mapped(block_key(i, lane & 31)) : block_key(i, lane & 31); };
   auto v_key = [&](int i) { return SP ? mapped(block_key(i, voff)) : block_key(i, voff); };
-  auto load_pte = [&](int i) { return make_int2(page_entry(p, pt, k_key(i)), page_entry(p, pt, v_key(i))); };
-  auto load_block = [&](int2 e, int i) { return load_kv<NG>(p, e, k_key(i), v_key(i), g0, j, q4); };
+  // PG: the wave's block i (clamped like block_key) from scalars: its first key
+  // and its page's entry (a uniform load), in .x of the int2 the other kernels
+  // fill with the lane's K and V entries.
+  const int kw_s = __builtin_amdgcn_readfirstlane(kw);
+  const int nb_s = __builtin_amdgcn_readfirstlane(nb);
+  auto pg_key = [&](int i) { return start + (kw_s + KW * min(i, max(nb_s - 1, 0))) * kKeyBlock; };
+  auto load_pte = [&](int i) {
+    if constexpr (PG) return make_int2(pt[min(pg_key(i) >> p.page_shift, p.max_pages - 1)], 0);
+    else return make_int2(page_entry(p, pt, k_key(i)), page_entry(p, pt, v_key(i)));
+  };
+  auto load_block = [&](int2 e, int i) {
+    if constexpr (PG) return load_kv_page<NG>(p, e.x, pg_key(i), g0, j, q4);
+    else return load_kv<NG>(p, e, k_key(i), v_key(i), g0, j, q4);
+  };
 
   const int2 pte0 = load_pte(0);
   const int2 pte1 = load_pte(1);
@@ -395,6 +454,10 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   constexpr bool kLateB = LU <= 2;
   KvBlock<NG> bufA = load_block(pte0, 0);
   int2 pa = load_pte(2);
+  // PG: the single-block walk issues A's successor, its entry, then B's; the
+  // same order here (not left to the scheduler) keeps the memory-counter waits
+  // on the loop's entry path no tighter than on its back edge.
+  if constexpr (PG) asm volatile("" ::: "memory");
   KvBlock<NG> bufB;
   int2 pb;
   if constexpr (!kLateB) {
@@ -822,6 +885,10 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   // the block's operands are out of `buf` (it may load the next block there).
   auto one_block = [&](KvBlock<NG>& buf, const int kb, const int kend, auto next) {
     substitute(buf, kb);
+    // PG: a block that runs past the chunk's end zeroes the V bytes of its
+    // keys there.
+    if constexpr (PG)
+      if (kb + kKeyBlock > kend) zero_v_past(buf, kend - 1 - kb, q4);
     float z[1][NG][NRB][8];
     qk(buf, z[0]);
     v8h va[1][NG][4];
@@ -870,6 +937,10 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     // block count).  B = 8, L = 8, 64k-128k keys: HBM fetch 336 -> 208 MB per
     // step (the algorithmic bytes: 206 MB), 73.7 -> 70.9 us; a barrier every
     // pair 72.5 us, every block 78.9, every fourth pair 70.6 with 225 MB.
+    // (Refilling every buffer on every pass, with masked filler blocks for the
+    // waves past their own count, makes the compiler's memory-counter waits
+    // exact, but measured slower: B 8, L 8, 64k-128k keys, pages of 64: 60.7
+    // against 57.4-58.3 us.)
     const int nb_all = nblk > 0 ? (nblk + KW - 1) / KW : 0;
     for (int bi = 0; bi < nb_all; bi += 2) {
       const int kb0 = start + (kw + KW * bi) * kKeyBlock;
@@ -1250,10 +1321,10 @@ __global__ __launch_bounds__(64) void combine_kernel(StepParams p) {
   if (q == 0) *reinterpret_cast<uint2*>(p.out + (int64_t)tok * (kQHeads * kHeadDim) + h * kHeadDim + c4) = ov;
 }
 
-template <int LU, bool HS, int KW, bool SP = false, bool BAL = false>
+template <int LU, bool HS, int KW, bool SP = false, bool BAL = false, bool PG = false>
 hipError_t launch_lu(const StepParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)p.batch * (unsigned)p.tgroups * (unsigned)p.splits;
-  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW, SP, BAL>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
+  hipLaunchKernelGGL((fused_step_kernel<LU, HS, KW, SP, BAL, PG>), dim3(grid), dim3(64 * (HS ? 2 : 1) * KW), 0,
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && p.sep_combine) {
@@ -1268,6 +1339,7 @@ hipError_t launch_served(const StepParams& p, hipStream_t stream) {
   if constexpr (LU == kMaxQLen) {
     // A whole verify block per unit: one KV head per wave only.
     if (!p.head_split) return hipErrorInvalidValue;
+    if (p.balanced && p.page_shift >= 5) return launch_lu<LU, true, kAttnWaves, false, true, true>(p, stream);
     return p.balanced ? launch_lu<LU, true, kAttnWaves, false, true>(p, stream)
                       : launch_lu<LU, true, kAttnWaves>(p, stream);
   } else if constexpr (max_q_len_for(LU) >= LU) {

@@ -63,3 +63,21 @@ def test_scaled_paged_verify():
         _say(f"[gpu] balanced scaled verify S={s}")
         res = run_gpu(x, num_splits=s)
         check_full(x, res, ref, f"balanced scaled S={s}")
+
+
+@pytest.mark.parametrize("page_size", [32, 64, 256])
+@pytest.mark.parametrize("splits", [0, 5, 24])
+def test_whole_block_units_on_page_blocks(page_size, splits):
+    """Balanced units of a whole verify block (q_len 8, one group under a long
+    key bound) over pages of 32 or more keys, where every 32-key block lies in
+    one page and the kernel takes a block's rows from one page entry: uneven
+    lengths leave units whose last block runs past their chunk and waves with
+    masked filler blocks; the scaled cache on one case."""
+    lens = np.array([1, 33, 700, 64, 1500, 95], np.int32)
+    w = synth.small(name="page_blocks", batch=len(lens), q_len=8, window=0, page_size=page_size,
+                    rope_theta=500000.0, kv_scale=0.5 if page_size == 64 else 1.0,
+                    qkv_std=1.4142135 if page_size == 64 else 1.0, seq_lo=1, seq_hi=1500)
+    x = synth.make_inputs(w, seed=950 + page_size + splits, seq_lens=lens)
+    _say(f"[gpu] page blocks: P={page_size} S={splits or 'plan'}")
+    res = run_gpu(x, num_splits=splits, ctx_bound=100000)
+    check_full(x, res, Reference(x), f"page blocks P={page_size} S={splits}")
