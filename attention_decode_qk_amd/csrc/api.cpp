@@ -484,6 +484,9 @@ int run_step(mi355x_gated_attn_ctx* ctx, const void* qkv, const int64_t* positio
   sp.block_idx = block_idx;
   sp.sparse_block = c.sparse_block;
   sp.sparse_topk = c.sparse_topk;
+  sp.sparse_shift = c.sparse_block > 0 && (c.sparse_block & (c.sparse_block - 1)) == 0
+                        ? __builtin_ctz((unsigned)c.sparse_block)
+                        : -1;
   sp.cu_seqlens_q = cu_seqlens_q;
   sp.total_q = cu_seqlens_q ? total_q : (int64_t)c.batch * c.q_len;
   sp.token_req = token_req;

@@ -98,6 +98,7 @@ struct StepParams {
                                  // null: query b uses row b
   int32_t pt_rows;               // sparse prefill: rows of page_table (token_req is clamped to them)
   float inv_freq[kHeadDim / 2];
+  int32_t sparse_shift;          // log2(sparse_block) if a power of two, else -1
 };
 
 // attn_start (may be null): for q_len > kMaxQLen, an event recorded between

@@ -368,9 +368,12 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
   };
   // SP: virtual index -> key of the request; false (and key 0, a row in bounds)
   // when the slot is empty or the key lies at or past the cached length.
+  // SP: list slot of virtual index v (>= 0) and its offset in the slot's block
+  // (a shift when the block size is a power of two).
+  auto sp_slot = [&](int v) { return p.sparse_shift >= 0 ? v >> p.sparse_shift : v / p.sparse_block; };
   auto sp_key = [&](int v, int& key) {
     if constexpr (SP) {
-      const int slot = v / p.sparse_block;
+      const int slot = sp_slot(v);
       const int bid = s_blk[g0][slot];
       key = bid * p.sparse_block + (v - slot * p.sparse_block);
       const bool ok = bid >= 0 && key < cs;
@@ -644,7 +647,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
       // q_len 1: the new key p0, wherever this block's list slot holds it (a
       // 32-key block lies in one slot: BS and the chunks are multiples of 32).
       if (kbase >= end) return;
-      const int slot = kbase / p.sparse_block;
+      const int slot = sp_slot(kbase);
       const int bid = s_blk[g0][slot];
       const int k0 = bid * p.sparse_block + (kbase - slot * p.sparse_block);
       if (bid < 0 || p0 < k0 || p0 >= k0 + kKeyBlock) return;
@@ -747,7 +750,7 @@ __global__ __launch_bounds__(64 * KW * (HS ? 2 : 1)) void fused_step_kernel(Step
     if constexpr (SP) {
       // A block past the chunk is invisible; otherwise its keys are visible when
       // their slot is used and they lie below the cached length (q_len 1).
-      const int slot = min(kbase, kend - 1) / p.sparse_block;
+      const int slot = sp_slot(min(kbase, kend - 1));
       const int bid = kbase < kend ? s_blk[g0][slot] : -1;
       const int k0 = bid * p.sparse_block + (kbase - slot * p.sparse_block);
       if (bid >= 0 && k0 + kKeyBlock - 1 < cs) return;
