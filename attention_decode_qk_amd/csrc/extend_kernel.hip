@@ -197,6 +197,21 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
     g = rr % kKvHeads;
     tile = (rr / kKvHeads) % tb;
     ks = rr / (kKvHeads * tb);
+  } else if (S == 1 && p.window == 0 && p.batch * n_tiles >= 128 && p.batch * n_tiles <= 256) {
+    // Without a window a tile's keys grow with its position and with its
+    // request's prefix.  Every workgroup is resident at once (two per compute
+    // unit), and workgroups b and b + 256 share a unit: the first 128 tile
+    // pairs (both KV heads, adjacent workgroups) take the tiles longest first,
+    // requests interleaved, and the rest the same ranks mirrored, so each unit
+    // holds a long tile and a short one of the opposite rank.
+    const int q = (int)(blockIdx.x >> 1);
+    const int T = p.batch * n_tiles;
+    if (q >= T) return;
+    g = (int)(blockIdx.x & 1);
+    const int rank = q < 128 ? q : T - 1 - (q - 128);
+    b = rank % p.batch;
+    tile = n_tiles - 1 - rank / p.batch;
+    ks = 0;
   } else {
     const int n_wg = p.batch * n_tiles * kKvHeads * S;
     const int per_xcd = (n_wg + kXcds - 1) / kXcds;
