@@ -53,10 +53,11 @@ constexpr int kXcds = 8;                        // MI355X: accelerator complex d
 
 // Prologue: kExtPrologueTokens new tokens per workgroup, their 160 items each
 // ((16 q, 2 k, 2 v head rows) x 8 column slices, eight lanes per head row) dealt
-// over the 256 threads, three per thread at most; every item's load is issued
-// first.  The threads holding two items compute the tokens' RoPE sincos table
-// while the others finish their third norm; RoPE, the e4m3 codes and the
-// stores follow the barrier.
+// over the 256 threads, three per thread at most.  The sincos table's positions
+// are requested first, then every item's load; the threads holding two items
+// compute the tokens' RoPE sincos table while the rows arrive, then their
+// norms, and the others their three norms; RoPE, the e4m3 codes and the stores
+// follow the barrier.
 constexpr int kExtPrologueTokens = 4;
 constexpr int kExtItems = (kQHeads + 2 * kKvHeads) * 8;                              // per token
 constexpr int kExtPrologueIters = (kExtPrologueTokens * kExtItems + 255) / 256;      // 3
@@ -69,6 +70,18 @@ __global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
   const int64_t T = p.total_q;
   const int64_t t0 = (int64_t)blockIdx.x * kExtPrologueTokens;
   const int tid = threadIdx.x;
+  // The sincos table's inputs are requested first, so that its fp64 sincos
+  // runs while the projection rows are still arriving (loads return in issue
+  // order).  Without RoPE, positions may be absent: a cache row index is read
+  // instead (same type, always present) and ignored.
+  const int cs_tok = max(tid - kExtCsBase, 0) >> 5;
+  const int64_t cs_pos = (p.rope ? p.positions : p.cache_loc)[min(t0 + cs_tok, T - 1)];
+  // (read through the argument segment as volatile: a plain load of the
+  // argument's table may be scheduled after the rows', and then waits for them)
+  const float freq = reinterpret_cast<const volatile __attribute__((address_space(4))) float*>(
+      (const __attribute__((address_space(4))) uint8_t*)__builtin_amdgcn_kernarg_segment_ptr() +
+      offsetof(StepParams, inv_freq))[tid & 31];
+  asm volatile("" ::: "memory");
   uint4 xv[kExtPrologueIters];
 #pragma unroll
   for (int it = 0; it < kExtPrologueIters; ++it) {
@@ -77,11 +90,13 @@ __global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
     const int rem = item % kExtItems;
     xv[it] = *reinterpret_cast<const uint4*>(p.qkv + tk * kWidth + (rem >> 3) * kHeadDim + (rem & 7) * 8);
   }
-  // Without RoPE, positions may be absent: a cache row index is read instead
-  // (same type, always present) and ignored.
-  const int cs_tok = max(tid - kExtCsBase, 0) >> 5;
-  const int64_t cs_pos = (p.rope ? p.positions : p.cache_loc)[min(t0 + cs_tok, T - 1)];
-  const float freq = p.inv_freq[tid & 31];
+  if (p.rope && tid >= kExtCsBase) {
+    const float ang = (float)cs_pos * freq;
+    double sd, cd;
+    sincos((double)ang, &sd, &cd);
+    s_cs[cs_tok][tid & 31][0] = (float)cd;
+    s_cs[cs_tok][tid & 31][1] = (float)sd;
+  }
   const float ks = p.scaled ? *p.k_scale : 1.0f;
   const float vs = p.scaled ? *p.v_scale : 1.0f;
 
@@ -106,13 +121,6 @@ __global__ __launch_bounds__(256) void extend_prologue_kernel(StepParams p) {
         for (int k = 0; k < 8; ++k) y[it][k] = p.scaled ? round_bf16(x[k] / vs) : x[k];  // raw value
       }
     }
-  }
-  if (p.rope && tid >= kExtCsBase) {
-    const float ang = (float)cs_pos * freq;
-    double sd, cd;
-    sincos((double)ang, &sd, &cd);
-    s_cs[cs_tok][tid & 31][0] = (float)cd;
-    s_cs[cs_tok][tid & 31][1] = (float)sd;
   }
   lds_barrier();
 #pragma unroll
