@@ -40,10 +40,12 @@ constexpr int kExtRows = kExtTile * kGroup;     // 128 query rows
 constexpr int kExtWaves = 8;                    // two key groups of four waves
 constexpr int kExtStageKeys = 2 * kKeyBlock;    // keys staged per barrier (one block per group)
 constexpr int kExtKStride = kHeadDim + 16;      // LDS bytes per staged K row (fp8; bank spread)
-// LDS bytes per staged V row (f16 x 64 dims + pad): the four keys one
-// transposing read covers start 8 banks apart, so its 16 lanes' 8-byte pieces
-// fill all 32 banks once.
-constexpr int kExtVStride = 2 * kHeadDim + 32;
+// LDS bytes per staged V row (f16 x 64 dims + 48 bytes of pad): an odd number
+// of 16-byte units, so the staging stores of consecutive keys (one key per
+// lane, 16 bytes each) start in different banks.  Measured against 160- and
+// 192-byte rows, whose transposing reads conflict less but whose stores
+// conflict more, the fastest.
+constexpr int kExtVStride = 2 * kHeadDim + 48;
 constexpr int kExtVBlock = kKeyBlock * kExtVStride;                   // one block's 32 rows
 constexpr int kExtKBytes = 2 * kExtStageKeys * kExtKStride;           // double-buffered K
 constexpr int kExtVBytes = 2 * 2 * kExtVBlock;                        // double-buffered V, 2 blocks
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(64 * kExtWaves, 4) void extend_attn_kernel(StepPara
   // Staging buffers during the key loop; merge rows and (m, l) after it.
   __shared__ __align__(16) uint8_t smem[kExtSmem];
   auto s_k = reinterpret_cast<uint8_t(*)[kExtStageKeys][kExtKStride]>(smem);                  // [2][64][80]
-  auto s_v = reinterpret_cast<uint8_t(*)[2][kExtVBlock]>(smem + kExtKBytes);                  // [2][2][5120]
+  auto s_v = reinterpret_cast<uint8_t(*)[2][kExtVBlock]>(smem + kExtKBytes);                  // [2][2][5632]
   auto s_o = reinterpret_cast<float(*)[kHeadDim + 4]>(smem);                                  // [128][68]
   auto s_ml = reinterpret_cast<float2*>(smem + kExtRows * (kHeadDim + 4) * 4);                // [128]
 
